@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark: complete-sketch throughput of SparseStack on one MI355X.
+
+Step = one complete FP16-accumulate SparseStack sketch of the scale
+workload (A 2^20 x 256 FP32 N(0,1), zeta = 4, d = 512 = 2n): metadata
+generation + output zeroing + application, all in libsksketch's HIP
+kernels, with A already resident in HBM (FP16 sketching page §V-A: complete
+sketch time includes initialization, map generation and application).
+
+value = algorithmic bytes (A + metadata + sketch, each counted once) per
+step / step time, in GB/s.  The same run times the comparison legs: the
+flat FP32 scatter (one global atomic per contribution), the LDS-privatized
+FP32 sketch, the page's flat FP16 design, and BlockPerm-SJLT on its own
+workload (A 2^21 x 512, d = 1024, M = 64, kappa = 4, s = 1).  The roofline
+block times the dominant kernel (the FP16 LDS apply kernel) alone with HIP
+events on its stream; cpu_baseline times the CPU oracle on a row sample of
+the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --profile-pass   # short fixed run for rocprofv3 --pmc
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, published
+M_ROWS, N_COLS, D_ROWS, ZETA = 1 << 20, 256, 512, 4
+BP_M, BP_N, BP_D, BP_BLOCKS, BP_KAPPA = 1 << 21, 512, 1024, 64, 4
+SEED = 1
+
+
+def sparsestack_bytes(m, n, d, zeta, out_elem):
+    """A read once (4mn) + metadata row_idx/val (8 m zeta) + sketch (d n)."""
+    return 4 * m * n + 8 * m * zeta + out_elem * d * n
+
+
+def blockperm_bytes(m, n, d):
+    return 4 * m * n + 4 * d * n
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps            # ms per call
+
+
+def cpu_baseline(A_host, sample_rows):
+    """The CPU oracle (metadata + fp64 sketch) on the first sample_rows rows
+    of the scale workload's A (a host copy of the device input),
+    single-threaded; bytes per second of the same algorithmic-byte count."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    sample_rows = min(sample_rows, A_host.shape[0])
+    A = A_host[:sample_rows]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ri, v = oracle.meta_ref(SEED, sample_rows, D_ROWS, ZETA)
+        B = oracle.sketch_f64(A, ri, v, D_ROWS, ZETA)
+        t1 = time.perf_counter()
+    assert np.isfinite(B).all()
+    sec = t1 - t0
+    gbs = sparsestack_bytes(sample_rows, N_COLS, D_ROWS, ZETA, 4) / sec / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle metadata + fp64 sketch of the first {sample_rows} of {M_ROWS} "
+                      f"rows (n={N_COLS}, zeta={ZETA}, d={D_ROWS}), {sec:.2f} s, 1 thread; "
+                      f"host reports {os.cpu_count()} cpus, affinity "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-sample-rows", type=int, default=M_ROWS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-blockperm", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="few fixed launches of the dominant kernel and a 1 GiB copy, no JSON")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the multi-GPU path is a design note, not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_sketching_amd import binding as b
+    from sparse_sketching_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    b.load()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    m, n, d, zeta = M_ROWS, N_COLS, D_ROWS, ZETA
+    A = inputs.gaussian_torch(m, n, seed=0)
+    ri = torch.empty(m * zeta, dtype=torch.int32, device=dev)
+    val = torch.empty(m * zeta, dtype=torch.float32, device=dev)
+    B16 = torch.empty((d, n), dtype=torch.float16, device=dev)
+    B32 = torch.empty((d, n), dtype=torch.float32, device=dev)
+
+    def meta():
+        b.sk_meta_generate(SEED, 0, m, d, zeta, ri, val, sp)
+
+    def f16(flags=0):
+        b.sk_apply_f16acc(A, m, n, n, ri, val, zeta, B16, d, n, flags, sp)
+
+    def f32(flags=0):
+        b.sk_apply_f32(A, m, n, n, ri, val, zeta, B32, d, n, flags, sp)
+
+    if args.profile_pass:
+        meta()
+        for _ in range(3):
+            f16(b.SK_ACCUMULATE)
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)                          # 1 GiB read + 1 GiB write
+        torch.cuda.synchronize()
+        print("profile pass done: 3 x f16 LDS apply (accumulate), 3 x 1 GiB copy", flush=True)
+        return
+
+    K, W = args.steps, args.warmup
+    bytes16 = sparsestack_bytes(m, n, d, zeta, 2)
+    bytes32 = sparsestack_bytes(m, n, d, zeta, 4)
+
+    # headline step: complete FP16-accumulate sketch
+    ms16 = timed(lambda: (meta(), f16()), K, W, stream)
+    print(f"[bench] f16acc complete sketch {ms16:.4f} ms", file=sys.stderr, flush=True)
+    ms32_flat = timed(lambda: (meta(), f32(b.SK_VARIANT_FLAT)), K, W, stream)
+    ms32_lds = timed(lambda: (meta(), f32(b.SK_VARIANT_LDS)), K, W, stream)
+    ms16_flat = timed(lambda: (meta(), f16(b.SK_VARIANT_FLAT)), max(1, K // 4), 1, stream)
+    print(f"[bench] f32 flat {ms32_flat:.4f} ms, f32 lds {ms32_lds:.4f} ms, "
+          f"f16 flat {ms16_flat:.4f} ms", file=sys.stderr, flush=True)
+    # the dominant kernel alone: SK_ACCUMULATE skips the zeroing launch
+    ms_kernel = timed(lambda: f16(b.SK_ACCUMULATE), K, W, stream)
+    ms_meta = timed(meta, K, W, stream)
+    # device copy bandwidth for context
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ms_copy = timed(lambda: dst.copy_(src), K, 2, stream)
+    copy_gbs = 2 * src.numel() * 4 / ms_copy / 1e6
+    del src, dst
+
+    A_host = None if args.no_cpu_baseline else A.cpu().numpy()
+    bp = None
+    if not args.no_blockperm:
+        del A, ri, val
+        torch.cuda.empty_cache()
+        Abp = inputs.gaussian_torch(BP_M, BP_N, seed=0)
+        Y = torch.empty((BP_D, BP_N), dtype=torch.float32, device=dev)
+        ms_bp = timed(lambda: b.sk_apply_blockperm(Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS, BP_KAPPA,
+                                                   1, SEED, Y, BP_N, 0, sp), K, W, stream)
+        gbs_bp = blockperm_bytes(BP_M, BP_N, BP_D) / ms_bp / 1e6
+        bp = {"workload": f"BlockPerm-SJLT m=2^21 n={BP_N} d={BP_D} M={BP_BLOCKS} "
+                          f"kappa={BP_KAPPA} s=1", "ms": round(ms_bp, 4),
+              "GBps": round(gbs_bp, 1), "hbm_frac": round(gbs_bp / HBM_PEAK_GBS, 4)}
+        del Abp, Y
+
+    gbs16 = bytes16 / ms16 / 1e6
+    kernel_gbs = bytes16 / ms_kernel / 1e6
+    out = {
+        "metric": "complete-sketch SA GB/s and % HBM roofline, zeta=4, d=2n, FP16-acc vs FP32",
+        "value": round(gbs16, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms16, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32-in/f16-acc",
+        "data": "synthetic N(0,1) A drawn on device with a seeded generator",
+        "config": {"workload": f"SparseStack m=2^20 n={n} zeta={zeta} d={d} (d=2n), dense N(0,1)",
+                   "m": m, "n": n, "d": d, "zeta": zeta, "seed": SEED,
+                   "algorithmic_bytes": bytes16},
+        "hbm_frac": round(gbs16 / HBM_PEAK_GBS, 4),
+        "fp32_flat_ms": round(ms32_flat, 5),
+        "fp32_flat_GBps": round(bytes32 / ms32_flat / 1e6, 2),
+        "fp32_lds_ms": round(ms32_lds, 5),
+        "fp16_flat_ms": round(ms16_flat, 5),
+        "speedup_vs_fp32_flat": round(ms32_flat / ms16, 3),
+        "speedup_vs_fp32_lds": round(ms32_lds / ms16, 3),
+        "meta_ms": round(ms_meta, 5),
+        "copy_GBps": round(copy_gbs, 1),
+        "blockperm": bp,
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "k_f16_lds<64,4>",
+                     "kernel_ms": round(ms_kernel, 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(A_host, args.cpu_sample_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

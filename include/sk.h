@@ -1,0 +1,178 @@
+/*
+ * sk.h: C ABI of the MI355X (gfx950) sparse-sketching library libsksketch.so.
+ *
+ * The library forms the sketch B = S A of a tall FP32 matrix A (m x n,
+ * m >> n) for a sparse oblivious subspace embedding S (d x m):
+ *
+ *   - SparseStack: every input row is spread over zeta independent
+ *     CountSketch blocks of d/zeta output rows each, with one signed nonzero
+ *     of magnitude 1/sqrt(zeta) per block; zeta = 1 is CountSketch.
+ *     ("On the Robustness of Sparse Randomized Sketching to FP16 Rounding
+ *     on GPUs", §I, §II-A, §III-A, §IV-A.)
+ *   - BlockPerm-SJLT: M x M blocks wired by a union of kappa edge-disjoint
+ *     permutations, with a CountSketch-like hash inside each wired block.
+ *     ("FlashSketch: Sketch-Kernel Co-Design for Fast Sparse Sketching on
+ *     GPUs", §4, §5, App. D.)
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are row-major.  A has leading dimension lda (elements) >= n,
+ *     B has leading dimension ldb (elements) >= n.
+ *   - Every pointer to matrix or metadata storage is a DEVICE pointer on the
+ *     current HIP device.  The caller owns all memory; the library never
+ *     allocates, frees or keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on that stream and returns without
+ *     synchronizing the host.
+ *   - Arguments are validated before any HIP call; on failure nothing is
+ *     enqueued and a non-zero sk_status is returned.  A failed launch
+ *     returns SK_ERR_HIP.  Faults of enqueued work surface at the caller's
+ *     next synchronization, as for any HIP kernel.
+ *   - m = 0 is a valid empty input: B is zeroed (or left as is with
+ *     SK_ACCUMULATE) and A / metadata pointers may then be NULL.
+ *   - Output semantics: B = S A by default (the call zeroes B on the stream
+ *     first, and that zeroing is part of the complete sketch time, FP16
+ *     sketching page §V-A); with SK_ACCUMULATE it computes B += S A, so a
+ *     matrix can be sketched in row chunks (see sk_meta_generate).
+ *   - A and B must not overlap (SK_ERR_ARG).
+ *   - Calls are reentrant and hold no state between calls.
+ */
+#ifndef SK_SKETCH_H
+#define SK_SKETCH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sk_status {
+    SK_OK = 0,
+    SK_ERR_NULL = 1,        /* a required pointer is NULL */
+    SK_ERR_SHAPE = 2,       /* sizes or leading dimensions are inconsistent */
+    SK_ERR_ALIGN = 3,       /* a buffer or stride breaks an alignment rule */
+    SK_ERR_UNSUPPORTED = 4, /* a valid request this library does not build */
+    SK_ERR_HIP = 5,         /* the HIP runtime reported an error */
+    SK_ERR_ARG = 6          /* invalid flags, aliasing, or other argument */
+} sk_status;
+
+/* flags for the apply calls */
+#define SK_ACCUMULATE   1u  /* B += S A instead of B = S A */
+#define SK_VARIANT_FLAT 2u  /* one global atomic per contribution */
+#define SK_VARIANT_LDS  4u  /* LDS-privatized partial sketches (default when
+                               the d x slice partial fits in LDS) */
+
+/*
+ * sk_meta_generate: routing and sign metadata of a SparseStack sketch.
+ * (FP16 sketching page §III-C: the metadata is made once per sketch by a
+ * coupled Philox kernel and stored as contiguous int32 and FP32 arrays of
+ * length m*zeta; every apply kernel consumes it.)
+ *
+ * For global row g = row_offset + i (0 <= i < m) and stack block
+ * t (0 <= t < zeta), let (w0, w1, w2, w3) = Philox-4x32-10 (Salmon et al.,
+ * SC'11) of counter (g mod 2^32, g >> 32, t div 4, 0) and key
+ * (seed mod 2^32, seed >> 32), and w = w_{t mod 4}.  Then
+ *     row_idx[i*zeta + t] = t*(d/zeta) + floor(w * (d/zeta) / 2^32)
+ *     val[i*zeta + t]     = (w & 1 ? -1 : +1) * float32(1/sqrt(zeta))
+ * The counter is the GLOBAL row, so metadata for rows [r0, r0+m) equals
+ * the slice of the whole matrix's metadata: a matrix sketched chunk by
+ * chunk with SK_ACCUMULATE gives the same S as in one call.
+ *
+ *   seed       64-bit sketch seed.
+ *   row_offset first global row (>= 0).
+ *   m          rows (>= 0), d output rows (>= 1), 1 <= zeta <= d, d % zeta == 0.
+ *   row_idx    device int32[m*zeta] (written).
+ *   val        device float[m*zeta] (written).
+ * Errors: SK_ERR_SHAPE on bad sizes, SK_ERR_NULL on NULL outputs with m > 0.
+ */
+sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t d,
+                           int32_t zeta, int32_t *row_idx, float *val, void *stream);
+
+/*
+ * sk_apply_f32: B = S A (or B += S A) in FP32 from the metadata above.
+ * (FP16 sketching page §III-A: every input row contributes a*val to zeta
+ * output rows; A is read once and reused over the zeta loop.)
+ *
+ *   A        device float, m x n, lda >= n.
+ *   row_idx, val  device metadata of length m*zeta (sk_meta_generate's
+ *            layout).  Entries with row_idx outside [0, d) contribute
+ *            nothing.
+ *   B        device float, d x n, ldb >= n.
+ *   flags    SK_ACCUMULATE, and at most one of SK_VARIANT_FLAT (one global
+ *            FP32 atomic add per contribution: the flat scatter) or
+ *            SK_VARIANT_LDS (per-workgroup FP32 partials in LDS, flushed with
+ *            global atomics).  0 picks LDS when it fits, else FLAT.
+ * FP32 additions happen in an unspecified order (atomics).
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE (n, d < 1, zeta range, d % zeta,
+ * lda/ldb < n), SK_ERR_ARG (both variants, aliasing), SK_ERR_UNSUPPORTED
+ * (SK_VARIANT_LDS forced where the partial cannot fit in LDS).
+ */
+sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda,
+                       const int32_t *row_idx, const float *val, int32_t zeta,
+                       float *B, int32_t d, int64_t ldb, uint32_t flags, void *stream);
+
+/*
+ * sk_apply_f16acc: FP16-accumulated sketch.
+ * (FP16 sketching page §III-B, §III-C, §III-D: inputs and signed products
+ * stay FP32; each contribution is converted to FP16 with round-to-nearest-
+ * even, subnormals kept; two adjacent columns are accumulated together by a
+ * packed f16x2 addition whose result is discarded, each half rounded to
+ * nearest-even; the sketch is stored in FP16.)
+ *
+ *   A        device float, m x n; n even, lda even, A 8-byte aligned.
+ *   B        device IEEE binary16 bits (uint16), d x n; ldb even, B 4-byte
+ *            aligned.  Overflow gives +-inf, inf + -inf gives NaN.
+ *   flags    as for sk_apply_f32.  SK_VARIANT_FLAT is the page's design: one
+ *            packed global atomic per contribution pair.  SK_VARIANT_LDS (the
+ *            default) accumulates FP16 partials of row chunks in LDS with
+ *            packed LDS atomics and adds each partial to B with packed global
+ *            atomics: the same RN operations in a two-level order.
+ * Errors: as sk_apply_f32, plus SK_ERR_SHAPE for odd n and SK_ERR_ALIGN for
+ * odd lda/ldb or misaligned A/B.
+ */
+sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
+                          const int32_t *row_idx, const float *val, int32_t zeta,
+                          uint16_t *B, int32_t d, int64_t ldb, uint32_t flags,
+                          void *stream);
+
+/*
+ * sk_apply_blockperm: Y = S A (or Y += S A) for S ~ BlockPerm-SJLT.
+ * (FlashSketch page §4: input rows in M contiguous blocks of B_c = m/M,
+ * output rows in M blocks of B_r = d/M; output block g reads the kappa input
+ * blocks of N(g), a union of kappa edge-disjoint permutations; inside a
+ * wired block pair each input row goes to s hashed output rows with
+ * Rademacher signs; each block is scaled so each nonzero is
+ * +-1/sqrt(kappa*s).  §5: S is never stored; wiring and hashes are made on
+ * the fly, accumulation is private to a workgroup in LDS, each output tile is
+ * written once and there are no global atomics.)
+ *
+ * Wiring: pi_j(g) = (sigma(g) + j*M/kappa) mod M, j = 0..kappa-1, with sigma
+ * the Fisher-Yates permutation of [M] whose swap partner for k = M-1..1 is
+ * floor(w0*(k+1)/2^32), w0 the first word of Philox-4x32-10 of counter
+ * (k, 0, 0, 2) and key (seed lo, seed hi).
+ * Hash: with fmix32 the MurmurHash3 32-bit finalizer and
+ * c(H, x) = fmix32(H ^ x) + 0x9E3779B9, the block key is
+ * K(g,h) = c(c(c(c(0x9E3779B9, seed lo), seed hi), g), h); input row r of
+ * block h (0 <= r < B_c) goes to output row g*B_r + floor(v*B_r/2^32) of
+ * output block g with sign (v & 1 ? -1 : +1), v = fmix32(K(g,h) ^ r).
+ *
+ *   A      device float, m x n, lda >= n.  Y device float, d x n, ldy >= n.
+ *   M      blocks (1..1024), m % M == 0, d % M == 0, kappa | M.
+ *   s      nonzeros per column inside a block; only s = 1 is built
+ *          (SK_ERR_UNSUPPORTED otherwise).
+ *   flags  SK_ACCUMULATE only.
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_UNSUPPORTED (s != 1, or a
+ * kappa*B_r tile too large for LDS), SK_ERR_ARG (other flags, aliasing).
+ */
+sk_status sk_apply_blockperm(const float *A, int64_t m, int32_t n, int64_t lda,
+                             int32_t d, int32_t M, int32_t kappa, int32_t s,
+                             uint64_t seed, float *Y, int64_t ldy, uint32_t flags,
+                             void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *sk_status_string(sk_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SK_SKETCH_H */

@@ -1,0 +1,188 @@
+"""Python binding of libsksketch (the C ABI declared in include/sk.h).
+
+Argument marshalling only: every step of the sketch runs in the library's
+HIP kernels.  torch supplies device memory (tensors) and the stream
+(torch.cuda.current_stream() unless one is given).  The low-level functions
+carry the C names and take tensors or raw device addresses; the helpers
+below them allocate outputs with torch and call those functions.
+
+The library is loaded from this package directory on first use; when it is
+missing or was built for another device the call fails loudly.  There is no
+CPU fallback.
+"""
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsksketch.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "sk.h")
+
+SK_OK, SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ALIGN, SK_ERR_UNSUPPORTED, SK_ERR_HIP, SK_ERR_ARG = range(7)
+SK_ACCUMULATE = 1
+SK_VARIANT_FLAT = 2
+SK_VARIANT_LDS = 4
+
+_c = ctypes
+_SIGNATURES = {
+    "sk_meta_generate": (_c.c_int, [_c.c_uint64, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32,
+                                     _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "sk_apply_f32": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
+                                _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
+                                _c.c_uint32, _c.c_void_p]),
+    "sk_apply_f16acc": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
+                                   _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
+                                   _c.c_uint32, _c.c_void_p]),
+    "sk_apply_blockperm": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32,
+                                      _c.c_int32, _c.c_int32, _c.c_int32, _c.c_uint64, _c.c_void_p,
+                                      _c.c_int64, _c.c_uint32, _c.c_void_p]),
+    "sk_status_string": (_c.c_char_p, [_c.c_int]),
+}
+
+_lib = None
+
+
+class SketchError(RuntimeError):
+    """A non-zero sk_status returned by the library."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+def load(path=LIB_PATH):
+    """Load libsksketch.so and bind every entry point (idempotent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m sparse_sketching_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_symbols(header=HEADER):
+    """Names of the functions declared in include/sk.h."""
+    with open(header) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sk_\w+)\s*\(", text)))
+
+
+def status_string(status):
+    try:
+        return load().sk_status_string(int(status)).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status):
+    if status != SK_OK:
+        raise SketchError(fn, status)
+
+
+# ---- the C entry points, same names and argument order -------------------
+
+def sk_meta_generate(seed, row_offset, m, d, zeta, row_idx, val, stream=None):
+    _check("sk_meta_generate", load().sk_meta_generate(
+        seed, row_offset, m, d, zeta, _ptr(row_idx), _ptr(val), _stream(stream)))
+
+
+def sk_apply_f32(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, stream=None):
+    _check("sk_apply_f32", load().sk_apply_f32(
+        _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, flags,
+        _stream(stream)))
+
+
+def sk_apply_f16acc(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, stream=None):
+    _check("sk_apply_f16acc", load().sk_apply_f16acc(
+        _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, flags,
+        _stream(stream)))
+
+
+def sk_apply_blockperm(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags=0, stream=None):
+    _check("sk_apply_blockperm", load().sk_apply_blockperm(
+        _ptr(A), m, n, lda, d, M, kappa, s, seed, _ptr(Y), ldy, flags, _stream(stream)))
+
+
+# ---- tensor helpers ------------------------------------------------------
+
+def _need_device(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() == 2 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major with unit column stride")
+
+
+def meta(seed, m, d, zeta, row_offset=0, device=None, stream=None):
+    """(row_idx int32[m*zeta], val float32[m*zeta]) on the device."""
+    import torch
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    row_idx = torch.empty(m * zeta, dtype=torch.int32, device=device)
+    val = torch.empty(m * zeta, dtype=torch.float32, device=device)
+    sk_meta_generate(seed, row_offset, m, d, zeta, row_idx, val, stream)
+    return row_idx, val
+
+
+def apply(A, row_idx, val, zeta, d, precision="f16acc", out=None, flags=0, stream=None):
+    """B = S A from metadata; precision "f32" (float32 B) or "f16acc" (float16 B)."""
+    import torch
+    _need_device(A, torch.float32, "A")
+    m, n = A.shape
+    dt = torch.float16 if precision == "f16acc" else torch.float32
+    if out is None:
+        out = torch.empty((d, n), dtype=dt, device=A.device)
+    _need_device(out, dt, "out")
+    if m:
+        _need_device(row_idx, torch.int32, "row_idx")
+        _need_device(val, torch.float32, "val")
+        if row_idx.numel() < m * zeta or val.numel() < m * zeta:
+            raise ValueError("metadata shorter than m*zeta")
+    fn = sk_apply_f16acc if precision == "f16acc" else sk_apply_f32
+    fn(A, m, n, A.stride(0) if m else n, row_idx if m else None, val if m else None, zeta,
+       out, d, out.stride(0), flags, stream)
+    return out
+
+
+def sketch(A, d, zeta, seed, precision="f16acc", flags=0, stream=None):
+    """Complete sketch: metadata generation, output zeroing and application."""
+    row_idx, val = meta(seed, A.shape[0], d, zeta, device=A.device, stream=stream)
+    return apply(A, row_idx, val, zeta, d, precision, flags=flags, stream=stream)
+
+
+def blockperm(A, d, M, kappa, seed, s=1, out=None, flags=0, stream=None):
+    """Y = S A for S ~ BlockPerm-SJLT (float32)."""
+    import torch
+    _need_device(A, torch.float32, "A")
+    m, n = A.shape
+    if out is None:
+        out = torch.empty((d, n), dtype=torch.float32, device=A.device)
+    _need_device(out, torch.float32, "out")
+    sk_apply_blockperm(A, m, n, A.stride(0), d, M, kappa, s, seed, out, out.stride(0), flags,
+                       stream)
+    return out

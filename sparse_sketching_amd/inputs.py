@@ -15,7 +15,11 @@ Workloads (shapes and distributions of the FP16 sketching page's grids,
   most of the column-space energy (§V-C coherence study).
 * ``range_stress(m, n, k)``: N(0, 1) rows times lognormal(0, 2) row scales
   (exp(2Z), Z ~ N(0, 1)), times the common factor 2^k (§V-E rescaling).
-* ``orth(A)``: U = Q of the fp64 thin QR of A, stored as FP32.
+* ``orth(A)``: an orthonormal basis U of range(A) (fp64 Cholesky QR, two
+  passes), stored as FP32.
+* ``*_torch`` variants draw the same kind of input on the device with
+  torch's seeded generator (used for the largest workloads, where host
+  generation would dominate test time); their host copies feed the oracle.
 """
 import numpy as np
 
@@ -56,8 +60,34 @@ def range_stress(m, n, k, seed=0):
 
 
 def orth(A):
-    Q, _ = np.linalg.qr(np.asarray(A, dtype=np.float64), mode="reduced")
+    """Orthonormal basis of range(A): two passes of Cholesky QR in fp64
+    (accurate for the well-conditioned workloads here), stored as FP32."""
+    Q = np.asarray(A, dtype=np.float64)
+    for _ in range(2):
+        R = np.linalg.cholesky(Q.T @ Q).T
+        Q = np.linalg.solve(R.T, Q.T).T
     return Q.astype(np.float32)
+
+
+def orth_torch(A):
+    """orth() on the device with torch (fp64 Cholesky QR, two passes)."""
+    import torch
+    Q = A.to(torch.float64)
+    for _ in range(2):
+        L = torch.linalg.cholesky(Q.T @ Q)
+        Q = torch.linalg.solve_triangular(L, Q.T, upper=False).T
+    return Q.to(torch.float32).contiguous()
+
+
+def coherent_torch(m, n, seed=0, head=1e3, device="cuda"):
+    """coherent() drawn on the device with torch's seeded generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    A = torch.randn((m, n), generator=g, device=device, dtype=torch.float32)
+    p = torch.randperm(m, generator=g, device=device)[:n]
+    A[p, torch.arange(n, device=device)] += head
+    return A
 
 
 def gaussian_torch(m, n, seed=0, device="cuda"):

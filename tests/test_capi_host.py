@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/sk.h declares, and rejects invalid arguments before it
+makes any HIP call."""
+import ctypes
+
+import pytest
+
+from sparse_sketching_amd import binding as b
+
+FAKE = 1 << 40          # never dereferenced: validation fails before any use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return b.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = b.header_symbols()
+    assert set(names) == {"sk_meta_generate", "sk_apply_f32", "sk_apply_f16acc",
+                          "sk_apply_blockperm", "sk_status_string"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.sk_status_string(s)
+    assert b.status_string(b.SK_ERR_ALIGN) == "misaligned buffer or stride"
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((1, 0, -1, 64, 4, FAKE, FAKE + 4096), b.SK_ERR_SHAPE),      # m < 0
+    ((1, -5, 10, 64, 4, FAKE, FAKE + 4096), b.SK_ERR_SHAPE),     # row_offset < 0
+    ((1, 0, 10, 64, 3, FAKE, FAKE + 4096), b.SK_ERR_SHAPE),      # d % zeta
+    ((1, 0, 10, 4, 8, FAKE, FAKE + 4096), b.SK_ERR_SHAPE),       # zeta > d
+    ((1, 0, 10, 64, 0, FAKE, FAKE + 4096), b.SK_ERR_SHAPE),      # zeta < 1
+    ((1, 0, 10, 64, 4, None, FAKE), b.SK_ERR_NULL),
+    ((1, 0, 10, 64, 4, FAKE, None), b.SK_ERR_NULL),
+    ((1, 0, 10, 64, 4, FAKE, FAKE + 8), b.SK_ERR_ARG),            # outputs overlap
+    ((1, 0, 0, 64, 4, None, None), b.SK_OK),                     # empty: nothing to do
+])
+def test_meta_validation(lib, args, expect):
+    assert lib.sk_meta_generate(*args, None) == expect
+
+
+A, RI, V, B = FAKE, FAKE + (1 << 34), FAKE + (1 << 35), FAKE + (1 << 36)
+
+
+@pytest.mark.parametrize("fn", ["sk_apply_f32", "sk_apply_f16acc"])
+@pytest.mark.parametrize("args,expect", [
+    ((A, 100, 0, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_SHAPE),      # n < 1
+    ((A, 100, 64, 32, RI, V, 4, B, 64, 64, 0), b.SK_ERR_SHAPE),     # lda < n
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 32, 0), b.SK_ERR_SHAPE),     # ldb < n
+    ((A, 100, 64, 64, RI, V, 3, B, 64, 64, 0), b.SK_ERR_SHAPE),     # d % zeta
+    ((A, -1, 64, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_SHAPE),
+    ((A, 100, 64, 64, RI, V, 4, B, 0, 64, 0), b.SK_ERR_SHAPE),      # d < 1
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 6), b.SK_ERR_ARG),       # FLAT|LDS
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 8), b.SK_ERR_ARG),       # unknown flag
+    ((None, 100, 64, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_NULL),
+    ((A, 100, 64, 64, None, V, 4, B, 64, 64, 0), b.SK_ERR_NULL),
+    ((A, 100, 64, 64, RI, None, 4, B, 64, 64, 0), b.SK_ERR_NULL),
+    ((A, 100, 64, 64, RI, V, 4, None, 64, 64, 0), b.SK_ERR_NULL),
+    ((A, 100, 64, 64, RI, V, 4, A + 256, 64, 64, 0), b.SK_ERR_ARG),  # B inside A
+    ((A, 100, 64, 64, RI, V, 4, RI + 64, 64, 64, 0), b.SK_ERR_ARG),  # B inside metadata
+])
+def test_apply_validation(lib, fn, args, expect):
+    assert getattr(lib, fn)(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 100, 63, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_SHAPE),     # odd n
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 65, 0), b.SK_ERR_ALIGN),     # odd ldb
+    ((A, 100, 64, 64, RI, V, 4, B + 2, 64, 64, 0), b.SK_ERR_ALIGN), # B not 4-byte aligned
+    ((A, 100, 64, 65, RI, V, 4, B, 64, 64, 0), b.SK_ERR_ALIGN),     # odd lda
+    ((A + 4, 100, 64, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_ALIGN), # A not 8-byte aligned
+])
+def test_f16acc_pair_rules(lib, args, expect):
+    assert lib.sk_apply_f16acc(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 1000, 64, 64, 64, 64, 4, 1, 7, B, 64, 0), b.SK_ERR_SHAPE),    # m % M
+    ((A, 1024, 64, 64, 60, 64, 4, 1, 7, B, 64, 0), b.SK_ERR_SHAPE),    # d % M
+    ((A, 1024, 64, 64, 64, 64, 3, 1, 7, B, 64, 0), b.SK_ERR_SHAPE),    # kappa does not divide M
+    ((A, 1024, 64, 32, 64, 64, 4, 1, 7, B, 64, 0), b.SK_ERR_SHAPE),    # lda < n
+    ((A, 1024, 64, 64, 64, 64, 4, 1, 7, B, 32, 0), b.SK_ERR_SHAPE),    # ldy < n
+    ((A, 1024, 64, 64, 64, 64, 4, 2, 7, B, 64, 0), b.SK_ERR_SHAPE),    # s > B_r = 1
+    ((A, 1024, 64, 64, 128, 64, 4, 2, 7, B, 64, 0), b.SK_ERR_UNSUPPORTED),  # s = 2
+    ((A, 2048, 64, 64, 2048, 2048, 4, 1, 7, B, 64, 0), b.SK_ERR_UNSUPPORTED),  # M too large
+    ((A, 1024, 64, 64, 64, 64, 4, 1, 7, B, 64, 2), b.SK_ERR_ARG),      # variant flag
+    ((None, 1024, 64, 64, 64, 64, 4, 1, 7, B, 64, 0), b.SK_ERR_NULL),
+    ((A, 1024, 64, 64, 64, 64, 4, 1, 7, None, 64, 0), b.SK_ERR_NULL),
+    ((A, 1024, 64, 64, 64, 64, 4, 1, 7, A + 64, 64, 0), b.SK_ERR_ARG),
+    ((A, 0, 64, 64, 64, 64, 4, 1, 7, B, 64, 0), b.SK_ERR_SHAPE),
+])
+def test_blockperm_validation(lib, args, expect):
+    assert lib.sk_apply_blockperm(*args, None) == expect
+
+
+def test_figure2_shape_is_accepted_up_to_s(lib):
+    # FlashSketch Figure 2: M=16, B_r=64, B_c=128, kappa=4, s=2 (d_in=2048, k=1024):
+    # the shapes validate; s=2 is a valid request this library does not build.
+    assert lib.sk_apply_blockperm(A, 2048, 64, 64, 1024, 16, 4, 2, 7, B, 64, 0, None) == \
+        b.SK_ERR_UNSUPPORTED
