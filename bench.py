@@ -120,41 +120,47 @@ def main():
     B16 = torch.empty((d, n), dtype=torch.float16, device=dev)
     B32 = torch.empty((d, n), dtype=torch.float32, device=dev)
 
+    ws16 = b.workspace(A, d, zeta, "f16acc")
+    ws32 = b.workspace(A, d, zeta, "f32")
+
     def meta():
         b.sk_meta_generate(SEED, 0, m, d, zeta, ri, val, sp)
 
-    def f16(flags=0):
-        b.sk_apply_f16acc(A, m, n, n, ri, val, zeta, B16, d, n, flags, sp)
+    def f16(flags=0, ws=ws16):
+        b.sk_apply_f16acc(A, m, n, n, ri, val, zeta, B16, d, n, flags, ws, 0, sp)
 
-    def f32(flags=0):
-        b.sk_apply_f32(A, m, n, n, ri, val, zeta, B32, d, n, flags, sp)
+    def f32(flags=0, ws=ws32):
+        b.sk_apply_f32(A, m, n, n, ri, val, zeta, B32, d, n, flags, ws, 0, sp)
 
     if args.profile_pass:
         meta()
         for _ in range(3):
-            f16(b.SK_ACCUMULATE)
+            f16()
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)                          # 1 GiB read + 1 GiB write
         torch.cuda.synchronize()
-        print("profile pass done: 3 x f16 LDS apply (accumulate), 3 x 1 GiB copy", flush=True)
+        print("profile pass done: 3 x f16 LDS apply + reduce, 3 x 1 GiB copy", flush=True)
         return
 
     K, W = args.steps, args.warmup
     bytes16 = sparsestack_bytes(m, n, d, zeta, 2)
     bytes32 = sparsestack_bytes(m, n, d, zeta, 4)
 
-    # headline step: complete FP16-accumulate sketch
+    # headline step: complete FP16-accumulate sketch (metadata, then the LDS
+    # apply whose store-and-reduce flush also initializes B)
     ms16 = timed(lambda: (meta(), f16()), K, W, stream)
     print(f"[bench] f16acc complete sketch {ms16:.4f} ms", file=sys.stderr, flush=True)
-    ms32_flat = timed(lambda: (meta(), f32(b.SK_VARIANT_FLAT)), K, W, stream)
-    ms32_lds = timed(lambda: (meta(), f32(b.SK_VARIANT_LDS)), K, W, stream)
-    ms16_flat = timed(lambda: (meta(), f16(b.SK_VARIANT_FLAT)), max(1, K // 4), 1, stream)
-    print(f"[bench] f32 flat {ms32_flat:.4f} ms, f32 lds {ms32_lds:.4f} ms, "
-          f"f16 flat {ms16_flat:.4f} ms", file=sys.stderr, flush=True)
-    # the dominant kernel alone: SK_ACCUMULATE skips the zeroing launch
+    ms16_atomic = timed(lambda: (meta(), f16(0, None)), K, W, stream)
+    ms32_flat = timed(lambda: (meta(), f32(b.SK_VARIANT_FLAT, None)), K, W, stream)
+    ms32_lds = timed(lambda: (meta(), f32()), K, W, stream)
+    ms16_flat = timed(lambda: (meta(), f16(b.SK_VARIANT_FLAT, None)), max(1, K // 4), 1, stream)
+    print(f"[bench] f16 lds+atomic flush {ms16_atomic:.4f} ms, f32 flat {ms32_flat:.4f} ms, "
+          f"f32 lds {ms32_lds:.4f} ms, f16 flat {ms16_flat:.4f} ms", file=sys.stderr, flush=True)
+    # the apply alone (apply kernel + its reduce), and the metadata kernel alone
     ms_kernel = timed(lambda: f16(b.SK_ACCUMULATE), K, W, stream)
+    ms_kernel_atomic = timed(lambda: f16(b.SK_ACCUMULATE, None), K, W, stream)
     ms_meta = timed(meta, K, W, stream)
     # device copy bandwidth for context
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -162,11 +168,13 @@ def main():
     ms_copy = timed(lambda: dst.copy_(src), K, 2, stream)
     copy_gbs = 2 * src.numel() * 4 / ms_copy / 1e6
     del src, dst
+    print(f"[bench] apply+reduce {ms_kernel:.4f} ms, apply(atomic flush) {ms_kernel_atomic:.4f} ms, "
+          f"meta {ms_meta:.4f} ms, copy {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
     A_host = None if args.no_cpu_baseline else A.cpu().numpy()
     bp = None
     if not args.no_blockperm:
-        del A, ri, val
+        del A, ri, val, ws16, ws32
         torch.cuda.empty_cache()
         Abp = inputs.gaussian_torch(BP_M, BP_N, seed=0)
         Y = torch.empty((BP_D, BP_N), dtype=torch.float32, device=dev)
@@ -176,6 +184,7 @@ def main():
         bp = {"workload": f"BlockPerm-SJLT m=2^21 n={BP_N} d={BP_D} M={BP_BLOCKS} "
                           f"kappa={BP_KAPPA} s=1", "ms": round(ms_bp, 4),
               "GBps": round(gbs_bp, 1), "hbm_frac": round(gbs_bp / HBM_PEAK_GBS, 4)}
+        print(f"[bench] blockperm {ms_bp:.4f} ms {gbs_bp:.0f} GB/s", file=sys.stderr, flush=True)
         del Abp, Y
 
     gbs16 = bytes16 / ms16 / 1e6
@@ -201,6 +210,7 @@ def main():
         "fp32_flat_GBps": round(bytes32 / ms32_flat / 1e6, 2),
         "fp32_lds_ms": round(ms32_lds, 5),
         "fp16_flat_ms": round(ms16_flat, 5),
+        "fp16_lds_atomic_flush_ms": round(ms16_atomic, 5),
         "speedup_vs_fp32_flat": round(ms32_flat / ms16, 3),
         "speedup_vs_fp32_lds": round(ms32_lds / ms16, 3),
         "meta_ms": round(ms_meta, 5),
@@ -208,8 +218,9 @@ def main():
         "blockperm": bp,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "k_f16_lds<64,4>",
-                     "kernel_ms": round(ms_kernel, 5)},
+                     "traffic": None, "kernel": "k_lock_apply<AccF16,4> + k_lock_reduce<AccF16>",
+                     "kernel_ms": round(ms_kernel, 5),
+                     "apply_atomic_flush_ms": round(ms_kernel_atomic, 5)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -39,6 +39,7 @@
 #ifndef SK_SKETCH_H
 #define SK_SKETCH_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -60,6 +61,10 @@ typedef enum sk_status {
 #define SK_VARIANT_FLAT 2u  /* one global atomic per contribution */
 #define SK_VARIANT_LDS  4u  /* LDS-privatized partial sketches (default when
                                the d x slice partial fits in LDS) */
+
+/* precision argument of sk_apply_workspace_size */
+#define SK_PRECISION_F32    0
+#define SK_PRECISION_F16ACC 1
 
 /*
  * sk_meta_generate: routing and sign metadata of a SparseStack sketch.
@@ -97,42 +102,72 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
  *            layout).  Entries with row_idx outside [0, d) contribute
  *            nothing.
  *   B        device float, d x n, ldb >= n.
- *   flags    SK_ACCUMULATE, and at most one of SK_VARIANT_FLAT (one global
- *            FP32 atomic add per contribution: the flat scatter) or
- *            SK_VARIANT_LDS (per-workgroup FP32 partials in LDS, flushed with
- *            global atomics).  0 picks LDS when it fits, else FLAT.
- * FP32 additions happen in an unspecified order (atomics).
+ *   flags    SK_ACCUMULATE, and at most one of
+ *              SK_VARIANT_FLAT: one no-return global FP32 atomic add per
+ *                contribution (the page's scatter; the in-house baseline);
+ *              SK_VARIANT_LDS: each workgroup keeps a private d x slice FP32
+ *                partial in LDS, updated by plain read-add-write under
+ *                per-row LDS locks, and flushes it once.
+ *            0 picks LDS when the partial fits in LDS and zeta <= 64, else
+ *            FLAT.
+ *   workspace, workspace_bytes
+ *            optional device scratch for the LDS variant (4-byte aligned,
+ *            disjoint from every other buffer; size from
+ *            sk_apply_workspace_size).  With a workspace the partials are
+ *            stored there and a second kernel writes B as their sum, in a
+ *            fixed order (no global atomics, no separate zeroing of B).
+ *            NULL: partials are added to B with global atomics.  Ignored by
+ *            the FLAT variant.  The caller owns it; its contents on return
+ *            are unspecified.  Calls that share a workspace must be ordered
+ *            (same stream).
+ * FP32 additions happen in an unspecified order (atomics, LDS locks).
  * Errors: SK_ERR_NULL, SK_ERR_SHAPE (n, d < 1, zeta range, d % zeta,
- * lda/ldb < n), SK_ERR_ARG (both variants, aliasing), SK_ERR_UNSUPPORTED
- * (SK_VARIANT_LDS forced where the partial cannot fit in LDS).
+ * lda/ldb < n), SK_ERR_ARG (both variants, aliasing, workspace smaller than
+ * required), SK_ERR_ALIGN (workspace not 4-byte aligned),
+ * SK_ERR_UNSUPPORTED (SK_VARIANT_LDS forced where the partial cannot fit in
+ * LDS or zeta > 64).
  */
 sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda,
                        const int32_t *row_idx, const float *val, int32_t zeta,
-                       float *B, int32_t d, int64_t ldb, uint32_t flags, void *stream);
+                       float *B, int32_t d, int64_t ldb, uint32_t flags,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sk_apply_f16acc: FP16-accumulated sketch.
  * (FP16 sketching page §III-B, §III-C, §III-D: inputs and signed products
  * stay FP32; each contribution is converted to FP16 with round-to-nearest-
  * even, subnormals kept; two adjacent columns are accumulated together by a
- * packed f16x2 addition whose result is discarded, each half rounded to
- * nearest-even; the sketch is stored in FP16.)
+ * packed f16x2 addition, each half rounded to nearest-even; the sketch is
+ * stored in FP16.)
  *
  *   A        device float, m x n; n even, lda even, A 8-byte aligned.
  *   B        device IEEE binary16 bits (uint16), d x n; ldb even, B 4-byte
  *            aligned.  Overflow gives +-inf, inf + -inf gives NaN.
  *   flags    as for sk_apply_f32.  SK_VARIANT_FLAT is the page's design: one
- *            packed global atomic per contribution pair.  SK_VARIANT_LDS (the
- *            default) accumulates FP16 partials of row chunks in LDS with
- *            packed LDS atomics and adds each partial to B with packed global
- *            atomics: the same RN operations in a two-level order.
+ *            no-return packed global atomic per contribution pair.
+ *            SK_VARIANT_LDS (the default) accumulates FP16 partials of row
+ *            chunks in LDS (packed f16x2 words, nearest-even additions) and
+ *            then adds the partials to B: the same RN operations in a
+ *            two-level order.
+ *   workspace, workspace_bytes  as for sk_apply_f32.
  * Errors: as sk_apply_f32, plus SK_ERR_SHAPE for odd n and SK_ERR_ALIGN for
  * odd lda/ldb or misaligned A/B.
  */
 sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *row_idx, const float *val, int32_t zeta,
                           uint16_t *B, int32_t d, int64_t ldb, uint32_t flags,
-                          void *stream);
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sk_apply_workspace_size: bytes of workspace that sk_apply_f32
+ * (precision SK_PRECISION_F32) or sk_apply_f16acc (SK_PRECISION_F16ACC)
+ * uses for these sizes and flags on the current device; 0 when the chosen
+ * variant uses none (FLAT, m = 0, or an LDS plan that does not fit).
+ * Errors: SK_ERR_NULL (bytes NULL), SK_ERR_SHAPE, SK_ERR_ARG (precision or
+ * flags), SK_ERR_HIP (device query failed).
+ */
+sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32_t d,
+                                  int32_t zeta, uint32_t flags, size_t *bytes);
 
 /*
  * sk_apply_blockperm: Y = S A (or Y += S A) for S ~ BlockPerm-SJLT.

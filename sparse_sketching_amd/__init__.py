@@ -5,10 +5,12 @@ The compute path is libsksketch.so (hand-written HIP kernels behind the C ABI
 of include/sk.h); ``binding`` marshals torch tensors into it.  ``inputs``
 draws the seeded synthetic workloads.
 """
-from .binding import (SK_ACCUMULATE, SK_VARIANT_FLAT, SK_VARIANT_LDS, SketchError, apply,
-                      blockperm, load, meta, sk_apply_blockperm, sk_apply_f16acc, sk_apply_f32,
-                      sk_meta_generate, sketch, status_string)
+from .binding import (SK_ACCUMULATE, SK_PRECISION_F16ACC, SK_PRECISION_F32, SK_VARIANT_FLAT,
+                      SK_VARIANT_LDS, SketchError, apply, blockperm, load, meta,
+                      sk_apply_blockperm, sk_apply_f16acc, sk_apply_f32, sk_apply_workspace_size,
+                      sk_meta_generate, sketch, status_string, workspace)
 
-__all__ = ["SK_ACCUMULATE", "SK_VARIANT_FLAT", "SK_VARIANT_LDS", "SketchError", "apply",
-           "blockperm", "load", "meta", "sk_apply_blockperm", "sk_apply_f16acc", "sk_apply_f32",
-           "sk_meta_generate", "sketch", "status_string"]
+__all__ = ["SK_ACCUMULATE", "SK_PRECISION_F16ACC", "SK_PRECISION_F32", "SK_VARIANT_FLAT",
+           "SK_VARIANT_LDS", "SketchError", "apply", "blockperm", "load", "meta",
+           "sk_apply_blockperm", "sk_apply_f16acc", "sk_apply_f32", "sk_apply_workspace_size",
+           "sk_meta_generate", "sketch", "status_string", "workspace"]

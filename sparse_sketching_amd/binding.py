@@ -22,6 +22,8 @@ SK_OK, SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ALIGN, SK_ERR_UNSUPPORTED, SK_ERR_HIP, 
 SK_ACCUMULATE = 1
 SK_VARIANT_FLAT = 2
 SK_VARIANT_LDS = 4
+SK_PRECISION_F32 = 0
+SK_PRECISION_F16ACC = 1
 
 _c = ctypes
 _SIGNATURES = {
@@ -29,10 +31,12 @@ _SIGNATURES = {
                                      _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "sk_apply_f32": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
                                 _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
-                                _c.c_uint32, _c.c_void_p]),
+                                _c.c_uint32, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "sk_apply_f16acc": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
                                    _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
-                                   _c.c_uint32, _c.c_void_p]),
+                                   _c.c_uint32, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "sk_apply_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32,
+                                           _c.c_int32, _c.c_uint32, _c.POINTER(_c.c_size_t)]),
     "sk_apply_blockperm": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32,
                                       _c.c_int32, _c.c_int32, _c.c_int32, _c.c_uint64, _c.c_void_p,
                                       _c.c_int64, _c.c_uint32, _c.c_void_p]),
@@ -89,6 +93,17 @@ def _ptr(x):
     return x.data_ptr()
 
 
+def _nbytes(buf, nbytes):
+    """Byte size of a workspace given as a tensor (its storage) or an address."""
+    if buf is None:
+        return 0
+    if nbytes:
+        return nbytes
+    if isinstance(buf, int):
+        raise ValueError("a raw workspace address needs workspace_bytes")
+    return buf.numel() * buf.element_size()
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -110,16 +125,26 @@ def sk_meta_generate(seed, row_offset, m, d, zeta, row_idx, val, stream=None):
         seed, row_offset, m, d, zeta, _ptr(row_idx), _ptr(val), _stream(stream)))
 
 
-def sk_apply_f32(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, stream=None):
+def sk_apply_f32(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, workspace=None,
+                 workspace_bytes=0, stream=None):
     _check("sk_apply_f32", load().sk_apply_f32(
         _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, flags,
-        _stream(stream)))
+        _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)))
 
 
-def sk_apply_f16acc(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, stream=None):
+def sk_apply_f16acc(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, workspace=None,
+                    workspace_bytes=0, stream=None):
     _check("sk_apply_f16acc", load().sk_apply_f16acc(
         _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, flags,
-        _stream(stream)))
+        _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def sk_apply_workspace_size(precision, m, n, d, zeta, flags=0):
+    """Bytes of workspace the apply call uses (0: none)."""
+    out = ctypes.c_size_t(0)
+    _check("sk_apply_workspace_size", load().sk_apply_workspace_size(
+        precision, m, n, d, zeta, flags, ctypes.byref(out)))
+    return out.value
 
 
 def sk_apply_blockperm(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags=0, stream=None):
@@ -149,8 +174,23 @@ def meta(seed, m, d, zeta, row_offset=0, device=None, stream=None):
     return row_idx, val
 
 
-def apply(A, row_idx, val, zeta, d, precision="f16acc", out=None, flags=0, stream=None):
-    """B = S A from metadata; precision "f32" (float32 B) or "f16acc" (float16 B)."""
+def workspace(A, d, zeta, precision="f16acc", flags=0):
+    """A device byte tensor large enough for apply()'s store-and-reduce flush
+    (None when the chosen variant needs none)."""
+    import torch
+    prec = SK_PRECISION_F16ACC if precision == "f16acc" else SK_PRECISION_F32
+    nbytes = sk_apply_workspace_size(prec, A.shape[0], A.shape[1], d, zeta, flags)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=A.device)
+
+
+def apply(A, row_idx, val, zeta, d, precision="f16acc", out=None, flags=0, ws=True, stream=None):
+    """B = S A from metadata; precision "f32" (float32 B) or "f16acc" (float16 B).
+
+    ws=True allocates the workspace the LDS variant uses for its
+    store-and-reduce flush; ws=None makes it flush with global atomics; a
+    byte tensor is used as the workspace."""
     import torch
     _need_device(A, torch.float32, "A")
     m, n = A.shape
@@ -163,16 +203,18 @@ def apply(A, row_idx, val, zeta, d, precision="f16acc", out=None, flags=0, strea
         _need_device(val, torch.float32, "val")
         if row_idx.numel() < m * zeta or val.numel() < m * zeta:
             raise ValueError("metadata shorter than m*zeta")
+    if ws is True:
+        ws = workspace(A, d, zeta, precision, flags)
     fn = sk_apply_f16acc if precision == "f16acc" else sk_apply_f32
     fn(A, m, n, A.stride(0) if m else n, row_idx if m else None, val if m else None, zeta,
-       out, d, out.stride(0), flags, stream)
+       out, d, out.stride(0), flags, ws, 0, stream)
     return out
 
 
-def sketch(A, d, zeta, seed, precision="f16acc", flags=0, stream=None):
-    """Complete sketch: metadata generation, output zeroing and application."""
+def sketch(A, d, zeta, seed, precision="f16acc", flags=0, ws=True, stream=None):
+    """Complete sketch: metadata generation, output initialization and application."""
     row_idx, val = meta(seed, A.shape[0], d, zeta, device=A.device, stream=stream)
-    return apply(A, row_idx, val, zeta, d, precision, flags=flags, stream=stream)
+    return apply(A, row_idx, val, zeta, d, precision, flags=flags, ws=ws, stream=stream)
 
 
 def blockperm(A, d, M, kappa, seed, s=1, out=None, flags=0, stream=None):

@@ -6,17 +6,20 @@
 // and kappa input blocks.  One workgroup owns one component and one 32-column
 // tile: it reads each input row of its kappa input blocks exactly once,
 // hashes the row for each of the component's kappa output blocks on the fly
-// (no stored S, §5.2), accumulates into a private kappa*B_r x 32 FP32 tile in
-// LDS with LDS atomics (§5.1), and writes every output element once with a
-// plain store: no global atomics.  (The page's own grid gives each output
-// block its own thread block, which reads each input block kappa times; the
-// component grid reads A once.)
+// (no stored S, §5.2), accumulates in LDS (§5.1), and writes every output
+// element once with a plain store: no global atomics.  (The page's own grid
+// gives each output block its own thread block, which reads each input block
+// kappa times; the component grid reads A once.)
 //
-// Wave layout: a wavefront covers two rows x 32 columns per load (two
-// 128-byte segments); a batch is 64 rows, whose hashes lane k computes for
-// row k and the other lanes fetch with ds_bpermute.  The LDS tile keeps the
-// two half-waves in separate 32-word halves of a 64-word row, so the 64
-// lanes of one LDS atomic always hit 64 different banks.
+// LDS: gfx950 performs floating-point LDS atomics one lane at a time, so each
+// wavefront owns a private kappa*B_r x 64 FP32 tile and updates it with plain
+// read-add-write; the wave tiles are summed once at the end.  A wavefront
+// covers two rows x 32 columns per load (two 128-byte segments); the two
+// half-waves keep separate 32-word halves of each 64-word tile row, so the
+// 64 lanes of one update always touch 64 different words (and banks).
+// Hashes: lane k hashes row k of a 64-row batch for every output block of the
+// component; the half-waves pick up the packed (row, sign) entries of their
+// rows with v_readlane, leaving the LDS pipe to the tile updates.
 #include "sk_internal.hpp"
 #include "sk_apply_common.hpp"
 #include "sk_rng.hpp"
@@ -26,13 +29,14 @@ namespace {
 
 constexpr int kTile = 32;   // columns per workgroup
 constexpr int kBatch = 64;  // rows per wavefront batch
+constexpr int kMaxWaves = 8;
 
 template <int KAPPA>
-__global__ __launch_bounds__(1024) void k_blockperm(const BlockPermArgs args) {
-    extern __shared__ float acc[];           // (KAPPA*B_r) x 64 floats
+__global__ __launch_bounds__(kMaxWaves * 64) void k_blockperm(const BlockPermArgs args) {
+    extern __shared__ float acc[];            // nw x (KAPPA*B_r) x 64 floats
     __shared__ uint32_t keys[KAPPA * KAPPA];  // K(g_l, h_j) at [l*KAPPA + j]
     __shared__ int32_t gout[KAPPA];
-    constexpr int NPW = (KAPPA + 1) / 2;     // packed 16-bit entries per lane
+    constexpr int NPW = (KAPPA + 1) / 2;      // packed 16-bit entries per lane
     const int32_t Br = args.Br;
     const int32_t C = args.C;
     const int64_t Bc = args.Bc;
@@ -41,12 +45,14 @@ __global__ __launch_bounds__(1024) void k_blockperm(const BlockPermArgs args) {
     const int half = lane >> 5;
     const int32_t col = blockIdx.x * kTile + (lane & 31);
     const bool active = col < args.n;
+    const int32_t col_c = active ? col : args.n - 1;
     const int nthr = blockDim.x;
     const int nw = nthr >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int trows = KAPPA * Br;
+    float *tile = acc + (int64_t)wave * trows * 64 + lane;
 
-    for (int k = threadIdx.x; k < trows * 64; k += nthr) acc[k] = 0.f;
+    for (int k = threadIdx.x; k < nw * trows * 64; k += nthr) acc[k] = 0.f;
     if (threadIdx.x < KAPPA * KAPPA) {
         const int l = threadIdx.x / KAPPA, j = threadIdx.x % KAPPA;
         keys[threadIdx.x] = blockperm_key(args.seed, args.ginv[rho + l * C], (uint32_t)(rho + j * C));
@@ -61,17 +67,18 @@ __global__ __launch_bounds__(1024) void k_blockperm(const BlockPermArgs args) {
 #pragma unroll
         for (int l = 0; l < KAPPA; ++l) kj[l] = __builtin_amdgcn_readfirstlane(keys[l * KAPPA + j]);
         for (int64_t b = (int64_t)wave * kBatch; b < Bc; b += (int64_t)nw * kBatch) {
-            // uniform row base per pair of rows + one 32-bit lane offset: the
-            // loads take the scalar-base form and need no 64-bit addresses
+            // rows clamped into the block and columns into the matrix, so
+            // every load is in bounds and the loop is branch-free; values of
+            // rows past the block or columns past n are zeroed before use
             float a[kBatch / 2];
-            const uint32_t off = (uint32_t)(half * args.lda + col);
 #pragma unroll
             for (int q = 0; q < kBatch / 2; ++q) {
-                const float *pq = Ablk + (b + 2 * q) * args.lda;
                 const int64_t r = b + 2 * q + half;
-                a[q] = (active && r < Bc) ? pq[off] : 0.f;
+                const int64_t rc = r < Bc ? r : Bc - 1;
+                a[q] = Ablk[rc * args.lda + col_c];
             }
-            // lane k hashes row b + k for every output block of the component
+            // lane k hashes row b + k for every output block of the component:
+            // entry = tile row (l*B_r + bucket) | sign << 15
             const uint32_t rr = (uint32_t)(b + lane);
             uint32_t packed[NPW];
 #pragma unroll
@@ -84,20 +91,27 @@ __global__ __launch_bounds__(1024) void k_blockperm(const BlockPermArgs args) {
             }
 #pragma unroll
             for (int q = 0; q < kBatch / 2; ++q) {
-                const int src = (2 * q + half) << 2;
                 uint32_t ev[NPW];
 #pragma unroll
-                for (int w = 0; w < NPW; ++w)
-                    ev[w] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)packed[w]);
-                const int64_t r = b + 2 * q + half;
-                if (active && r < Bc) {
-                    const float x = a[q] * scale;
-#pragma unroll
-                    for (int l = 0; l < KAPPA; ++l) {
-                        const uint32_t e = (ev[l / 2] >> (16 * (l & 1))) & 0xFFFFu;
-                        atomic_add_lds_f32(acc + (int)(e & 0x7FFFu) * 64 + lane, (e >> 15) ? -x : x);
-                    }
+                for (int w = 0; w < NPW; ++w) {
+                    const uint32_t e0 = (uint32_t)__builtin_amdgcn_readlane((int)packed[w], 2 * q);
+                    const uint32_t e1 = (uint32_t)__builtin_amdgcn_readlane((int)packed[w], 2 * q + 1);
+                    ev[w] = half ? e1 : e0;
                 }
+                const int64_t r = b + 2 * q + half;
+                const float x = (active && r < Bc) ? a[q] * scale : 0.f;
+                // the kappa updates of one row hit kappa different output
+                // blocks, so their tile rows differ: all reads, then all writes
+                float *p[KAPPA];
+                float t[KAPPA];
+#pragma unroll
+                for (int l = 0; l < KAPPA; ++l) {
+                    const uint32_t e = (ev[l / 2] >> (16 * (l & 1))) & 0xFFFFu;
+                    p[l] = tile + (int)(e & 0x7FFFu) * 64;
+                    t[l] = *p[l] + ((e >> 15) ? -x : x);
+                }
+#pragma unroll
+                for (int l = 0; l < KAPPA; ++l) *p[l] = t[l];
             }
         }
     }
@@ -107,7 +121,11 @@ __global__ __launch_bounds__(1024) void k_blockperm(const BlockPermArgs args) {
         const int cc = k - tr * kTile;
         const int32_t c = blockIdx.x * kTile + cc;
         if (c < args.n) {
-            const float s = acc[tr * 64 + cc] + acc[tr * 64 + 32 + cc];
+            float s = 0.f;
+            for (int w = 0; w < nw; ++w) {
+                const float *t = acc + ((int64_t)w * trows + tr) * 64;
+                s += t[cc] + t[32 + cc];
+            }
             const int l = tr / Br;
             const int64_t orow = (int64_t)gout[l] * Br + (tr - l * Br);
             float *p = args.Y + orow * args.ldy + c;
@@ -118,12 +136,25 @@ __global__ __launch_bounds__(1024) void k_blockperm(const BlockPermArgs args) {
 
 }  // namespace
 
-int blockperm_max_rows(const DevInfo &di) { return di.max_lds / (64 * (int)sizeof(float)) - 1; }
+// LDS the kernel's static arrays (keys, gout) may take, kept out of the tiles.
+constexpr int kStaticLds = 1024;
+
+// One wave tile must fit: kappa*B_r rows of 64 floats.
+int blockperm_max_rows(const DevInfo &di) {
+    return (di.max_lds - kStaticLds) / (64 * (int)sizeof(float));
+}
 
 hipError_t launch_blockperm(const BlockPermArgs &args, int32_t kappa, hipStream_t s) {
-    const size_t lds = (size_t)kappa * args.Br * 64 * sizeof(float);
+    const size_t wave_bytes = (size_t)kappa * args.Br * 64 * sizeof(float);
+    DevInfo di;
+    hipError_t e0 = dev_info(&di);
+    if (e0 != hipSuccess) return e0;
+    int nw = (int)((size_t)(di.max_lds - kStaticLds) / wave_bytes);
+    if (nw > kMaxWaves) nw = kMaxWaves;
+    if (nw < 1) return hipErrorInvalidValue;
+    const size_t lds = wave_bytes * nw;
     const dim3 grid((unsigned)((args.n + kTile - 1) / kTile), (unsigned)args.C);
-    const dim3 block(1024);
+    const dim3 block(nw * 64);
 #define SK_LAUNCH(K)                                                                          \
     do {                                                                                      \
         auto kern = k_blockperm<K>;                                                           \

@@ -34,16 +34,23 @@ hipError_t dev_info(DevInfo *out) {
     return hipSuccess;
 }
 
-// Widest power-of-two slice (<= 64 lanes) whose d x slice partial of 4-byte
-// words fits in LDS.  A partial that takes more than half the LDS runs one
-// 1024-thread workgroup per CU; smaller partials run 512-thread workgroups,
-// several per CU.  Row chunks are sized so the grid fills every CU.
-bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, LdsPlan *p) {
+// LDS plan for k_lock_apply.  The slice is the widest power of two (at most
+// 64 lanes, at least 8, no wider than the row needs) whose d x slice partial
+// plus d lock words fit in LDS.  A plan that takes more than half the LDS
+// runs one 1024-thread workgroup per CU; smaller ones run 512-thread
+// workgroups, several per CU.  Row chunks are sized so the grid fills every
+// CU, with at least 256 rows per chunk so the one flush per workgroup stays
+// small next to the rows it streams.
+bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, int32_t zeta,
+              LdsPlan *p) {
+    if (zeta > 64) return false;
+    // d x slice partial words, d lock words, one 64-word dummy row per wave
+    auto need = [&](int sl) { return ((int64_t)d * (sl + 1) + 16 * 64) * 4; };
     int slice = 64;
-    while (slice > 8 && ((int64_t)d * slice * 4 > di.max_lds || slice / 2 >= lanes_total)) slice /= 2;
-    if ((int64_t)d * slice * 4 > di.max_lds) return false;
+    while (slice > 8 && (need(slice) > di.max_lds || slice / 2 >= lanes_total)) slice /= 2;
+    if (need(slice) > di.max_lds) return false;
     p->slice = slice;
-    p->lds_bytes = (size_t)d * slice * 4;
+    p->lds_bytes = (size_t)need(slice);
     const int per_cu_lds = (int)(di.max_lds / (int64_t)p->lds_bytes);
     int per_cu;
     if (per_cu_lds < 2) {
@@ -54,13 +61,17 @@ bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, LdsP
         per_cu = per_cu_lds < 4 ? per_cu_lds : 4;
     }
     p->slices = (lanes_total + slice - 1) / slice;
-    int64_t want = (int64_t)di.num_cu * per_cu / p->slices;
+    int64_t want = ((int64_t)di.num_cu * per_cu + p->slices - 1) / p->slices;
+    const int64_t max_chunks = (m + 255) / 256;
+    if (want > max_chunks) want = max_chunks;
+    if (want > 65535) want = 65535;
     if (want < 1) want = 1;
     int64_t rows = (m + want - 1) / want;
     if (rows < 1) rows = 1;
     p->rows_per_chunk = rows;
     p->chunks = (m + rows - 1) / rows;
     if (p->chunks < 1) p->chunks = 1;
+    p->ws_bytes = (size_t)p->slices * (size_t)p->chunks * (size_t)d * (size_t)slice * 4;
     return true;
 }
 
@@ -102,6 +113,60 @@ sk_status check_apply(const float *A, int64_t m, int32_t n, int64_t lda, const i
     return SK_OK;
 }
 
+// Variant choice and launch shared by the two SparseStack precisions.
+sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t lda,
+                         const int32_t *row_idx, const float *val, int32_t zeta, void *B, int32_t d,
+                         int64_t ldb, uint32_t flags, void *workspace, size_t workspace_bytes,
+                         hipStream_t s) {
+    sk::DevInfo di;
+    hipError_t e = sk::dev_info(&di);
+    if (e != hipSuccess) return SK_ERR_HIP;
+    sk::LdsPlan plan{};
+    const int64_t lanes = f16 ? n / 2 : n;
+    const bool lds_ok = m > 0 && sk::plan_lds(di, m, lanes, d, zeta, &plan);
+    if ((flags & SK_VARIANT_LDS) && !lds_ok && m > 0) return SK_ERR_UNSUPPORTED;
+    const bool use_lds = m > 0 && !(flags & SK_VARIANT_FLAT) && lds_ok;
+    const bool accumulate = (flags & SK_ACCUMULATE) != 0;
+    uint32_t *ws = nullptr;
+    if (use_lds && workspace != nullptr) {
+        if (workspace_bytes < plan.ws_bytes) return SK_ERR_ARG;
+        ws = static_cast<uint32_t *>(workspace);
+    }
+    // the store-and-reduce flush writes every element of B itself
+    if (!accumulate && ws == nullptr) {
+        e = f16 ? sk::launch_zero_words(reinterpret_cast<uint32_t *>(B), d, n / 2, ldb / 2, s)
+                : sk::launch_zero_words(reinterpret_cast<uint32_t *>(B), d, n, ldb, s);
+        if (e != hipSuccess) return SK_ERR_HIP;
+    }
+    if (m == 0) return SK_OK;
+    if (f16) {
+        uint16_t *B16 = static_cast<uint16_t *>(B);
+        if (use_lds)
+            return hip_status(sk::launch_f16_lds(plan, A, m, n, lda, row_idx, val, zeta, B16, d, ldb,
+                                                 ws, accumulate ? 1 : 0, s));
+        return hip_status(sk::launch_f16_flat(A, m, n, lda, row_idx, val, zeta, B16, d, ldb, s));
+    }
+    float *B32 = static_cast<float *>(B);
+    if (use_lds)
+        return hip_status(sk::launch_f32_lds(plan, A, m, n, lda, row_idx, val, zeta, B32, d, ldb, ws,
+                                             accumulate ? 1 : 0, s));
+    return hip_status(sk::launch_f32_flat(A, m, n, lda, row_idx, val, zeta, B32, d, ldb, s));
+}
+
+sk_status check_workspace(const void *ws, size_t bytes, const float *A, int64_t m, int32_t n,
+                          int64_t lda, const int32_t *row_idx, const float *val, int32_t zeta,
+                          const void *B, size_t bspan) {
+    if (ws == nullptr) return SK_OK;
+    if ((uintptr_t)ws % 4 != 0) return SK_ERR_ALIGN;
+    if (overlaps(ws, bytes, B, bspan)) return SK_ERR_ARG;
+    if (m > 0) {
+        if (overlaps(ws, bytes, A, span_bytes(m, n, lda, 4))) return SK_ERR_ARG;
+        if (overlaps(ws, bytes, row_idx, (size_t)m * zeta * 4)) return SK_ERR_ARG;
+        if (overlaps(ws, bytes, val, (size_t)m * zeta * 4)) return SK_ERR_ARG;
+    }
+    return SK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,49 +198,48 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
 
 sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda, const int32_t *row_idx,
                        const float *val, int32_t zeta, float *B, int32_t d, int64_t ldb,
-                       uint32_t flags, void *stream) {
+                       uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
     sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 4, d, ldb, flags);
     if (st != SK_OK) return st;
-    const hipStream_t s = (hipStream_t)stream;
-    sk::DevInfo di;
-    hipError_t e = sk::dev_info(&di);
-    if (e != hipSuccess) return SK_ERR_HIP;
-    sk::LdsPlan plan{};
-    const bool lds_ok = m > 0 && sk::plan_lds(di, m, n, d, &plan);
-    if ((flags & SK_VARIANT_LDS) && !lds_ok && m > 0) return SK_ERR_UNSUPPORTED;
-    if (!(flags & SK_ACCUMULATE)) {
-        e = sk::launch_zero_words(reinterpret_cast<uint32_t *>(B), d, n, ldb, s);
-        if (e != hipSuccess) return SK_ERR_HIP;
-    }
-    if (m == 0) return SK_OK;
-    if (!(flags & SK_VARIANT_FLAT) && lds_ok)
-        return hip_status(sk::launch_f32_lds(plan, A, m, n, lda, row_idx, val, zeta, B, d, ldb, s));
-    return hip_status(sk::launch_f32_flat(A, m, n, lda, row_idx, val, zeta, B, d, ldb, s));
+    st = check_workspace(workspace, workspace_bytes, A, m, n, lda, row_idx, val, zeta, B,
+                         span_bytes(d, n, ldb, 4));
+    if (st != SK_OK) return st;
+    return apply_dispatch(false, A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags, workspace,
+                          workspace_bytes, (hipStream_t)stream);
 }
 
 sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
-                          int32_t d, int64_t ldb, uint32_t flags, void *stream) {
+                          int32_t d, int64_t ldb, uint32_t flags, void *workspace,
+                          size_t workspace_bytes, void *stream) {
     sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 2, d, ldb, flags);
     if (st != SK_OK) return st;
     if (n % 2 != 0) return SK_ERR_SHAPE;
     if (ldb % 2 != 0 || (uintptr_t)B % 4 != 0) return SK_ERR_ALIGN;
     if (m > 0 && (lda % 2 != 0 || (uintptr_t)A % 8 != 0)) return SK_ERR_ALIGN;
-    const hipStream_t s = (hipStream_t)stream;
+    st = check_workspace(workspace, workspace_bytes, A, m, n, lda, row_idx, val, zeta, B,
+                         span_bytes(d, n, ldb, 2));
+    if (st != SK_OK) return st;
+    return apply_dispatch(true, A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags, workspace,
+                          workspace_bytes, (hipStream_t)stream);
+}
+
+sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32_t d,
+                                  int32_t zeta, uint32_t flags, size_t *bytes) {
+    if (bytes == nullptr) return SK_ERR_NULL;
+    *bytes = 0;
+    if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC) return SK_ERR_ARG;
+    if (m < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0) return SK_ERR_SHAPE;
+    if (precision == SK_PRECISION_F16ACC && n % 2 != 0) return SK_ERR_SHAPE;
+    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS)) return SK_ERR_ARG;
+    if ((flags & SK_VARIANT_FLAT) && (flags & SK_VARIANT_LDS)) return SK_ERR_ARG;
+    if (m == 0 || (flags & SK_VARIANT_FLAT)) return SK_OK;
     sk::DevInfo di;
-    hipError_t e = sk::dev_info(&di);
-    if (e != hipSuccess) return SK_ERR_HIP;
+    if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
     sk::LdsPlan plan{};
-    const bool lds_ok = m > 0 && sk::plan_lds(di, m, n / 2, d, &plan);
-    if ((flags & SK_VARIANT_LDS) && !lds_ok && m > 0) return SK_ERR_UNSUPPORTED;
-    if (!(flags & SK_ACCUMULATE)) {
-        e = sk::launch_zero_words(reinterpret_cast<uint32_t *>(B), d, n / 2, ldb / 2, s);
-        if (e != hipSuccess) return SK_ERR_HIP;
-    }
-    if (m == 0) return SK_OK;
-    if (!(flags & SK_VARIANT_FLAT) && lds_ok)
-        return hip_status(sk::launch_f16_lds(plan, A, m, n, lda, row_idx, val, zeta, B, d, ldb, s));
-    return hip_status(sk::launch_f16_flat(A, m, n, lda, row_idx, val, zeta, B, d, ldb, s));
+    const int64_t lanes = precision == SK_PRECISION_F16ACC ? n / 2 : n;
+    if (sk::plan_lds(di, m, lanes, d, zeta, &plan)) *bytes = plan.ws_bytes;
+    return SK_OK;
 }
 
 sk_status sk_apply_blockperm(const float *A, int64_t m, int32_t n, int64_t lda, int32_t d,

@@ -20,30 +20,39 @@ hipError_t launch_zero_words(uint32_t *B, int64_t rows, int64_t words, int64_t l
 hipError_t launch_meta(uint64_t seed, int64_t row_offset, int64_t m, int32_t d, int32_t zeta,
                        float scale, int32_t *row_idx, float *val, hipStream_t stream);
 
-// Shape of an LDS-privatized SparseStack launch.
+// Shape of an LDS-privatized SparseStack launch (k_lock_apply).
 struct LdsPlan {
-    int slice;              // columns (FP32) or column pairs (FP16) per workgroup
+    int slice;              // lanes per slice: columns (FP32) or column pairs (FP16)
     int threads;            // workgroup size
     int64_t rows_per_chunk; // input rows per workgroup
     int64_t chunks;         // row chunks (grid y)
     int64_t slices;         // column slices (grid x)
-    size_t lds_bytes;       // dynamic LDS per workgroup
+    size_t lds_bytes;       // dynamic LDS per workgroup: d x slice partial + d locks
+    size_t ws_bytes;        // workspace for the store-and-reduce flush
 };
-// Returns false when even the narrowest slice does not fit in LDS.
-bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, LdsPlan *plan);
+// Returns false when even the narrowest slice does not fit in LDS, or when
+// zeta is beyond what one lock instruction covers (then the flat kernel runs).
+bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, int32_t zeta,
+              LdsPlan *plan);
 
 hipError_t launch_f32_flat(const float *A, int64_t m, int32_t n, int64_t lda,
                            const int32_t *row_idx, const float *val, int32_t zeta, float *B,
                            int32_t d, int64_t ldb, hipStream_t stream);
-hipError_t launch_f32_lds(const LdsPlan &plan, const float *A, int64_t m, int32_t n, int64_t lda,
-                          const int32_t *row_idx, const float *val, int32_t zeta, float *B,
-                          int32_t d, int64_t ldb, hipStream_t stream);
 hipError_t launch_f16_flat(const float *A, int64_t m, int32_t n, int64_t lda,
                            const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
                            int32_t d, int64_t ldb, hipStream_t stream);
+// LDS-privatized apply.  ws == NULL: the partials are added to B with global
+// atomics (B must hold its start value).  ws != NULL: the partials are
+// stored to ws (plan.ws_bytes) and a reduce kernel writes B (accumulate=0)
+// or adds to it (accumulate=1) in chunk order.
+hipError_t launch_f32_lds(const LdsPlan &plan, const float *A, int64_t m, int32_t n, int64_t lda,
+                          const int32_t *row_idx, const float *val, int32_t zeta, float *B,
+                          int32_t d, int64_t ldb, uint32_t *ws, int accumulate,
+                          hipStream_t stream);
 hipError_t launch_f16_lds(const LdsPlan &plan, const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
-                          int32_t d, int64_t ldb, hipStream_t stream);
+                          int32_t d, int64_t ldb, uint32_t *ws, int accumulate,
+                          hipStream_t stream);
 
 constexpr int kBlockPermMaxM = 1024;
 struct BlockPermArgs {

@@ -74,8 +74,10 @@ def orth_torch(A):
     import torch
     Q = A.to(torch.float64)
     for _ in range(2):
-        L = torch.linalg.cholesky(Q.T @ Q)
-        Q = torch.linalg.solve_triangular(L, Q.T, upper=False).T
+        L = torch.linalg.cholesky(Q.T @ Q)          # n x n, Q^T Q = L L^T
+        # Q <- Q L^{-T}: invert the small factor and multiply, so the tall
+        # operand only meets a plain matrix product
+        Q = Q @ torch.linalg.inv(L).T.contiguous()
     return Q.to(torch.float32).contiguous()
 
 

@@ -18,7 +18,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
     assert set(names) == {"sk_meta_generate", "sk_apply_f32", "sk_apply_f16acc",
-                          "sk_apply_blockperm", "sk_status_string"}
+                          "sk_apply_workspace_size", "sk_apply_blockperm", "sk_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -65,7 +65,39 @@ A, RI, V, B = FAKE, FAKE + (1 << 34), FAKE + (1 << 35), FAKE + (1 << 36)
     ((A, 100, 64, 64, RI, V, 4, RI + 64, 64, 64, 0), b.SK_ERR_ARG),  # B inside metadata
 ])
 def test_apply_validation(lib, fn, args, expect):
-    assert getattr(lib, fn)(*args, None) == expect
+    assert getattr(lib, fn)(*args, None, 0, None) == expect
+
+
+WS = FAKE + (1 << 37)
+
+
+@pytest.mark.parametrize("fn", ["sk_apply_f32", "sk_apply_f16acc"])
+@pytest.mark.parametrize("ws,nbytes,expect", [
+    (WS + 2, 1 << 20, b.SK_ERR_ALIGN),            # workspace not 4-byte aligned
+    (A + 64, 1 << 20, b.SK_ERR_ARG),              # workspace overlaps A
+    (B - 16, 64, b.SK_ERR_ARG),                   # workspace overlaps B
+    (RI + 4, 64, b.SK_ERR_ARG),                   # workspace overlaps the metadata
+])
+def test_workspace_validation(lib, fn, ws, nbytes, expect):
+    args = (A, 100, 64, 64, RI, V, 4, B, 64, 64, 0)
+    assert getattr(lib, fn)(*args, ws, nbytes, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((2, 100, 64, 64, 4, 0), b.SK_ERR_ARG),        # unknown precision
+    ((0, 100, 0, 64, 4, 0), b.SK_ERR_SHAPE),       # n < 1
+    ((1, 100, 63, 64, 4, 0), b.SK_ERR_SHAPE),      # odd n for FP16
+    ((0, 100, 64, 64, 3, 0), b.SK_ERR_SHAPE),      # d % zeta
+    ((0, 100, 64, 64, 4, 6), b.SK_ERR_ARG),        # FLAT|LDS
+    ((0, 0, 64, 64, 4, 0), b.SK_OK),               # m = 0: no workspace
+    ((1, 100, 64, 64, 4, 2), b.SK_OK),             # FLAT: no workspace
+])
+def test_workspace_size_validation(lib, args, expect):
+    out = ctypes.c_size_t(123)
+    assert lib.sk_apply_workspace_size(*args, ctypes.byref(out)) == expect
+    if expect == b.SK_OK:
+        assert out.value == 0
+    assert lib.sk_apply_workspace_size(*args, None) == b.SK_ERR_NULL
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -76,7 +108,7 @@ def test_apply_validation(lib, fn, args, expect):
     ((A + 4, 100, 64, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_ALIGN), # A not 8-byte aligned
 ])
 def test_f16acc_pair_rules(lib, args, expect):
-    assert lib.sk_apply_f16acc(*args, None) == expect
+    assert lib.sk_apply_f16acc(*args, None, 0, None) == expect
 
 
 @pytest.mark.parametrize("args,expect", [

@@ -19,36 +19,53 @@ from tests.gpuutil import dev, say, sync, to_dev
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = {"flat": b.SK_VARIANT_FLAT, "lds": b.SK_VARIANT_LDS}
+# (flags, workspace): the page's flat scatter; the LDS-privatized apply with
+# the store-and-reduce flush (workspace); the same with the atomic flush
+VARIANTS = {"flat": (b.SK_VARIANT_FLAT, None), "lds": (b.SK_VARIANT_LDS, True),
+            "lds_atomic": (b.SK_VARIANT_LDS, None)}
+ALL = list(VARIANTS)
+U16 = 2.0**-11          # unit roundoff of binary16
 
 
-def run(A, d, zeta, seed, precision, flags=0, meta=None):
+def f16_tolerance(K):
+    """Relative Frobenius bar for an FP16-accumulated sketch whose output
+    entries each receive K contributions.  4e-3 is the bar at the sketch
+    sizes the FP16 sketching page's study uses (d = 2n, K in the thousands);
+    a degenerate shape (d = zeta: every input row hits every output row)
+    piles K = m contributions on each entry, and a running FP16 sum of K
+    random-sign terms then carries a relative error of about u*sqrt(K/12)
+    whatever the order, so the bar there is four times that estimate."""
+    return max(4e-3, 4 * U16 * math.sqrt(K / 12))
+
+
+def run(A, d, zeta, seed, precision, variant="lds", meta=None):
     """Metadata (GPU) + apply (GPU); returns (B on host as fp64, ri, v host)."""
     Ad = A if isinstance(A, torch.Tensor) else to_dev(A)
     m = Ad.shape[0]
     ri, v = meta if meta is not None else b.meta(seed, m, d, zeta, device=dev())
-    B = b.apply(Ad, ri, v, zeta, d, precision=precision, flags=flags)
+    flags, ws = VARIANTS[variant]
+    B = b.apply(Ad, ri, v, zeta, d, precision=precision, flags=flags, ws=ws)
     sync()
     return B.cpu().numpy().astype(np.float64), ri, v
 
 
 # ---------------------------------------------------------------- tiny config
 
-@pytest.mark.parametrize("variant", ["flat", "lds"])
+@pytest.mark.parametrize("variant", ALL)
 @pytest.mark.parametrize("zeta", [1, 4])
 def test_tiny_f32_vs_dense(variant, zeta):
     """A 4096 x 32 N(0,1) seed 0, d = 64: against the dense S*A brute force."""
     say(f"tiny f32 {variant} zeta={zeta}")
     m, n, d = 4096, 32, 64
     A = inputs.gaussian(m, n)
-    B, _, _ = run(A, d, zeta, 1, "f32", VARIANTS[variant])
+    B, _, _ = run(A, d, zeta, 1, "f32", variant)
     ri, v = oracle.meta_ref(1, m, d, zeta)
     ref = oracle.dense_S(ri, v, m, d, zeta) @ A.astype(np.float64)
     assert oracle.rel_frob(B, ref) <= 1e-5
 
 
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
-@pytest.mark.parametrize("variant", ["flat", "lds"])
+@pytest.mark.parametrize("variant", ALL)
 def test_exact_inputs_bit_exact(precision, variant):
     """Integer inputs (FP32, |A| <= 8) and {-1,0,1} inputs (FP16): every
     partial sum is exactly representable, so the order of atomics cannot
@@ -57,7 +74,7 @@ def test_exact_inputs_bit_exact(precision, variant):
     m, n, d, zeta = 4096, 32, 64, 4
     lo, hi = (-8, 8) if precision == "f32" else (-1, 1)
     A = inputs.integer_matrix(m, n, lo, hi)
-    B, _, _ = run(A, d, zeta, 1, precision, VARIANTS[variant])
+    B, _, _ = run(A, d, zeta, 1, precision, variant)
     ri, v = oracle.meta_ref(1, m, d, zeta)
     if precision == "f16acc":
         assert 0.5 * np.bincount(ri, minlength=d).max() < 1024
@@ -65,29 +82,33 @@ def test_exact_inputs_bit_exact(precision, variant):
 
 
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
-@pytest.mark.parametrize("variant", ["flat", "lds"])
+@pytest.mark.parametrize("variant", ALL)
 @pytest.mark.parametrize("zeta", [1, 4, 8])
 def test_coordinate_input(precision, variant, zeta):
     """A = [I_n 0]^T: SA equals the first n columns of S exactly."""
     m, n, d = 4096, 32, 64
     A = inputs.coordinate(m, n)
-    B, _, _ = run(A, d, zeta, 8, precision, VARIANTS[variant])
+    B, _, _ = run(A, d, zeta, 8, precision, variant)
     ri, v = oracle.meta_ref(8, m, d, zeta)
-    assert np.array_equal(B, oracle.dense_S(ri[:n * zeta], v[:n * zeta], n, d, zeta))
+    S_n = oracle.dense_S(ri[:n * zeta], v[:n * zeta], n, d, zeta)
+    if precision == "f16acc":
+        # one contribution per entry: B = +0 + RN_f16(val), e.g. 1/sqrt(8)
+        S_n = S_n.astype(np.float32).astype(np.float16).astype(np.float64)
+    assert np.array_equal(B, S_n)
 
 
-@pytest.mark.parametrize("variant", ["flat", "lds"])
+@pytest.mark.parametrize("variant", ALL)
 def test_tiny_f16_vs_fp64(variant):
     m, n, d, zeta = 4096, 32, 64, 4
     A = inputs.gaussian(m, n)
-    B, _, _ = run(A, d, zeta, 1, "f16acc", VARIANTS[variant])
+    B, _, _ = run(A, d, zeta, 1, "f16acc", variant)
     ri, v = oracle.meta_ref(1, m, d, zeta)
     assert oracle.rel_frob(B, oracle.sketch_f64(A, ri, v, d, zeta)) <= 4e-3
 
 
 # ------------------------------------------------------- FP16 number format
 
-@pytest.mark.parametrize("variant", ["flat", "lds"])
+@pytest.mark.parametrize("variant", ALL)
 def test_f16_conversion_ties_subnormals_overflow(variant):
     """Coordinate input, zeta = 4 (scale 1/2): each output entry receives one
     contribution q = a/2, so B = RN_f16(q) for every a.  Covers the page's
@@ -100,7 +121,7 @@ def test_f16_conversion_ties_subnormals_overflow(variant):
                         dtype=np.float32)
     vals = np.resize(specials, n)
     A = inputs.coordinate(4096, n) * vals[None, :]
-    B, _, _ = run(A, d, zeta, 3, "f16acc", VARIANTS[variant])
+    B, _, _ = run(A, d, zeta, 3, "f16acc", variant)
     ri, v = oracle.meta_ref(3, 4096, d, zeta)
     # one contribution per entry: B = +0 + RN(q), so the order is irrelevant
     expect = oracle.sketch_f16_rn_emul(A, ri, v, d, zeta)
@@ -109,13 +130,13 @@ def test_f16_conversion_ties_subnormals_overflow(variant):
     assert np.array_equal(np.signbit(B), np.signbit(expect))
 
 
-@pytest.mark.parametrize("variant", ["flat", "lds"])
+@pytest.mark.parametrize("variant", ALL)
 def test_f16_subnormal_accumulation(variant):
     """Sums that stay in the FP16 subnormal range are exact multiples of
     h = 2^-24: the atomics must keep subnormals (§III-C) and equal fp64."""
     m, n, d, zeta = 4096, 32, 64, 4
     A = inputs.integer_matrix(m, n, -3, 3, seed=5) * np.float32(2.0**-23)   # q = k * 2^-24
-    B, _, _ = run(A, d, zeta, 4, "f16acc", VARIANTS[variant])
+    B, _, _ = run(A, d, zeta, 4, "f16acc", variant)
     ri, v = oracle.meta_ref(4, m, d, zeta)
     ref = oracle.sketch_f64(A, ri, v, d, zeta)
     assert np.abs(ref).max() < 2.0**-14            # whole computation subnormal
@@ -125,7 +146,7 @@ def test_f16_subnormal_accumulation(variant):
 # ---------------------------------------------------- ragged and edge cases
 
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
-@pytest.mark.parametrize("variant", ["flat", "lds"])
+@pytest.mark.parametrize("variant", ALL)
 @pytest.mark.parametrize("m,n,d,zeta,pad", [
     (1000, 38, 96, 3, 6),       # ragged rows / columns, zeta = 3, padded strides
     (777, 130, 40, 8, 2),       # more columns than one slice, zeta = 8
@@ -143,13 +164,14 @@ def test_ragged_shapes(precision, variant, m, n, d, zeta, pad):
     ldb = n + pad
     out = torch.full((d, ldb), 7.0, dtype=torch.float16 if precision == "f16acc" else torch.float32,
                      device=dev())
-    b.apply(Ad, ri, v, zeta, d, precision=precision, out=out[:, :n], flags=VARIANTS[variant])
+    flags, ws = VARIANTS[variant]
+    b.apply(Ad, ri, v, zeta, d, precision=precision, out=out[:, :n], flags=flags, ws=ws)
     sync()
     B = out.cpu().numpy().astype(np.float64)
     assert np.all(B[:, n:] == 7.0)              # padding untouched
     ri_h, v_h = oracle.meta_ref(6, m, d, zeta)
     ref = oracle.sketch_f64(np.ascontiguousarray(A[:, :n]), ri_h, v_h, d, zeta)
-    tol = 1e-5 if precision == "f32" else 4e-3
+    tol = 1e-5 if precision == "f32" else f16_tolerance(m * zeta // d)
     assert oracle.rel_frob(B[:, :n], ref) <= tol
 
 
@@ -194,8 +216,8 @@ def test_out_of_range_rows_are_ignored(precision):
     bad[3::11] = -1
     keep = (bad >= 0) & (bad < d)
     ref = oracle.sketch_f64(A, np.where(keep, bad, 0).astype(np.int32), np.where(keep, v_h, 0).astype(np.float32), d, zeta)
-    for variant in ("flat", "lds"):
-        B, _, _ = run(A, d, zeta, 0, precision, VARIANTS[variant], meta=(to_dev(bad), to_dev(v_h)))
+    for variant in ALL:
+        B, _, _ = run(A, d, zeta, 0, precision, variant, meta=(to_dev(bad), to_dev(v_h)))
         assert np.array_equal(B, ref)
 
 
@@ -226,19 +248,20 @@ def scale_case():
     return Ad, A, d, zeta, seed, oracle.sketch_f64(A, ri, v, d, zeta)
 
 
-@pytest.mark.parametrize("variant", ["flat", "lds"])
+@pytest.mark.parametrize("variant", ALL)
 def test_scale_f32(scale_case, variant):
     Ad, A, d, zeta, seed, ref = scale_case
     say(f"scale f32 {variant}")
-    B, _, _ = run(Ad, d, zeta, seed, "f32", VARIANTS[variant])
+    B, _, _ = run(Ad, d, zeta, seed, "f32", variant)
     assert oracle.rel_frob(B, ref) <= 1e-5
 
 
-def test_scale_f16acc(scale_case):
-    """The default (LDS two-level) FP16 sketch meets the 4e-3 bar."""
+@pytest.mark.parametrize("variant", ["lds", "lds_atomic"])
+def test_scale_f16acc(scale_case, variant):
+    """The LDS two-level FP16 sketch meets the 4e-3 bar."""
     Ad, A, d, zeta, seed, ref = scale_case
-    say("scale f16acc lds")
-    B, _, _ = run(Ad, d, zeta, seed, "f16acc", 0)
+    say(f"scale f16acc {variant}")
+    B, _, _ = run(Ad, d, zeta, seed, "f16acc", variant)
     err = oracle.rel_frob(B, ref)
     say(f"  rel err {err:.3e}")
     assert err <= 4e-3
@@ -249,7 +272,7 @@ def test_scale_f16acc_flat_error_model(scale_case):
     per entry in one FP16 running sum; its error follows the random-walk
     estimate u*sqrt(K/12) (u = 2^-11) and so misses the 4e-3 bar here."""
     Ad, A, d, zeta, seed, ref = scale_case
-    B, _, _ = run(Ad, d, zeta, seed, "f16acc", b.SK_VARIANT_FLAT)
+    B, _, _ = run(Ad, d, zeta, seed, "f16acc", "flat")
     err = oracle.rel_frob(B, ref)
     pred = 2.0**-11 * math.sqrt((A.shape[0] * zeta / d) / 12)
     say(f"  flat rel err {err:.3e} (model {pred:.3e})")
