@@ -148,6 +148,13 @@ def main():
     bytes16 = sparsestack_bytes(m, n, d, zeta, 2)
     bytes32 = sparsestack_bytes(m, n, d, zeta, 4)
 
+    # bring clocks and caches to a steady state before any timed region
+    for _ in range(max(20, W)):
+        meta()
+        f16()
+        f32(b.SK_VARIANT_FLAT, None)
+    torch.cuda.synchronize()
+
     # headline step: complete FP16-accumulate sketch (metadata, then the LDS
     # apply whose store-and-reduce flush also initializes B)
     ms16 = timed(lambda: (meta(), f16()), K, W, stream)

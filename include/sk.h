@@ -99,15 +99,18 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
  *
  *   A        device float, m x n, lda >= n.
  *   row_idx, val  device metadata of length m*zeta (sk_meta_generate's
- *            layout).  Entries with row_idx outside [0, d) contribute
- *            nothing.
+ *            layout).  Entry i*zeta+t belongs to stack block t: it
+ *            contributes only if row_idx lies in that block's rows
+ *            [t*d/zeta, (t+1)*d/zeta); any other entry (outside [0, d), or in
+ *            another block) contributes nothing.
  *   B        device float, d x n, ldb >= n.
  *   flags    SK_ACCUMULATE, and at most one of
  *              SK_VARIANT_FLAT: one no-return global FP32 atomic add per
  *                contribution (the page's scatter; the in-house baseline);
- *              SK_VARIANT_LDS: each workgroup keeps a private d x slice FP32
- *                partial in LDS, updated by plain read-add-write under
- *                per-row LDS locks, and flushes it once.
+ *              SK_VARIANT_LDS: each workgroup keeps a private FP32 partial
+ *                of a column slice (and a group of stack blocks) in LDS,
+ *                updated by read, add and integer compare-and-swap, and
+ *                flushes it once.
  *            0 picks LDS when the partial fits in LDS and zeta <= 64, else
  *            FLAT.
  *   workspace, workspace_bytes
@@ -202,6 +205,25 @@ sk_status sk_apply_blockperm(const float *A, int64_t m, int32_t n, int64_t lda,
                              int32_t d, int32_t M, int32_t kappa, int32_t s,
                              uint64_t seed, float *Y, int64_t ldy, uint32_t flags,
                              void *stream);
+
+/*
+ * sk_lds_plan_describe: the launch plan sk_apply_f32 (precision
+ * SK_PRECISION_F32) or sk_apply_f16acc (SK_PRECISION_F16ACC) makes for its
+ * LDS variant, for the given sizes, A's leading dimension lda, whether A's
+ * base address allows two-word lane loads (wide_ok: 16-byte aligned for
+ * FP16, 8-byte for FP32) and the device's compute units and per-workgroup
+ * LDS bytes.  Pure host computation: no HIP call, no device needed.  For
+ * tests and tools that check a plan against the kernels' index bounds.
+ *   out  int64[SK_PLAN_FIELDS], written: {lds_variant_used (0: the flat
+ *        kernel runs), words per lane, lanes per slice, block groups,
+ *        blocks per group, threads per workgroup, rows per chunk, chunks,
+ *        slices, workgroups, LDS bytes per workgroup, workspace bytes}.
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ARG (precision, num_cu, max_lds).
+ */
+#define SK_PLAN_FIELDS 12
+sk_status sk_lds_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda, int32_t d,
+                               int32_t zeta, int32_t wide_ok, int32_t num_cu, int32_t max_lds,
+                               int64_t *out);
 
 /* Static, NUL-terminated description of a status code. */
 const char *sk_status_string(sk_status status);

@@ -40,6 +40,9 @@ _SIGNATURES = {
     "sk_apply_blockperm": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32,
                                       _c.c_int32, _c.c_int32, _c.c_int32, _c.c_uint64, _c.c_void_p,
                                       _c.c_int64, _c.c_uint32, _c.c_void_p]),
+    "sk_lds_plan_describe": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32,
+                                        _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
+                                        _c.POINTER(_c.c_int64)]),
     "sk_status_string": (_c.c_char_p, [_c.c_int]),
 }
 
@@ -150,6 +153,18 @@ def sk_apply_workspace_size(precision, m, n, d, zeta, flags=0):
 def sk_apply_blockperm(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags=0, stream=None):
     _check("sk_apply_blockperm", load().sk_apply_blockperm(
         _ptr(A), m, n, lda, d, M, kappa, s, seed, _ptr(Y), ldy, flags, _stream(stream)))
+
+
+PLAN_FIELDS = ("lds", "words", "slice", "groups", "zg", "threads", "rows_per_chunk", "chunks",
+               "slices", "grid", "lds_bytes", "ws_bytes")
+
+
+def sk_lds_plan_describe(precision, m, n, lda, d, zeta, wide_ok, num_cu, max_lds):
+    """The LDS launch plan as a dict (host computation, no device needed)."""
+    out = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    _check("sk_lds_plan_describe", load().sk_lds_plan_describe(
+        precision, m, n, lda, d, zeta, int(bool(wide_ok)), num_cu, max_lds, out))
+    return dict(zip(PLAN_FIELDS, list(out)))
 
 
 # ---- tensor helpers ------------------------------------------------------

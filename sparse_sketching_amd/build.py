@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsksketch.so")
-SOURCES = ["capi.hip", "meta.hip", "apply_f32.hip", "apply_f16.hip", "apply_lds.hip",
+SOURCES = ["capi.hip", "meta.hip", "apply_f32.hip", "apply_f16.hip", "apply_stack.hip",
            "blockperm.hip"]
 ARCH = "gfx950"
 

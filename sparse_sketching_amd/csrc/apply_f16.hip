@@ -24,6 +24,7 @@ __global__ __launch_bounds__(256) void k_f16_flat(const float *__restrict__ A, i
                                                   int64_t rows_per_wg) {
     constexpr int U = 4;
     const int zeta = ZETA ? ZETA : zeta_rt;
+    const int32_t db = d / zeta;    // rows per stack block; entry t must lie in block t
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t pair = blockIdx.x * 64 + lane;
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void k_f16_flat(const float *__restrict__ A, i
             for_each_block<ZETA>(zeta, [&](int t) {
                 const int32_t r = ri[t];
                 const float v = vv[t];
-                if (active && (uint32_t)r < (uint32_t)d)
+                if (active && (uint32_t)(r - t * db) < (uint32_t)db)
                     atomic_add_global_h2(B2 + (int64_t)r * ldb2 + pair,
                                          cvt_rn_h2(a[u].x * v, a[u].y * v));
             });

@@ -24,6 +24,7 @@ __global__ __launch_bounds__(256) void k_f32_flat(const float *__restrict__ A, i
                                                   int64_t rows_per_wg) {
     constexpr int U = 4;        // rows in flight per wavefront
     const int zeta = ZETA ? ZETA : zeta_rt;
+    const int32_t db = d / zeta;    // rows per stack block; entry t must lie in block t
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t col = blockIdx.x * 64 + lane;
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void k_f32_flat(const float *__restrict__ A, i
             const float *vv = val + i * zeta;
             for_each_block<ZETA>(zeta, [&](int t) {
                 const int32_t r = ri[t];
-                if (active && (uint32_t)r < (uint32_t)d)
+                if (active && (uint32_t)(r - t * db) < (uint32_t)db)
                     atomic_add_global_f32(B + (int64_t)r * ldb + col, a[u] * vv[t]);
             });
         }

@@ -34,23 +34,47 @@ hipError_t dev_info(DevInfo *out) {
     return hipSuccess;
 }
 
-// LDS plan for k_lock_apply.  The slice is the widest power of two (at most
-// 64 lanes, at least 8, no wider than the row needs) whose d x slice partial
-// plus d lock words fit in LDS.  A plan that takes more than half the LDS
-// runs one 1024-thread workgroup per CU; smaller ones run 512-thread
-// workgroups, several per CU.  Row chunks are sized so the grid fills every
-// CU, with at least 256 rows per chunk so the one flush per workgroup stays
-// small next to the rows it streams.
-bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, int32_t zeta,
-              LdsPlan *p) {
-    if (zeta > 64) return false;
-    // d x slice partial words, d lock words, one 64-word dummy row per wave
-    auto need = [&](int sl) { return ((int64_t)d * (sl + 1) + 16 * 64) * 4; };
-    int slice = 64;
-    while (slice > 8 && (need(slice) > di.max_lds || slice / 2 >= lanes_total)) slice /= 2;
-    if (need(slice) > di.max_lds) return false;
-    p->slice = slice;
-    p->lds_bytes = (size_t)need(slice);
+// LDS plan for k_stack_apply.  Preference order: two-word lanes (half the
+// instructions per byte of A) with at most max_groups_wide block groups;
+// then one-word lanes with all blocks in one group.  Extra groups re-read A
+// through L2, which pays off for FP32 (twice the hits per byte of A) but not
+// for FP16 (measured on MI355X: 2^20 x 256, d = 512).  For each, the slice is the widest
+// power of two (at most 64 lanes, at least 8, no wider than the row needs)
+// whose partial (plus the wavefronts' 64-lane dummy rows) fits in LDS.  A
+// plan that takes more than half the LDS runs one 1024-thread workgroup per
+// CU; smaller ones run 512-thread workgroups, several per CU.  Row chunks
+// are sized so the grid fills every CU, with at least 256 rows per chunk so
+// the one flush per workgroup stays small next to the rows it streams.
+bool plan_lds(const DevInfo &di, int64_t m, int64_t units, bool wide_ok, int max_groups_wide,
+              int32_t d, int32_t zeta, LdsPlan *p) {
+    if (zeta > 64 || units < 1) return false;
+    const int64_t db = d / zeta;
+    bool found = false;
+    for (int w = 2; w >= 1 && !found; --w) {
+        if (w == 2 && (!wide_ok || units % 2 != 0 || units / 2 < 64)) continue;
+        const int64_t lpos = units / w;
+        for (int sp = 64; sp >= 8 && !found; sp /= 2) {
+            if (sp > 8 && sp / 2 >= lpos) continue;
+            // two-word lanes are built only for full 64-lane slices
+            if (w == 2 && sp != 64) break;
+            for (int g = 1; g <= zeta && !found; ++g) {
+                if (zeta % g != 0) continue;
+                if (w == 2 && g > max_groups_wide) break;
+                if (w == 1 && g > 1) break;
+                const int64_t zg = zeta / g;
+                const int64_t need = (zg * db * sp + 16 * 64) * w * 4;
+                if (need > di.max_lds) continue;
+                p->words = w;
+                p->slice = sp;
+                p->groups = g;
+                p->zg = (int)zg;
+                p->lds_bytes = (size_t)need;
+                p->slices = (lpos + sp - 1) / sp;
+                found = true;
+            }
+        }
+    }
+    if (!found) return false;
     const int per_cu_lds = (int)(di.max_lds / (int64_t)p->lds_bytes);
     int per_cu;
     if (per_cu_lds < 2) {
@@ -60,8 +84,8 @@ bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, int3
         p->threads = 512;
         per_cu = per_cu_lds < 4 ? per_cu_lds : 4;
     }
-    p->slices = (lanes_total + slice - 1) / slice;
-    int64_t want = ((int64_t)di.num_cu * per_cu + p->slices - 1) / p->slices;
+    const int64_t per_chunk = p->slices * p->groups;
+    int64_t want = ((int64_t)di.num_cu * per_cu + per_chunk - 1) / per_chunk;
     const int64_t max_chunks = (m + 255) / 256;
     if (want > max_chunks) want = max_chunks;
     if (want > 65535) want = 65535;
@@ -71,7 +95,10 @@ bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, int3
     p->rows_per_chunk = rows;
     p->chunks = (m + rows - 1) / rows;
     if (p->chunks < 1) p->chunks = 1;
-    p->ws_bytes = (size_t)p->slices * (size_t)p->chunks * (size_t)d * (size_t)slice * 4;
+    const int64_t units_sc = p->slices * p->chunks;      // (slice, chunk) pairs
+    p->grid = (units_sc + 7) / 8 * 8 * p->groups;
+    p->ws_bytes = (size_t)p->slices * (size_t)p->chunks * (size_t)d * (size_t)p->slice *
+                  (size_t)p->words * 4;
     return true;
 }
 
@@ -122,8 +149,13 @@ sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t
     hipError_t e = sk::dev_info(&di);
     if (e != hipSuccess) return SK_ERR_HIP;
     sk::LdsPlan plan{};
-    const int64_t lanes = f16 ? n / 2 : n;
-    const bool lds_ok = m > 0 && sk::plan_lds(di, m, lanes, d, zeta, &plan);
+    const int64_t units = f16 ? n / 2 : n;
+    // two-word lanes load 16 (FP16) or 8 (FP32) bytes per row
+    const int64_t vec = f16 ? 4 : 2;
+    const bool wide_ok = lda % vec == 0 && (uintptr_t)A % (vec * 4) == 0;
+    // the LDS kernel addresses 16 rows of A from one base with 32-bit offsets
+    const bool lds_ok = m > 0 && lda <= ((int64_t)1 << 24) &&
+                        sk::plan_lds(di, m, units, wide_ok, f16 ? 1 : 2, d, zeta, &plan);
     if ((flags & SK_VARIANT_LDS) && !lds_ok && m > 0) return SK_ERR_UNSUPPORTED;
     const bool use_lds = m > 0 && !(flags & SK_VARIANT_FLAT) && lds_ok;
     const bool accumulate = (flags & SK_ACCUMULATE) != 0;
@@ -237,8 +269,40 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
     sk::DevInfo di;
     if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
     sk::LdsPlan plan{};
-    const int64_t lanes = precision == SK_PRECISION_F16ACC ? n / 2 : n;
-    if (sk::plan_lds(di, m, lanes, d, zeta, &plan)) *bytes = plan.ws_bytes;
+    const int64_t units = precision == SK_PRECISION_F16ACC ? n / 2 : n;
+    // sizes for the widest plan: a two-word plan needs no more workspace
+    // than the one-word plan the same call may fall back to
+    size_t best = 0;
+    const int gw = precision == SK_PRECISION_F16ACC ? 1 : 2;
+    if (sk::plan_lds(di, m, units, true, gw, d, zeta, &plan)) best = plan.ws_bytes;
+    if (sk::plan_lds(di, m, units, false, gw, d, zeta, &plan) && plan.ws_bytes > best)
+        best = plan.ws_bytes;
+    *bytes = best;
+    return SK_OK;
+}
+
+sk_status sk_lds_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda, int32_t d,
+                               int32_t zeta, int32_t wide_ok, int32_t num_cu, int32_t max_lds,
+                               int64_t *out) {
+    if (out == nullptr) return SK_ERR_NULL;
+    for (int i = 0; i < SK_PLAN_FIELDS; ++i) out[i] = 0;
+    if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC) return SK_ERR_ARG;
+    if (m < 1 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0 || lda < n)
+        return SK_ERR_SHAPE;
+    if (precision == SK_PRECISION_F16ACC && n % 2 != 0) return SK_ERR_SHAPE;
+    if (num_cu < 1 || max_lds < 1) return SK_ERR_ARG;
+    const bool f16 = precision == SK_PRECISION_F16ACC;
+    const int64_t vec = f16 ? 4 : 2;
+    sk::DevInfo di{num_cu, max_lds};
+    sk::LdsPlan p{};
+    if (lda > ((int64_t)1 << 24) ||
+        !sk::plan_lds(di, m, f16 ? n / 2 : n, wide_ok != 0 && lda % vec == 0, f16 ? 1 : 2, d,
+                      zeta, &p))
+        return SK_OK;
+    const int64_t v[SK_PLAN_FIELDS] = {1, p.words, p.slice, p.groups, p.zg, p.threads,
+                                       p.rows_per_chunk, p.chunks, p.slices, p.grid,
+                                       (int64_t)p.lds_bytes, (int64_t)p.ws_bytes};
+    for (int i = 0; i < SK_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }
 

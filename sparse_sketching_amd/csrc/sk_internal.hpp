@@ -20,20 +20,28 @@ hipError_t launch_zero_words(uint32_t *B, int64_t rows, int64_t words, int64_t l
 hipError_t launch_meta(uint64_t seed, int64_t row_offset, int64_t m, int32_t d, int32_t zeta,
                        float scale, int32_t *row_idx, float *val, hipStream_t stream);
 
-// Shape of an LDS-privatized SparseStack launch (k_lock_apply).
+// Shape of an LDS-privatized SparseStack launch (k_stack_apply).
 struct LdsPlan {
-    int slice;              // lanes per slice: columns (FP32) or column pairs (FP16)
+    int words;              // 32-bit words per lane (1, or 2 as one 64-bit word)
+    int slice;              // lanes per column slice
+    int groups;             // block groups: each row is read once per group
+    int zg;                 // stack blocks per group
     int threads;            // workgroup size
     int64_t rows_per_chunk; // input rows per workgroup
-    int64_t chunks;         // row chunks (grid y)
-    int64_t slices;         // column slices (grid x)
-    size_t lds_bytes;       // dynamic LDS per workgroup: d x slice partial + d locks
+    int64_t chunks;         // row chunks
+    int64_t slices;         // column slices
+    int64_t grid;           // workgroups (1-D, XCD-grouped)
+    size_t lds_bytes;       // dynamic LDS per workgroup: partial + dummy rows
     size_t ws_bytes;        // workspace for the store-and-reduce flush
 };
-// Returns false when even the narrowest slice does not fit in LDS, or when
-// zeta is beyond what one lock instruction covers (then the flat kernel runs).
-bool plan_lds(const DevInfo &di, int64_t m, int64_t lanes_total, int32_t d, int32_t zeta,
-              LdsPlan *plan);
+// Plan for `units` 32-bit words per row of B (columns, or column pairs for
+// FP16).  wide_ok: rows of A allow two-word (8- or 16-byte) lane loads.
+// Returns false when no slice fits in LDS, or zeta > 64 (the flat kernel
+// runs then).
+// max_groups_wide: block groups a two-word plan may use (each group reads
+// every row of A once more through L2).
+bool plan_lds(const DevInfo &di, int64_t m, int64_t units, bool wide_ok, int max_groups_wide,
+              int32_t d, int32_t zeta, LdsPlan *plan);
 
 hipError_t launch_f32_flat(const float *A, int64_t m, int32_t n, int64_t lda,
                            const int32_t *row_idx, const float *val, int32_t zeta, float *B,

@@ -18,7 +18,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
     assert set(names) == {"sk_meta_generate", "sk_apply_f32", "sk_apply_f16acc",
-                          "sk_apply_workspace_size", "sk_apply_blockperm", "sk_status_string"}
+                          "sk_apply_workspace_size", "sk_lds_plan_describe",
+                          "sk_apply_blockperm", "sk_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -135,3 +136,71 @@ def test_figure2_shape_is_accepted_up_to_s(lib):
     # the shapes validate; s=2 is a valid request this library does not build.
     assert lib.sk_apply_blockperm(A, 2048, 64, 64, 1024, 16, 4, 2, 7, B, 64, 0, None) == \
         b.SK_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------ LDS plan vs kernel bounds
+
+MI355X = dict(num_cu=256, max_lds=160 * 1024)
+PLAN_SHAPES = [
+    # (m, n, d, zeta): the scale, coherence, range and tiny workloads, ragged
+    # and degenerate test shapes, and wide/narrow extremes
+    (1 << 20, 256, 512, 4), (4096, 32, 64, 4), (4096, 32, 64, 1), (1 << 20, 128, 256, 1),
+    (1 << 20, 128, 512, 2), (1 << 20, 128, 1024, 8), (1 << 18, 128, 256, 8),
+    (4194304, 64, 128, 4), (1000, 38, 96, 3), (777, 130, 40, 8), (5, 2, 16, 16),
+    (3001, 64, 5, 5), (2048, 66, 88, 11), (2048, 16, 8192, 4), (9000, 32, 64, 4),
+    (1 << 16, 1024, 512, 4), (1 << 16, 512, 640, 4), (1 << 12, 4096, 64, 64), (300, 2, 64, 64),
+]
+
+
+@pytest.mark.parametrize("precision", [b.SK_PRECISION_F32, b.SK_PRECISION_F16ACC])
+@pytest.mark.parametrize("wide_ok", [True, False])
+@pytest.mark.parametrize("m,n,d,zeta", PLAN_SHAPES)
+def test_lds_plan_fits_kernel(lib, precision, wide_ok, m, n, d, zeta):
+    """Replays the apply kernel's workgroup mapping and LDS/workspace index
+    arithmetic on the plan: every (slice, chunk, block group) is covered
+    once, the partial and the wavefronts' dummy rows fit the LDS the plan
+    reserves, each workgroup's flush stays inside the workspace, and
+    two-word lanes only come with full 64-lane slices (the kernels that
+    exist)."""
+    f16 = precision == b.SK_PRECISION_F16ACC
+    if f16 and n % 2:
+        pytest.skip("odd n")
+    p = b.sk_lds_plan_describe(precision, m, n, n, d, zeta, wide_ok, **MI355X)
+    if not p["lds"]:
+        # flat fallback only when the partial cannot fit or zeta > 64
+        assert zeta > 64 or (d // zeta) * zeta * 8 * 4 + 16 * 64 * 4 > MI355X["max_lds"]
+        return
+    w, sp, g, zg = p["words"], p["slice"], p["groups"], p["zg"]
+    assert w in (1, 2) and sp in (8, 16, 32, 64) and g * zg == zeta
+    if w == 2:
+        assert sp == 64 and wide_ok
+    units = n // 2 if f16 else n
+    assert p["slices"] * sp * w >= units
+    assert p["threads"] in (512, 1024)
+    nw = p["threads"] // 64
+    db = d // zeta
+    dl = zg * db
+    assert (dl * sp + nw * 64) * w * 4 <= p["lds_bytes"] <= MI355X["max_lds"]
+    assert p["chunks"] * p["rows_per_chunk"] >= m > (p["chunks"] - 1) * p["rows_per_chunk"]
+    seen = set()
+    for wg in range(p["grid"]):
+        q = wg >> 3
+        grp, uid = q % g, (q // g) * 8 + (wg & 7)
+        if uid >= p["slices"] * p["chunks"]:
+            continue
+        sl, ch = uid % p["slices"], uid // p["slices"]
+        assert (sl, ch, grp) not in seen
+        seen.add((sl, ch, grp))
+        row0 = grp * zg * db
+        base = (sl * p["chunks"] + ch) * d * sp * w + row0 * sp * w
+        assert (base + dl * sp * w) * 4 <= p["ws_bytes"]
+    assert len(seen) == p["slices"] * p["chunks"] * g
+
+
+def test_plan_describe_validation(lib):
+    out = (ctypes.c_int64 * b.PLAN_FIELDS.__len__())()
+    assert lib.sk_lds_plan_describe(0, 10, 0, 8, 8, 1, 1, 256, 163840, out) == b.SK_ERR_SHAPE
+    assert lib.sk_lds_plan_describe(3, 10, 8, 8, 8, 1, 1, 256, 163840, out) == b.SK_ERR_ARG
+    assert lib.sk_lds_plan_describe(1, 10, 7, 8, 8, 1, 1, 256, 163840, out) == b.SK_ERR_SHAPE
+    assert lib.sk_lds_plan_describe(0, 10, 8, 8, 8, 1, 1, 0, 163840, out) == b.SK_ERR_ARG
+    assert lib.sk_lds_plan_describe(0, 10, 8, 8, 8, 1, 1, 256, 163840, None) == b.SK_ERR_NULL

@@ -221,6 +221,27 @@ def test_out_of_range_rows_are_ignored(precision):
         assert np.array_equal(B, ref)
 
 
+@pytest.mark.parametrize("precision", ["f32", "f16acc"])
+@pytest.mark.parametrize("variant", ALL)
+def test_general_values(precision, variant):
+    """Metadata values of differing magnitudes (any FP32 val, not only
+    +-1/sqrt(zeta)): every kernel applies val*a per contribution.  Values are
+    dyadic, so with integer A every FP32 partial sum is exact; for FP16 the
+    products are exact halves/quarters and sums stay below 2^10."""
+    say(f"general values {precision} {variant}")
+    m, n, d, zeta = 3000, 64, 64, 4
+    A = inputs.integer_matrix(m, n, -2, 2, seed=13)
+    ri_h, v_h = oracle.meta_ref(9, m, d, zeta)
+    g = np.random.default_rng(5)
+    v_gen = (v_h * g.choice(np.array([0.25, 0.5, 1.0, 2.0], dtype=np.float32), size=v_h.size)
+             ).astype(np.float32)
+    v_gen[::97] = v_h[::97]                     # some blocks keep equal magnitudes
+    B, _, _ = run(A, d, zeta, 0, precision, variant, meta=(to_dev(ri_h), to_dev(v_gen)))
+    ref = oracle.sketch_f64(A, ri_h, v_gen, d, zeta)
+    assert np.abs(ref).max() < 1024
+    assert np.array_equal(B, ref)
+
+
 def test_large_d_falls_back_to_flat():
     """d x 8 words exceed LDS: LDS is refused when forced, FLAT serves the default."""
     m, n, d, zeta = 2048, 16, 8192, 4
