@@ -3,18 +3,19 @@
 
 Step = one complete FP16-accumulate SparseStack sketch of the scale
 workload (A 2^20 x 256 FP32 N(0,1), zeta = 4, d = 512 = 2n): metadata
-generation + output zeroing + application, all in libsksketch's HIP
-kernels, with A already resident in HBM (FP16 sketching page §V-A: complete
-sketch time includes initialization, map generation and application).
+generation, then the LDS-privatized apply whose store-and-reduce flush also
+initializes B, all in libsksketch's HIP kernels, with A already resident in
+HBM (FP16 sketching page §V-A: complete sketch time includes
+initialization, map generation and application).
 
 value = algorithmic bytes (A + metadata + sketch, each counted once) per
 step / step time, in GB/s.  The same run times the comparison legs: the
 flat FP32 scatter (one global atomic per contribution), the LDS-privatized
 FP32 sketch, the page's flat FP16 design, and BlockPerm-SJLT on its own
 workload (A 2^21 x 512, d = 1024, M = 64, kappa = 4, s = 1).  The roofline
-block times the dominant kernel (the FP16 LDS apply kernel) alone with HIP
-events on its stream; cpu_baseline times the CPU oracle on a row sample of
-the same workload.
+block times the dominant call, one sk_apply_f16acc (the apply kernel and
+the reduce kernel it launches), with HIP events on its stream;
+cpu_baseline times the CPU oracle on the same workload's rows, one thread.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --profile-pass   # short fixed run for rocprofv3 --pmc
@@ -207,10 +208,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32-in/f16-acc",
+        "dtype": "f16",
         "data": "synthetic N(0,1) A drawn on device with a seeded generator",
         "config": {"workload": f"SparseStack m=2^20 n={n} zeta={zeta} d={d} (d=2n), dense N(0,1)",
                    "m": m, "n": n, "d": d, "zeta": zeta, "seed": SEED,
+                   "precision": "FP32 products, RN to FP16, FP16 RN accumulation",
                    "algorithmic_bytes": bytes16},
         "hbm_frac": round(gbs16 / HBM_PEAK_GBS, 4),
         "fp32_flat_ms": round(ms32_flat, 5),
@@ -225,7 +227,7 @@ def main():
         "blockperm": bp,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "k_lock_apply<AccF16,4> + k_lock_reduce<AccF16>",
+                     "traffic": None, "kernel": "k_stack_apply<AccF16,1,4,true> + k_stack_reduce<AccF16>",
                      "kernel_ms": round(ms_kernel, 5),
                      "apply_atomic_flush_ms": round(ms_kernel_atomic, 5)},
         "cpu_baseline": None,
