@@ -2,20 +2,24 @@
 """Benchmark: complete-sketch throughput of SparseStack on one MI355X.
 
 Step = one complete FP16-accumulate SparseStack sketch of the scale
-workload (A 2^20 x 256 FP32 N(0,1), zeta = 4, d = 512 = 2n): metadata
-generation, then the LDS-privatized apply whose store-and-reduce flush also
-initializes B, all in libsksketch's HIP kernels, with A already resident in
-HBM (FP16 sketching page §V-A: complete sketch time includes
-initialization, map generation and application).
+workload (A 2^20 x 256 FP32 N(0,1), zeta = 4, d = 512 = 2n) with A already
+resident in HBM: one sk_sketch_f16acc call, whose fused kernel draws the
+Philox metadata in-kernel and keeps its partials in registers, followed by
+the reduce kernel that writes (and so initializes) B (FP16 sketching page
+§V-A: complete sketch time includes initialization, map generation and
+application).
 
-value = algorithmic bytes (A + metadata + sketch, each counted once) per
-step / step time, in GB/s.  The same run times the comparison legs: the
-flat FP32 scatter (one global atomic per contribution), the LDS-privatized
-FP32 sketch, the page's flat FP16 design, and BlockPerm-SJLT on its own
-workload (A 2^21 x 512, d = 1024, M = 64, kappa = 4, s = 1).  The roofline
-block times the dominant call, one sk_apply_f16acc (the apply kernel and
-the reduce kernel it launches), with HIP events on its stream;
-cpu_baseline times the CPU oracle on the same workload's rows, one thread.
+value = the metric's algorithmic bytes (A + metadata + sketch, each counted
+once, as if the metadata were stored) per step / step time, in GB/s: the
+effective rate of the complete sketch.  The roofline block is stricter: it
+counts only the bytes the fused path must move (A + sketch) against the
+dominant call's time, measured with HIP events on its stream.  The same run
+times the comparison legs: the stored-metadata FP16 sketch (sk_meta_generate
++ the LDS apply), the flat FP32 scatter (one global atomic per
+contribution), the LDS and fused FP32 sketches, the page's flat FP16
+design, and BlockPerm-SJLT on its own workload (A 2^21 x 512, d = 1024,
+M = 64, kappa = 4, s = 1).  cpu_baseline times the CPU oracle on the same
+workload's rows, one thread.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --profile-pass   # short fixed run for rocprofv3 --pmc
@@ -39,6 +43,11 @@ SEED = 1
 def sparsestack_bytes(m, n, d, zeta, out_elem):
     """A read once (4mn) + metadata row_idx/val (8 m zeta) + sketch (d n)."""
     return 4 * m * n + 8 * m * zeta + out_elem * d * n
+
+
+def fused_bytes(m, n, d, out_elem):
+    """What the fused path must move: A once and the sketch once."""
+    return 4 * m * n + out_elem * d * n
 
 
 def blockperm_bytes(m, n, d):
@@ -123,6 +132,8 @@ def main():
 
     ws16 = b.workspace(A, d, zeta, "f16acc")
     ws32 = b.workspace(A, d, zeta, "f32")
+    wsf16 = b.sketch_workspace(A, d, zeta, "f16acc")
+    wsf32 = b.sketch_workspace(A, d, zeta, "f32")
 
     def meta():
         b.sk_meta_generate(SEED, 0, m, d, zeta, ri, val, sp)
@@ -133,7 +144,15 @@ def main():
     def f32(flags=0, ws=ws32):
         b.sk_apply_f32(A, m, n, n, ri, val, zeta, B32, d, n, flags, ws, 0, sp)
 
+    def fused16(flags=0):
+        b.sk_sketch_f16acc(SEED, 0, A, m, n, n, d, zeta, B16, n, flags, wsf16, 0, sp)
+
+    def fused32(flags=0):
+        b.sk_sketch_f32(SEED, 0, A, m, n, n, d, zeta, B32, n, flags, wsf32, 0, sp)
+
     if args.profile_pass:
+        for _ in range(3):
+            fused16()
         meta()
         for _ in range(3):
             f16()
@@ -142,7 +161,8 @@ def main():
         for _ in range(3):
             dst.copy_(src)                          # 1 GiB read + 1 GiB write
         torch.cuda.synchronize()
-        print("profile pass done: 3 x f16 LDS apply + reduce, 3 x 1 GiB copy", flush=True)
+        print("profile pass done: 3 x fused f16 sketch, 3 x f16 LDS apply + reduce, "
+              "3 x 1 GiB copy", flush=True)
         return
 
     K, W = args.steps, args.warmup
@@ -151,15 +171,21 @@ def main():
 
     # bring clocks and caches to a steady state before any timed region
     for _ in range(max(20, W)):
+        fused16()
         meta()
         f16()
         f32(b.SK_VARIANT_FLAT, None)
     torch.cuda.synchronize()
 
-    # headline step: complete FP16-accumulate sketch (metadata, then the LDS
-    # apply whose store-and-reduce flush also initializes B)
-    ms16 = timed(lambda: (meta(), f16()), K, W, stream)
-    print(f"[bench] f16acc complete sketch {ms16:.4f} ms", file=sys.stderr, flush=True)
+    # headline step: complete FP16-accumulate sketch in one fused call
+    ms16 = timed(fused16, K, W, stream)
+    print(f"[bench] f16acc complete sketch (fused) {ms16:.4f} ms", file=sys.stderr, flush=True)
+    ms32_fused = timed(fused32, K, W, stream)
+    # the stored-metadata sketch: metadata kernel, then the LDS apply whose
+    # store-and-reduce flush also initializes B
+    ms16_meta = timed(lambda: (meta(), f16()), K, W, stream)
+    print(f"[bench] f32 fused {ms32_fused:.4f} ms, f16acc meta+LDS apply {ms16_meta:.4f} ms",
+          file=sys.stderr, flush=True)
     ms16_atomic = timed(lambda: (meta(), f16(0, None)), K, W, stream)
     ms32_flat = timed(lambda: (meta(), f32(b.SK_VARIANT_FLAT, None)), K, W, stream)
     ms32_lds = timed(lambda: (meta(), f32()), K, W, stream)
@@ -182,7 +208,7 @@ def main():
     A_host = None if args.no_cpu_baseline else A.cpu().numpy()
     bp = None
     if not args.no_blockperm:
-        del A, ri, val, ws16, ws32
+        del A, ri, val, ws16, ws32, wsf16, wsf32
         torch.cuda.empty_cache()
         Abp = inputs.gaussian_torch(BP_M, BP_N, seed=0)
         Y = torch.empty((BP_D, BP_N), dtype=torch.float32, device=dev)
@@ -196,7 +222,8 @@ def main():
         del Abp, Y
 
     gbs16 = bytes16 / ms16 / 1e6
-    kernel_gbs = bytes16 / ms_kernel / 1e6
+    fbytes16 = fused_bytes(m, n, d, 2)
+    kernel_gbs = fbytes16 / ms16 / 1e6
     out = {
         "metric": "complete-sketch SA GB/s and % HBM roofline, zeta=4, d=2n, FP16-acc vs FP32",
         "value": round(gbs16, 2),
@@ -213,22 +240,29 @@ def main():
         "config": {"workload": f"SparseStack m=2^20 n={n} zeta={zeta} d={d} (d=2n), dense N(0,1)",
                    "m": m, "n": n, "d": d, "zeta": zeta, "seed": SEED,
                    "precision": "FP32 products, RN to FP16, FP16 RN accumulation",
+                   "path": "sk_sketch_f16acc (Philox metadata drawn in-kernel)",
                    "algorithmic_bytes": bytes16},
         "hbm_frac": round(gbs16 / HBM_PEAK_GBS, 4),
         "fp32_flat_ms": round(ms32_flat, 5),
         "fp32_flat_GBps": round(bytes32 / ms32_flat / 1e6, 2),
         "fp32_lds_ms": round(ms32_lds, 5),
+        "fp32_fused_ms": round(ms32_fused, 5),
+        "fp16_meta_lds_ms": round(ms16_meta, 5),
+        "fp16_meta_lds_GBps": round(bytes16 / ms16_meta / 1e6, 2),
         "fp16_flat_ms": round(ms16_flat, 5),
         "fp16_lds_atomic_flush_ms": round(ms16_atomic, 5),
         "speedup_vs_fp32_flat": round(ms32_flat / ms16, 3),
         "speedup_vs_fp32_lds": round(ms32_lds / ms16, 3),
+        "speedup_vs_fp32_fused": round(ms32_fused / ms16, 3),
+        "fp16_lds_apply_ms": round(ms_kernel, 5),
         "meta_ms": round(ms_meta, 5),
         "copy_GBps": round(copy_gbs, 1),
         "blockperm": bp,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "k_stack_apply<AccF16,1,4,true> + k_stack_reduce<AccF16>",
-                     "kernel_ms": round(ms_kernel, 5),
+                     "traffic": None,
+                     "kernel": "k_stack_fused<AccF16,32> + k_stack_reduce<AccF16>",
+                     "kernel_ms": round(ms16, 5), "algorithmic_bytes": fbytes16,
                      "apply_atomic_flush_ms": round(ms_kernel_atomic, 5)},
         "cpu_baseline": None,
     }

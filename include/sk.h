@@ -62,7 +62,7 @@ typedef enum sk_status {
 #define SK_VARIANT_LDS  4u  /* LDS-privatized partial sketches (default when
                                the d x slice partial fits in LDS) */
 
-/* precision argument of sk_apply_workspace_size */
+/* precision argument of sk_apply_workspace_size and sk_sketch_workspace_size */
 #define SK_PRECISION_F32    0
 #define SK_PRECISION_F16ACC 1
 
@@ -171,6 +171,79 @@ sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
  */
 sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32_t d,
                                   int32_t zeta, uint32_t flags, size_t *bytes);
+
+/*
+ * sk_sketch_f32 / sk_sketch_f16acc: the complete SparseStack sketch in one
+ * call, with the metadata drawn on the fly instead of stored.
+ * (FP16 sketching page §III-C: the routing and signs come from a
+ * counter-based Philox generator; FlashSketch page §5.2: a sketch's
+ * randomness can be made inside the apply kernel, so S is never stored.)
+ *
+ * Computes exactly what sk_meta_generate(seed, row_offset, m, d, zeta)
+ * followed by sk_apply_f32 / sk_apply_f16acc (same flags) computes: the
+ * same S, every contribution the FP32 product a*val, and for FP16 each
+ * contribution rounded to FP16 nearest-even and accumulated with FP16
+ * nearest-even additions.  The fused kernel keeps each workgroup's partial
+ * in registers and writes it once to the workspace; a reduce kernel then
+ * writes B as the sum of the partials in a fixed order (no atomics, B needs
+ * no separate zeroing).  Shapes the fused kernel does not cover (zeta > 16,
+ * d not a multiple of 16, fewer than 128 (FP16) / 64 (FP32) columns, rows
+ * of A not 16-byte (FP16) / 8-byte (FP32) aligned, row ownership that does
+ * not fit the registers) run sk_meta_generate into the workspace and then
+ * the LDS (or flat) apply; the result is the same sketch.
+ *
+ *   seed, row_offset  as for sk_meta_generate (row_offset >= 0 is the global
+ *            index of A's first row, so row chunks with SK_ACCUMULATE give
+ *            the sketch of the whole matrix).
+ *   A        device float, m x n, lda >= n (FP16: n, lda even, A 8-byte
+ *            aligned).
+ *   B        device float (FP32) or IEEE binary16 bits (FP16: ldb even, B
+ *            4-byte aligned), d x n, ldb >= n.
+ *   flags    SK_ACCUMULATE or 0.
+ *   workspace, workspace_bytes
+ *            device scratch, required when m > 0: 16-byte aligned, disjoint
+ *            from A and B, at least sk_sketch_workspace_size bytes.  The
+ *            caller owns it; its contents on return are unspecified; calls
+ *            that share it must be ordered (same stream).
+ * Errors: SK_ERR_NULL (A, B or workspace NULL when needed), SK_ERR_SHAPE
+ * (sizes, zeta range, d % zeta, lda/ldb < n, odd n for FP16, row_offset < 0),
+ * SK_ERR_ALIGN (workspace, or the FP16 alignment rules), SK_ERR_ARG (other
+ * flags, overlapping buffers, workspace smaller than required), SK_ERR_HIP.
+ */
+sk_status sk_sketch_f32(uint64_t seed, int64_t row_offset, const float *A, int64_t m, int32_t n,
+                        int64_t lda, int32_t d, int32_t zeta, float *B, int64_t ldb,
+                        uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
+sk_status sk_sketch_f16acc(uint64_t seed, int64_t row_offset, const float *A, int64_t m,
+                           int32_t n, int64_t lda, int32_t d, int32_t zeta, uint16_t *B,
+                           int64_t ldb, uint32_t flags, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * sk_sketch_workspace_size: workspace bytes an sk_sketch_f32 (precision
+ * SK_PRECISION_F32) or sk_sketch_f16acc (SK_PRECISION_F16ACC) call with
+ * these sizes needs on the current device, whatever its lda and A's
+ * alignment (the larger of the fused kernel's partials and the fallback's
+ * metadata plus apply workspace); 0 for m = 0.
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ARG (precision), SK_ERR_HIP.
+ */
+sk_status sk_sketch_workspace_size(int32_t precision, int64_t m, int32_t n, int32_t d,
+                                   int32_t zeta, size_t *bytes);
+
+/*
+ * sk_fused_plan_describe: the launch plan of the fused kernel behind
+ * sk_sketch_*, for the given sizes, lda, whether A's base is aligned for its
+ * lane loads (a_aligned), and the device's compute units and per-workgroup
+ * LDS bytes.  Pure host computation (no HIP call), for tests and tools that
+ * check a plan against the kernel's index bounds.
+ *   out  int64[SK_FUSED_PLAN_FIELDS], written: {fused kernel used (0: the
+ *        fallback runs), output rows per wavefront, output row groups,
+ *        column slices, rows per chunk, chunks, workgroups, workspace bytes}.
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ARG (precision, num_cu, max_lds).
+ */
+#define SK_FUSED_PLAN_FIELDS 8
+sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
+                                 int32_t a_aligned, int32_t d, int32_t zeta, int32_t num_cu,
+                                 int32_t max_lds, int64_t *out);
 
 /*
  * sk_apply_blockperm: Y = S A (or Y += S A) for S ~ BlockPerm-SJLT.

@@ -8,9 +8,12 @@ draws the seeded synthetic workloads.
 from .binding import (SK_ACCUMULATE, SK_PRECISION_F16ACC, SK_PRECISION_F32, SK_VARIANT_FLAT,
                       SK_VARIANT_LDS, SketchError, apply, blockperm, load, meta,
                       sk_apply_blockperm, sk_apply_f16acc, sk_apply_f32, sk_apply_workspace_size,
-                      sk_meta_generate, sketch, status_string, workspace)
+                      sk_meta_generate, sk_sketch_f16acc, sk_sketch_f32,
+                      sk_sketch_workspace_size, sketch, sketch_fused, sketch_workspace,
+                      status_string, workspace)
 
 __all__ = ["SK_ACCUMULATE", "SK_PRECISION_F16ACC", "SK_PRECISION_F32", "SK_VARIANT_FLAT",
            "SK_VARIANT_LDS", "SketchError", "apply", "blockperm", "load", "meta",
            "sk_apply_blockperm", "sk_apply_f16acc", "sk_apply_f32", "sk_apply_workspace_size",
-           "sk_meta_generate", "sketch", "status_string", "workspace"]
+           "sk_meta_generate", "sk_sketch_f16acc", "sk_sketch_f32", "sk_sketch_workspace_size",
+           "sketch", "sketch_fused", "sketch_workspace", "status_string", "workspace"]

@@ -43,6 +43,17 @@ _SIGNATURES = {
     "sk_lds_plan_describe": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32,
                                         _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
                                         _c.POINTER(_c.c_int64)]),
+    "sk_sketch_f32": (_c.c_int, [_c.c_uint64, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_int32,
+                                 _c.c_int64, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_int64,
+                                 _c.c_uint32, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "sk_sketch_f16acc": (_c.c_int, [_c.c_uint64, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_int32,
+                                    _c.c_int64, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_int64,
+                                    _c.c_uint32, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "sk_sketch_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32,
+                                            _c.c_int32, _c.POINTER(_c.c_size_t)]),
+    "sk_fused_plan_describe": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int64,
+                                          _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
+                                          _c.c_int32, _c.POINTER(_c.c_int64)]),
     "sk_status_string": (_c.c_char_p, [_c.c_int]),
 }
 
@@ -167,6 +178,40 @@ def sk_lds_plan_describe(precision, m, n, lda, d, zeta, wide_ok, num_cu, max_lds
     return dict(zip(PLAN_FIELDS, list(out)))
 
 
+def sk_sketch_f32(seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags=0, workspace=None,
+                  workspace_bytes=0, stream=None):
+    _check("sk_sketch_f32", load().sk_sketch_f32(
+        seed, row_offset, _ptr(A), m, n, lda, d, zeta, _ptr(B), ldb, flags, _ptr(workspace),
+        _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def sk_sketch_f16acc(seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags=0, workspace=None,
+                     workspace_bytes=0, stream=None):
+    _check("sk_sketch_f16acc", load().sk_sketch_f16acc(
+        seed, row_offset, _ptr(A), m, n, lda, d, zeta, _ptr(B), ldb, flags, _ptr(workspace),
+        _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def sk_sketch_workspace_size(precision, m, n, d, zeta):
+    """Bytes of workspace an sk_sketch_* call needs (0 for m = 0)."""
+    out = ctypes.c_size_t(0)
+    _check("sk_sketch_workspace_size", load().sk_sketch_workspace_size(
+        precision, m, n, d, zeta, ctypes.byref(out)))
+    return out.value
+
+
+FUSED_PLAN_FIELDS = ("fused", "rows_per_wave", "groups", "slices", "rows_per_chunk", "chunks",
+                     "grid", "ws_bytes")
+
+
+def sk_fused_plan_describe(precision, m, n, lda, a_aligned, d, zeta, num_cu, max_lds):
+    """The fused kernel's launch plan as a dict (host computation)."""
+    out = (ctypes.c_int64 * len(FUSED_PLAN_FIELDS))()
+    _check("sk_fused_plan_describe", load().sk_fused_plan_describe(
+        precision, m, n, lda, int(bool(a_aligned)), d, zeta, num_cu, max_lds, out))
+    return dict(zip(FUSED_PLAN_FIELDS, list(out)))
+
+
 # ---- tensor helpers ------------------------------------------------------
 
 def _need_device(t, dtype, name):
@@ -230,6 +275,36 @@ def sketch(A, d, zeta, seed, precision="f16acc", flags=0, ws=True, stream=None):
     """Complete sketch: metadata generation, output initialization and application."""
     row_idx, val = meta(seed, A.shape[0], d, zeta, device=A.device, stream=stream)
     return apply(A, row_idx, val, zeta, d, precision, flags=flags, ws=ws, stream=stream)
+
+
+def sketch_workspace(A, d, zeta, precision="f16acc"):
+    """A device byte tensor large enough for sketch_fused() (None for m = 0)."""
+    import torch
+    prec = SK_PRECISION_F16ACC if precision == "f16acc" else SK_PRECISION_F32
+    nbytes = sk_sketch_workspace_size(prec, A.shape[0], A.shape[1], d, zeta)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=A.device)
+
+
+def sketch_fused(A, d, zeta, seed, precision="f16acc", row_offset=0, out=None, flags=0, ws=None,
+                 stream=None):
+    """Complete sketch in one call, metadata drawn on the fly (same S as
+    meta(seed, ..., row_offset) + apply).  ws: a byte tensor of at least
+    sk_sketch_workspace_size bytes, or None to allocate one."""
+    import torch
+    _need_device(A, torch.float32, "A")
+    m, n = A.shape
+    dt = torch.float16 if precision == "f16acc" else torch.float32
+    if out is None:
+        out = torch.empty((d, n), dtype=dt, device=A.device)
+    _need_device(out, dt, "out")
+    if ws is None and m:
+        ws = sketch_workspace(A, d, zeta, precision)
+    fn = sk_sketch_f16acc if precision == "f16acc" else sk_sketch_f32
+    fn(seed, row_offset, A, m, n, A.stride(0) if m else n, d, zeta, out, out.stride(0), flags,
+       ws, 0, stream)
+    return out
 
 
 def blockperm(A, d, M, kappa, seed, s=1, out=None, flags=0, stream=None):

@@ -199,6 +199,89 @@ sk_status check_workspace(const void *ws, size_t bytes, const float *A, int64_t 
     return SK_OK;
 }
 
+// Fused sketch: workspace layout of the fallback (metadata + LDS apply):
+// row_idx, then val, then the apply's workspace, each 256-byte aligned.
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t fallback_ws_bytes(const sk::DevInfo &di, bool f16, int64_t m, int32_t n, int32_t d,
+                         int32_t zeta) {
+    const size_t meta = align256((size_t)m * (size_t)zeta * 4);
+    size_t apply = 0;
+    sk::LdsPlan lp{};
+    const int64_t units = f16 ? n / 2 : n;
+    const int gw = f16 ? 1 : 2;
+    if (sk::plan_lds(di, m, units, true, gw, d, zeta, &lp)) apply = lp.ws_bytes;
+    if (sk::plan_lds(di, m, units, false, gw, d, zeta, &lp) && lp.ws_bytes > apply)
+        apply = lp.ws_bytes;
+    return 2 * meta + align256(apply);
+}
+
+// Bytes any sk_sketch_* call with these sizes may need, whatever lda and
+// A's alignment: the larger of the fused plan and the fallback.
+size_t sketch_ws_bytes(const sk::DevInfo &di, bool f16, int64_t m, int32_t n, int32_t d,
+                       int32_t zeta) {
+    if (m == 0) return 0;
+    size_t need = fallback_ws_bytes(di, f16, m, n, d, zeta);
+    sk::FusedPlan fp{};
+    if (sk::plan_fused(di, f16, m, n, n, true, d, zeta, &fp) && fp.ws_bytes > need)
+        need = fp.ws_bytes;
+    return need;
+}
+
+sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const float *A, int64_t m,
+                          int32_t n, int64_t lda, int32_t d, int32_t zeta, void *B,
+                          int64_t ldb, uint32_t flags, void *workspace, size_t workspace_bytes,
+                          hipStream_t s) {
+    const size_t belem = f16 ? 2 : 4;
+    if (m < 0 || row_offset < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0)
+        return SK_ERR_SHAPE;
+    if (lda < n || ldb < n) return SK_ERR_SHAPE;
+    if (m > (INT64_MAX / 8) / (zeta > lda ? zeta : lda)) return SK_ERR_SHAPE;
+    if (f16 && n % 2 != 0) return SK_ERR_SHAPE;
+    if (flags & ~SK_ACCUMULATE) return SK_ERR_ARG;
+    if (B == nullptr) return SK_ERR_NULL;
+    if (f16 && (ldb % 2 != 0 || (uintptr_t)B % 4 != 0)) return SK_ERR_ALIGN;
+    const size_t bspan = span_bytes(d, n, ldb, belem);
+    const bool accumulate = (flags & SK_ACCUMULATE) != 0;
+    if (m > 0) {
+        if (A == nullptr || workspace == nullptr) return SK_ERR_NULL;
+        if (f16 && (lda % 2 != 0 || (uintptr_t)A % 8 != 0)) return SK_ERR_ALIGN;
+        if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
+        const size_t aspan = span_bytes(m, n, lda, 4);
+        if (overlaps(A, aspan, B, bspan)) return SK_ERR_ARG;
+        if (overlaps(workspace, workspace_bytes, A, aspan) ||
+            overlaps(workspace, workspace_bytes, B, bspan))
+            return SK_ERR_ARG;
+    }
+    sk::DevInfo di;
+    if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
+    if (m == 0) {
+        if (accumulate) return SK_OK;
+        const hipError_t e =
+            f16 ? sk::launch_zero_words(static_cast<uint32_t *>(B), d, n / 2, ldb / 2, s)
+                : sk::launch_zero_words(static_cast<uint32_t *>(B), d, n, ldb, s);
+        return hip_status(e);
+    }
+    if (workspace_bytes < sketch_ws_bytes(di, f16, m, n, d, zeta)) return SK_ERR_ARG;
+    const float scale = scale_of(zeta);
+    const uintptr_t align = f16 ? 16 : 8;
+    sk::FusedPlan fp{};
+    if (sk::plan_fused(di, f16, m, n, lda, (uintptr_t)A % align == 0, d, zeta, &fp))
+        return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, d, zeta, scale,
+                                           B, ldb, static_cast<uint32_t *>(workspace),
+                                           accumulate ? 1 : 0, s));
+    // not covered by the fused kernel: metadata into the workspace, then
+    // the LDS (or flat) apply with the rest of it
+    char *w = static_cast<char *>(workspace);
+    const size_t meta = align256((size_t)m * (size_t)zeta * 4);
+    int32_t *ri = reinterpret_cast<int32_t *>(w);
+    float *v = reinterpret_cast<float *>(w + meta);
+    hipError_t e = sk::launch_meta(seed, row_offset, m, d, zeta, scale, ri, v, s);
+    if (e != hipSuccess) return SK_ERR_HIP;
+    return apply_dispatch(f16, A, m, n, lda, ri, v, zeta, B, d, ldb, flags & SK_ACCUMULATE,
+                          w + 2 * meta, workspace_bytes - 2 * meta, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,6 +386,56 @@ sk_status sk_lds_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t 
                                        p.rows_per_chunk, p.chunks, p.slices, p.grid,
                                        (int64_t)p.lds_bytes, (int64_t)p.ws_bytes};
     for (int i = 0; i < SK_PLAN_FIELDS; ++i) out[i] = v[i];
+    return SK_OK;
+}
+
+sk_status sk_sketch_f32(uint64_t seed, int64_t row_offset, const float *A, int64_t m, int32_t n,
+                        int64_t lda, int32_t d, int32_t zeta, float *B, int64_t ldb,
+                        uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
+    return sketch_dispatch(false, seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags, workspace,
+                           workspace_bytes, (hipStream_t)stream);
+}
+
+sk_status sk_sketch_f16acc(uint64_t seed, int64_t row_offset, const float *A, int64_t m,
+                           int32_t n, int64_t lda, int32_t d, int32_t zeta, uint16_t *B,
+                           int64_t ldb, uint32_t flags, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    return sketch_dispatch(true, seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags, workspace,
+                           workspace_bytes, (hipStream_t)stream);
+}
+
+sk_status sk_sketch_workspace_size(int32_t precision, int64_t m, int32_t n, int32_t d,
+                                   int32_t zeta, size_t *bytes) {
+    if (bytes == nullptr) return SK_ERR_NULL;
+    *bytes = 0;
+    if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC) return SK_ERR_ARG;
+    if (m < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0) return SK_ERR_SHAPE;
+    if (precision == SK_PRECISION_F16ACC && n % 2 != 0) return SK_ERR_SHAPE;
+    sk::DevInfo di;
+    if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
+    *bytes = sketch_ws_bytes(di, precision == SK_PRECISION_F16ACC, m, n, d, zeta);
+    return SK_OK;
+}
+
+sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
+                                 int32_t a_aligned, int32_t d, int32_t zeta, int32_t num_cu,
+                                 int32_t max_lds, int64_t *out) {
+    if (out == nullptr) return SK_ERR_NULL;
+    for (int i = 0; i < SK_FUSED_PLAN_FIELDS; ++i) out[i] = 0;
+    if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC) return SK_ERR_ARG;
+    if (m < 1 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0 || lda < n)
+        return SK_ERR_SHAPE;
+    if (precision == SK_PRECISION_F16ACC && n % 2 != 0) return SK_ERR_SHAPE;
+    if (num_cu < 1 || max_lds < 1) return SK_ERR_ARG;
+    sk::DevInfo di{num_cu, max_lds};
+    sk::FusedPlan p{};
+    if (!sk::plan_fused(di, precision == SK_PRECISION_F16ACC, m, n, lda, a_aligned != 0, d, zeta,
+                        &p))
+        return SK_OK;
+    const int64_t v[SK_FUSED_PLAN_FIELDS] = {1, p.rows_per_wave, p.groups, p.slices,
+                                             p.rows_per_chunk, p.chunks, p.grid,
+                                             (int64_t)p.ws_bytes};
+    for (int i = 0; i < SK_FUSED_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }
 

@@ -1,0 +1,298 @@
+// Fused SparseStack sketch for gfx950: the metadata is drawn inside the
+// apply kernel instead of being stored (FP16 sketching page §III-C names a
+// Philox metadata kernel; the FlashSketch page §5.2 makes a sketch's
+// randomness on the fly and never stores S).
+//
+// What is computed: B (=|+=) S A for the SparseStack S whose entries are
+// exactly those sk_meta_generate writes for (seed, row_offset): for global
+// row g and stack block t, Philox-4x32-10 of counter (g lo, g hi, t div 4, 0)
+// and key (seed lo, seed hi) gives word w = w_{t mod 4}; the row lands on
+// output row t*db + mulhi(w, db) (db = d/zeta) with sign (w & 1 ? - : +)
+// and magnitude c = float32(1/sqrt(zeta)).  Every contribution is the FP32
+// product a*val (FP16 sketching page §III-A); in the FP16 variant it is
+// rounded to FP16 nearest-even and added with FP16 nearest-even additions
+// (§III-B).  All values share the magnitude c and nearest-even rounding is
+// odd, so each row is multiplied (and rounded) once and every hit adds it or
+// its negation: bit-identical to rounding a*val per hit.
+//
+// How (MI355X-specific):
+//  * A workgroup (16 wavefronts) owns a chunk of input rows, a column slice
+//    of 64 lanes x 2 words (256 columns for FP16 column pairs, 128 for FP32)
+//    and a group of 16*R consecutive output rows; wavefront w keeps the
+//    partial of its R output rows (inside one stack block) in registers:
+//    no atomics of any kind, and no LDS read-modify-write.
+//  * Rows stream through LDS in stages of 128: each wavefront loads 8 rows
+//    (one coalesced 64-lane load per row), scales and rounds them once and
+//    writes the two-word contributions to a double-buffered LDS stage; one
+//    wavefront per stage draws the Philox words of the stage's 128 rows
+//    (one row per lane) into LDS.  After one barrier every wavefront scans
+//    the stage's entries of its block with a ballot per owned row and adds
+//    each hit's contribution (sign applied by XOR) to that row's registers.
+//    The next stage's rows are in flight from HBM while a stage is applied.
+//  * The partial is written once to the workspace, and the reduce kernel of
+//    the LDS apply (sk_stack_apply.hpp) sums the chunks in a fixed order
+//    into B: deterministic, and B needs no separate zeroing.
+#include "sk_internal.hpp"
+#include "sk_rng.hpp"
+#include "sk_stack_apply.hpp"
+
+namespace sk {
+namespace {
+
+constexpr int kStage = 128;             // input rows per LDS stage
+constexpr int kWaves = 16;              // wavefronts per workgroup
+constexpr int kRowsPerWave = kStage / kWaves;
+constexpr int kLaneGroups = kStage / 64;
+
+// All LDS writes of this wavefront have landed, then a workgroup barrier.
+// Unlike __syncthreads this leaves the wavefront's global loads in flight,
+// which is what lets the next stage stream while this one is applied.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <class T, int R>
+__global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs args) {
+    constexpr int K = 2 * T::kCols;     // floats of A per lane per row
+    typedef FVec<K> vec_t;
+    constexpr int S = kStage, D = kRowsPerWave, NL = kLaneGroups;
+    __shared__ uint2 hs0[S * 64];       // stage contributions, row j at [j*64, j*64+64)
+    __shared__ uint2 hs1[S * 64];
+    __shared__ uint32_t me0[kFusedMaxZeta * S];  // entry (t, j) at t*S + j: bucket | sign << 31
+    __shared__ uint32_t me1[kFusedMaxZeta * S];
+
+    // workgroup -> (slice, chunk, row group); the groups of one (slice,
+    // chunk) are 8 ids apart (same XCD under round-robin dispatch)
+    const int32_t G = args.groups;
+    const int32_t wg = blockIdx.x;
+    const int32_t q = wg >> 3;
+    const int32_t grp = q % G;
+    const int32_t unit_id = (q / G) * 8 + (wg & 7);
+    if (unit_id >= args.slices * args.chunks) return;
+    const int32_t slice = unit_id % args.slices;
+    const int32_t chunk = unit_id / args.slices;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int zeta = args.zeta;
+    const uint32_t db = (uint32_t)(args.d / zeta);
+    const int32_t lo = (grp * kWaves + wave) * R;       // first output row of the wave
+    const int32_t t = lo / (int32_t)db;                  // its stack block
+    const uint32_t lob = (uint32_t)(lo - t * (int32_t)db);
+    const int64_t r0 = (int64_t)chunk * args.rows_per_chunk;
+    const int64_t r1 = r0 + args.rows_per_chunk < args.m ? r0 + args.rows_per_chunk : args.m;
+    const int32_t nst = (int32_t)((r1 - r0 + S - 1) / S);
+    const int64_t lda = args.lda;
+    // the lane's K columns, clamped into the row (lanes past the last column
+    // load valid memory; their partial words are never reduced)
+    const int32_t col = slice * 64 * K + lane * K;
+    const int32_t col_c = col <= args.n - K ? col : args.n - K;
+    const float *__restrict__ A = args.A + col_c;
+    const float c = args.scale;
+
+    uint32_t acc[R][2];
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[k][0] = acc[k][1] = 0u;
+
+    // rows of stage s owned by this wave, clamped into the chunk
+    vec_t a[D];
+    auto load = [&](int32_t s) {
+        const int64_t base = r0 + (int64_t)s * S + wave * D;
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int64_t row = base + u < r1 ? base + u : r1 - 1;
+            a[u] = load_vec<K>(reinterpret_cast<const char *>(A + row * lda));
+        }
+    };
+    // contributions of the loaded rows into stage buffer hs; metadata of
+    // stage s into me (one wave per stage, rotating)
+    auto stage = [&](int32_t s, uint2 *hs, uint32_t *me) {
+#pragma unroll
+        for (int u = 0; u < D; ++u)
+            hs[(wave * D + u) * 64 + lane] =
+                make_uint2(T::contrib(a[u].x, c), T::contrib(a[u].x + T::kCols, c));
+        if (wave == (s & (kWaves - 1))) {
+            const uint32_t k0 = (uint32_t)args.seed, k1 = (uint32_t)(args.seed >> 32);
+#pragma unroll
+            for (int h = 0; h < NL; ++h) {
+                const uint64_t g = (uint64_t)args.row_offset +
+                                   (uint64_t)(r0 + (int64_t)s * S + h * 64 + lane);
+                for (int gq = 0; gq * 4 < zeta; ++gq) {
+                    const u32x4 w4 = philox4x32_10(
+                        u32x4{(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)gq, 0u}, k0, k1);
+                    const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (gq * 4 + j < zeta)
+                            me[(gq * 4 + j) * S + h * 64 + lane] =
+                                mulhi32(ww[j], db) | (ww[j] << 31);
+                }
+            }
+        }
+    };
+    // every hit of stage s on this wave's rows
+    auto process = [&](int32_t s, const uint2 *hs, const uint32_t *me) {
+        int32_t rl[NL];
+        uint32_t sg[NL];
+#pragma unroll
+        for (int h = 0; h < NL; ++h) {
+            const uint32_t e = me[t * S + h * 64 + lane];
+            const int64_t row = r0 + (int64_t)s * S + h * 64 + lane;
+            const uint32_t rk = (e & 0x7FFFFFFFu) - lob;
+            rl[h] = row < r1 && rk < (uint32_t)R ? (int32_t)rk : -1;
+            sg[h] = e & 0x80000000u;
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+#pragma unroll
+            for (int h = 0; h < NL; ++h) {
+                uint64_t mk = __ballot(rl[h] == k);
+                while (mk) {
+                    const int i = __builtin_ctzll(mk);
+                    mk &= mk - 1;
+                    const uint32_t m = T::signmask((uint32_t)__builtin_amdgcn_readlane((int)sg[h], i));
+                    const uint2 x = hs[(h * 64 + i) * 64 + lane];
+                    acc[k][0] = T::sum(acc[k][0], x.x ^ m);
+                    acc[k][1] = T::sum(acc[k][1], x.y ^ m);
+                }
+            }
+        }
+    };
+
+    // stage 0 staged and stage 1 loading, then per stage: apply it, stage
+    // the next one into the other buffer, start loading the one after
+    load(0);
+    stage(0, hs0, me0);
+    load(1);
+    __syncthreads();
+    for (int32_t s0 = 0; s0 < nst; s0 += 2) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int32_t s = s0 + b;
+            if (s < nst) {
+                process(s, b ? hs1 : hs0, b ? me1 : me0);
+                stage(s + 1, b ? hs0 : hs1, b ? me0 : me1);
+                load(s + 2);
+                lds_barrier();
+            }
+        }
+    }
+    // the loads past the last stage (clamped rows) must land before exit
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // the wave's R partial rows of this (slice, chunk)
+    uint32_t *dst = args.ws + ((int64_t)slice * args.chunks + chunk) * (int64_t)args.d * 128 +
+                    (int64_t)lo * 128 + lane * 2;
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+        *reinterpret_cast<uint2 *>(dst + k * 128) = make_uint2(acc[k][0], acc[k][1]);
+}
+
+template <class T>
+const void *pick_fused(int R) {
+    switch (R) {
+        case 4: return (const void *)k_stack_fused<T, 4>;
+        case 8: return (const void *)k_stack_fused<T, 8>;
+        case 16: return (const void *)k_stack_fused<T, 16>;
+        case 32: return (const void *)k_stack_fused<T, 32>;
+        default: return nullptr;
+    }
+}
+
+template <class T>
+hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int64_t ldb_units,
+                          int32_t units, int accumulate, hipStream_t s) {
+    const void *kern = pick_fused<T>(p.rows_per_wave);
+    // the kernel's row ownership must match the plan the workspace was
+    // sized for: 16 waves x R rows x groups cover d exactly
+    if (kern == nullptr || (int64_t)kWaves * p.rows_per_wave * p.groups != fa.d ||
+        fa.groups != p.groups || fa.zeta > kFusedMaxZeta || fa.ws == nullptr)
+        return hipErrorInvalidValue;
+    FusedArgs a = fa;
+    void *params[] = {&a};
+    hipError_t e = hipLaunchKernel(kern, dim3((unsigned)p.grid), dim3(kWaves * 64), params, 0, s);
+    if (e != hipSuccess) return e;
+    StackApplyArgs r{};
+    r.B = B;
+    r.ws = fa.ws;
+    r.ldb = ldb_units;
+    r.units = units;
+    r.d = fa.d;
+    r.chunks = fa.chunks;
+    r.slices = fa.slices;
+    const int64_t total = (int64_t)fa.d * units;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65535) blocks = 65535;
+    k_stack_reduce<T><<<dim3((unsigned)blocks), 256, 0, s>>>(r, 128, accumulate);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Plan of the fused kernel.  Rows per wave R = d / (16 G) for the fewest
+// row groups G with R <= 32 (two words x R rows of registers per lane) and
+// R dividing d/zeta (a wave's rows inside one block); R must be one of the
+// built 4, 8, 16, 32.  Chunks are sized so one workgroup per CU fills the
+// device, in whole stages.  Narrow matrices (under half a slice of columns)
+// are left to the metadata + LDS apply path, which packs them better.
+bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
+                bool a_aligned, int32_t d, int32_t zeta, FusedPlan *p) {
+    const int K = f16 ? 4 : 2;
+    if (m < 1 || zeta > kFusedMaxZeta || n % K != 0 || lda % K != 0 || !a_aligned) return false;
+    if (n < 32 * K || d % kWaves != 0) return false;
+    if (di.max_lds < kFusedLdsBytes) return false;
+    const int64_t db = d / zeta;
+    int R = 0, G = 0;
+    for (int g = 1; (int64_t)kWaves * g <= d; g *= 2) {
+        if (d % (kWaves * g) != 0) break;
+        const int64_t r = d / (kWaves * g);
+        if (r > 32) continue;
+        if (r != 4 && r != 8 && r != 16 && r != 32) break;
+        if (db % r == 0) {
+            R = (int)r;
+            G = g;
+            break;
+        }
+    }
+    if (R == 0) return false;
+    p->rows_per_wave = R;
+    p->groups = G;
+    p->slices = (n + 64 * K - 1) / (64 * K);
+    const int64_t per_chunk = p->slices * G;
+    int64_t want = (di.num_cu + per_chunk - 1) / per_chunk;
+    const int64_t stages = (m + kStage - 1) / kStage;
+    if (want > stages) want = stages;
+    if (want > 65535) want = 65535;
+    if (want < 1) want = 1;
+    const int64_t st_per_chunk = (stages + want - 1) / want;
+    p->rows_per_chunk = st_per_chunk * kStage;
+    p->chunks = (m + p->rows_per_chunk - 1) / p->rows_per_chunk;
+    p->grid = (p->slices * p->chunks + 7) / 8 * 8 * G;
+    p->ws_bytes = (size_t)p->slices * (size_t)p->chunks * (size_t)d * 128 * 4;
+    return true;
+}
+
+hipError_t launch_fused(const FusedPlan &p, bool f16, const float *A, int64_t m, int32_t n,
+                        int64_t lda, uint64_t seed, int64_t row_offset, int32_t d, int32_t zeta,
+                        float scale, void *B, int64_t ldb, uint32_t *ws, int accumulate,
+                        hipStream_t s) {
+    FusedArgs a{};
+    a.A = A;
+    a.ws = ws;
+    a.m = m;
+    a.lda = lda;
+    a.rows_per_chunk = p.rows_per_chunk;
+    a.row_offset = row_offset;
+    a.seed = seed;
+    a.n = n;
+    a.d = d;
+    a.zeta = zeta;
+    a.chunks = (int32_t)p.chunks;
+    a.slices = (int32_t)p.slices;
+    a.groups = p.groups;
+    a.scale = scale;
+    if (f16) return launch_fused_t<AccF16>(p, a, B, ldb / 2, n / 2, accumulate, s);
+    return launch_fused_t<AccF32>(p, a, B, ldb, n, accumulate, s);
+}
+
+}  // namespace sk

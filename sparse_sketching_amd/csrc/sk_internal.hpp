@@ -62,6 +62,40 @@ hipError_t launch_f16_lds(const LdsPlan &plan, const float *A, int64_t m, int32_
                           int32_t d, int64_t ldb, uint32_t *ws, int accumulate,
                           hipStream_t stream);
 
+// Fused SparseStack sketch (metadata drawn in the apply kernel, fused.hip).
+constexpr int kFusedMaxZeta = 16;
+// static LDS of the fused kernel: two 128-row stages of 64 lanes x 8 bytes
+// and two metadata stages of kFusedMaxZeta x 128 entries
+constexpr int kFusedLdsBytes = 2 * 128 * 64 * 8 + 2 * kFusedMaxZeta * 128 * 4;
+struct FusedArgs {
+    const float *A;
+    uint32_t *ws;               // [slices][chunks][d][128] partial words
+    int64_t m, lda, rows_per_chunk, row_offset;
+    uint64_t seed;
+    int32_t n, d, zeta;
+    int32_t chunks, slices, groups;
+    float scale;                // float32(1/sqrt(zeta))
+};
+struct FusedPlan {
+    int rows_per_wave;          // R: output rows kept in one wavefront's registers
+    int groups;                 // G: output row groups (each reads A once)
+    int64_t slices;             // column slices (256 FP16 / 128 FP32 columns)
+    int64_t rows_per_chunk;     // input rows per workgroup (whole 128-row stages)
+    int64_t chunks;
+    int64_t grid;               // workgroups (1-D, XCD-grouped)
+    size_t ws_bytes;            // partial workspace
+};
+// a_aligned: A's base allows the kernel's lane loads (16 bytes for FP16,
+// 8 for FP32).  False: the fused kernel does not cover this call.
+bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
+                bool a_aligned, int32_t d, int32_t zeta, FusedPlan *plan);
+// Fused kernel into ws, then the chunk-order reduce into B (=, or += when
+// accumulate).  B is float* (FP32) or FP16 bits (uint16_t*), ldb in elements.
+hipError_t launch_fused(const FusedPlan &plan, bool f16, const float *A, int64_t m, int32_t n,
+                        int64_t lda, uint64_t seed, int64_t row_offset, int32_t d, int32_t zeta,
+                        float scale, void *B, int64_t ldb, uint32_t *ws, int accumulate,
+                        hipStream_t stream);
+
 constexpr int kBlockPermMaxM = 1024;
 struct BlockPermArgs {
     const float *A;

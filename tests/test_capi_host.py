@@ -19,7 +19,8 @@ def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
     assert set(names) == {"sk_meta_generate", "sk_apply_f32", "sk_apply_f16acc",
                           "sk_apply_workspace_size", "sk_lds_plan_describe",
-                          "sk_apply_blockperm", "sk_status_string"}
+                          "sk_sketch_f32", "sk_sketch_f16acc", "sk_sketch_workspace_size",
+                          "sk_fused_plan_describe", "sk_apply_blockperm", "sk_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -204,3 +205,132 @@ def test_plan_describe_validation(lib):
     assert lib.sk_lds_plan_describe(1, 10, 7, 8, 8, 1, 1, 256, 163840, out) == b.SK_ERR_SHAPE
     assert lib.sk_lds_plan_describe(0, 10, 8, 8, 8, 1, 1, 0, 163840, out) == b.SK_ERR_ARG
     assert lib.sk_lds_plan_describe(0, 10, 8, 8, 8, 1, 1, 256, 163840, None) == b.SK_ERR_NULL
+
+
+# ------------------------------------------------------ fused sketch calls
+
+WSF = FAKE + (1 << 38)
+
+
+@pytest.mark.parametrize("fn", ["sk_sketch_f32", "sk_sketch_f16acc"])
+@pytest.mark.parametrize("args,expect", [
+    ((1, 0, A, 100, 0, 64, 64, 4, B, 64, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),     # n < 1
+    ((1, -1, A, 100, 64, 64, 64, 4, B, 64, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),   # row_offset < 0
+    ((1, 0, A, -1, 64, 64, 64, 4, B, 64, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),     # m < 0
+    ((1, 0, A, 100, 64, 32, 64, 4, B, 64, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),    # lda < n
+    ((1, 0, A, 100, 64, 64, 64, 3, B, 64, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),    # d % zeta
+    ((1, 0, A, 100, 64, 64, 64, 4, B, 32, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),    # ldb < n
+    ((1, 0, A, 100, 64, 64, 64, 4, B, 64, 2, WSF, 1 << 30), b.SK_ERR_ARG),      # variant flag
+    ((1, 0, A, 100, 64, 64, 64, 4, None, 64, 0, WSF, 1 << 30), b.SK_ERR_NULL),
+    ((1, 0, None, 100, 64, 64, 64, 4, B, 64, 0, WSF, 1 << 30), b.SK_ERR_NULL),
+    ((1, 0, A, 100, 64, 64, 64, 4, B, 64, 0, None, 0), b.SK_ERR_NULL),          # no workspace
+    ((1, 0, A, 100, 64, 64, 64, 4, B, 64, 0, WSF + 4, 1 << 30), b.SK_ERR_ALIGN),  # 16-byte rule
+    ((1, 0, A, 100, 64, 64, 64, 4, A + 64, 64, 0, WSF, 1 << 30), b.SK_ERR_ARG),   # B inside A
+    ((1, 0, A, 100, 64, 64, 64, 4, B, 64, 0, A + 16, 1 << 20), b.SK_ERR_ARG),     # ws overlaps A
+    ((1, 0, A, 100, 64, 64, 64, 4, B, 64, 0, B - 64, 1 << 20), b.SK_ERR_ARG),     # ws overlaps B
+])
+def test_sketch_validation(lib, fn, args, expect):
+    assert getattr(lib, fn)(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((1, 0, A, 100, 63, 64, 64, 4, B, 64, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),    # odd n
+    ((1, 0, A, 100, 64, 64, 64, 4, B, 63, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),    # ldb < n (odd)
+    ((1, 0, A, 100, 64, 64, 64, 4, B, 65, 0, WSF, 1 << 30), b.SK_ERR_ALIGN),    # odd ldb
+    ((1, 0, A, 100, 64, 64, 64, 4, B + 2, 64, 0, WSF, 1 << 30), b.SK_ERR_ALIGN),  # B % 4
+    ((1, 0, A, 100, 64, 65, 64, 4, B, 64, 0, WSF, 1 << 30), b.SK_ERR_ALIGN),    # odd lda
+    ((1, 0, A + 4, 100, 64, 64, 64, 4, B, 64, 0, WSF, 1 << 30), b.SK_ERR_ALIGN),  # A % 8
+])
+def test_sketch_f16acc_pair_rules(lib, args, expect):
+    assert lib.sk_sketch_f16acc(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((2, 100, 64, 64, 4), b.SK_ERR_ARG),        # unknown precision
+    ((0, 100, 0, 64, 4), b.SK_ERR_SHAPE),       # n < 1
+    ((1, 100, 63, 64, 4), b.SK_ERR_SHAPE),      # odd n for FP16
+    ((0, 100, 64, 64, 3), b.SK_ERR_SHAPE),      # d % zeta
+    ((0, -1, 64, 64, 4), b.SK_ERR_SHAPE),
+])
+def test_sketch_workspace_size_validation(lib, args, expect):
+    out = ctypes.c_size_t(123)
+    assert lib.sk_sketch_workspace_size(*args, ctypes.byref(out)) == expect
+    assert out.value == 0
+    assert lib.sk_sketch_workspace_size(0, 100, 64, 64, 4, None) == b.SK_ERR_NULL
+
+
+FUSED_SHAPES = PLAN_SHAPES + [
+    (1 << 20, 256, 1024, 4), (1 << 20, 256, 256, 16), (1 << 20, 512, 512, 1), (130, 128, 512, 4),
+    (1, 128, 64, 4), (129, 256, 2048, 2), (1 << 21, 512, 1024, 4), (10_000, 384, 96, 3),
+    (5000, 256, 512, 32), (5000, 256, 64, 16),
+]
+
+
+@pytest.mark.parametrize("precision", [b.SK_PRECISION_F32, b.SK_PRECISION_F16ACC])
+@pytest.mark.parametrize("m,n,d,zeta", FUSED_SHAPES)
+def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
+    """Replays the fused kernel's workgroup and wavefront mapping on its
+    plan: every (slice, chunk, row group) is covered once, 16 wavefronts x R
+    rows x groups tile the d output rows exactly, each wavefront's R rows
+    lie inside one stack block (the block whose metadata it scans), chunks
+    are whole 128-row stages covering the m rows, the lanes' column loads
+    stay inside the row, and every partial store stays inside the
+    workspace."""
+    f16 = precision == b.SK_PRECISION_F16ACC
+    if f16 and n % 2:
+        pytest.skip("odd n")
+    K = 4 if f16 else 2
+    p = b.sk_fused_plan_describe(precision, m, n, n, True, d, zeta, **MI355X)
+    if not p["fused"]:
+        assert (zeta > 16 or n % K or n < 32 * K or d % 16
+                or all((d // (16 * g)) not in (4, 8, 16, 32) or (d // zeta) % (d // (16 * g))
+                       for g in (1, 2, 4, 8, 16, 32) if d % (16 * g) == 0))
+        return
+    R, g = p["rows_per_wave"], p["groups"]
+    assert R in (4, 8, 16, 32) and 16 * R * g == d
+    db = d // zeta
+    assert db % R == 0
+    assert p["rows_per_chunk"] % 128 == 0
+    assert p["chunks"] * p["rows_per_chunk"] >= m > (p["chunks"] - 1) * p["rows_per_chunk"]
+    assert p["slices"] * 64 * K >= n > (p["slices"] - 1) * 64 * K
+    for lane in (0, 63):
+        for sl in range(p["slices"]):
+            col = sl * 64 * K + lane * K
+            assert 0 <= min(col, n - K) and min(col, n - K) + K <= n
+    seen = set()
+    for wg in range(p["grid"]):
+        q = wg >> 3
+        grp, uid = q % g, (q // g) * 8 + (wg & 7)
+        if uid >= p["slices"] * p["chunks"]:
+            continue
+        sl, ch = uid % p["slices"], uid // p["slices"]
+        assert (sl, ch, grp) not in seen
+        seen.add((sl, ch, grp))
+        for wave in (0, 15):
+            lo = (grp * 16 + wave) * R
+            t = lo // db
+            assert t < zeta and t * db <= lo and lo + R <= (t + 1) * db
+            last = ((sl * p["chunks"] + ch) * d + lo + R - 1) * 128 + 63 * 2 + 1
+            assert (last + 1) * 4 <= p["ws_bytes"]
+    assert len(seen) == p["slices"] * p["chunks"] * g
+    # the fused kernel's metadata stage holds at most 16 blocks
+    assert zeta <= 16
+
+
+def test_fused_plan_alignment_and_validation(lib):
+    P16, P32 = b.SK_PRECISION_F16ACC, b.SK_PRECISION_F32
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, True, 512, 4, **MI355X)["fused"] == 1
+    # misaligned base, odd-multiple lda, narrow rows: left to the fallback
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, False, 512, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 258, True, 512, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 256, 257, True, 512, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 64, 64, True, 128, 4, **MI355X)["fused"] == 0
+    # LDS smaller than the kernel's stages
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, True, 512, 4, num_cu=256,
+                                    max_lds=64 * 1024)["fused"] == 0
+    out = (ctypes.c_int64 * len(b.FUSED_PLAN_FIELDS))()
+    assert lib.sk_fused_plan_describe(0, 10, 0, 8, 1, 8, 1, 256, 163840, out) == b.SK_ERR_SHAPE
+    assert lib.sk_fused_plan_describe(3, 10, 8, 8, 1, 8, 1, 256, 163840, out) == b.SK_ERR_ARG
+    assert lib.sk_fused_plan_describe(1, 10, 7, 8, 1, 8, 1, 256, 163840, out) == b.SK_ERR_SHAPE
+    assert lib.sk_fused_plan_describe(0, 10, 8, 8, 1, 8, 1, 0, 163840, out) == b.SK_ERR_ARG
+    assert lib.sk_fused_plan_describe(0, 10, 8, 8, 1, 8, 1, 256, 163840, None) == b.SK_ERR_NULL

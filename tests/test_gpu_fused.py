@@ -1,0 +1,222 @@
+"""GPU parity of the fused SparseStack sketch (sk_sketch_f32 /
+sk_sketch_f16acc: metadata drawn inside the apply kernel) against the CPU
+oracle, whose metadata comes from its own Philox (FP16 sketching page
+§III-C; FlashSketch page §5.2).
+
+Bars as for the stored-metadata apply: exact inputs bit for bit, FP32
+within relative Frobenius 1e-5 of fp64, FP16 within 4e-3 (or the error
+model's bar for degenerate shapes).  Shapes cover the fused kernel's own
+plans (each rows-per-wave size, row groups, several slices, ragged chunks,
+row offsets) and the shapes it hands to the metadata + LDS fallback."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_sketching_amd import binding as b
+from sparse_sketching_amd import inputs
+from tests.gpuutil import dev, say, sync, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MI355X = dict(num_cu=256, max_lds=160 * 1024)
+PREC = {"f32": b.SK_PRECISION_F32, "f16acc": b.SK_PRECISION_F16ACC}
+
+
+def fused_used(precision, m, n, lda, d, zeta):
+    return b.sk_fused_plan_describe(PREC[precision], m, n, lda, True, d, zeta, **MI355X)["fused"]
+
+
+def run_fused(A, d, zeta, seed, precision, row_offset=0, out=None, flags=0):
+    Ad = A if isinstance(A, torch.Tensor) else to_dev(A)
+    B = b.sketch_fused(Ad, d, zeta, seed, precision, row_offset=row_offset, out=out, flags=flags)
+    sync()
+    return B.cpu().numpy().astype(np.float64)
+
+
+# (m, n, d, zeta): rows per wave 4, 8, 16, 32; row groups 1 and 2; one and
+# several column slices; ragged row counts and single partial stages
+FUSED_SHAPES = [
+    (4096, 128, 64, 4),         # R = 4
+    (4096, 128, 64, 1),         # CountSketch
+    (3001, 256, 128, 4),        # R = 8, ragged last stage
+    (1000, 128, 256, 16),       # R = 16, zeta = 16 (four Philox blocks per row)
+    (2500, 384, 512, 4),        # R = 32, two FP16 / three FP32 slices, ragged slice
+    (5000, 128, 1024, 4),       # two row groups
+    (129, 256, 512, 1),         # one stage plus one row
+    (1, 128, 64, 4),            # a single row
+]
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16acc"])
+@pytest.mark.parametrize("m,n,d,zeta", FUSED_SHAPES)
+def test_fused_exact_inputs_bit_exact(precision, m, n, d, zeta):
+    """Integer inputs: every partial sum is exact (FP32 |A| <= 8; FP16
+    {-1,0,1} with sums far below 2^11), so the fused sketch must equal the
+    fp64 oracle bit for bit: a wrong hash, sign, lost or doubled hit changes
+    it."""
+    say(f"fused exact {precision} m={m} n={n} d={d} zeta={zeta}")
+    assert fused_used(precision, m, n, n, d, zeta)
+    lo, hi = (-8, 8) if precision == "f32" else (-1, 1)
+    A = inputs.integer_matrix(m, n, lo, hi, seed=21)
+    B = run_fused(A, d, zeta, 17, precision)
+    ri, v = oracle.meta_ref(17, m, d, zeta)
+    ref = oracle.sketch_f64(A, ri, v, d, zeta)
+    if precision == "f16acc":
+        assert np.abs(ref).max() < 1024
+    assert np.array_equal(B, ref)
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16acc"])
+@pytest.mark.parametrize("zeta", [2, 8])
+def test_fused_inexact_scales(precision, zeta):
+    """zeta = 2, 8: the scale 1/sqrt(zeta) is not a power of two, so the
+    products round; tolerance bars against fp64."""
+    m, n, d = 20000, 128, 256
+    A = inputs.gaussian(m, n, seed=6)
+    assert fused_used(precision, m, n, n, d, zeta)
+    B = run_fused(A, d, zeta, 3, precision)
+    ri, v = oracle.meta_ref(3, m, d, zeta)
+    tol = 1e-5 if precision == "f32" else 4e-3
+    assert oracle.rel_frob(B, oracle.sketch_f64(A, ri, v, d, zeta)) <= tol
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16acc"])
+def test_fused_general_values_and_padding(precision):
+    """N(0,1) input with padded strides (lda > n, ldb > n): tolerance bars,
+    and B's padding columns are left untouched."""
+    m, n, d, zeta, pad = 7000, 256, 512, 4, 8
+    A = inputs.gaussian(m, n + pad, seed=4)
+    Ad = to_dev(A)[:, :n]
+    assert fused_used(precision, m, n, n + pad, d, zeta)
+    dt = torch.float16 if precision == "f16acc" else torch.float32
+    out = torch.full((d, n + pad), 7.0, dtype=dt, device=dev())
+    b.sketch_fused(Ad, d, zeta, 5, precision, out=out[:, :n])
+    sync()
+    B = out.cpu().numpy().astype(np.float64)
+    assert np.all(B[:, n:] == 7.0)
+    ri, v = oracle.meta_ref(5, m, d, zeta)
+    ref = oracle.sketch_f64(np.ascontiguousarray(A[:, :n]), ri, v, d, zeta)
+    tol = 1e-5 if precision == "f32" else 4e-3
+    assert oracle.rel_frob(B[:, :n], ref) <= tol
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16acc"])
+def test_fused_row_offset_chunks_accumulate(precision):
+    """Row chunks sketched with their global row offsets and SK_ACCUMULATE
+    give the sketch of the whole matrix (exact inputs)."""
+    m, n, d, zeta = 9000, 128, 256, 4
+    A = inputs.integer_matrix(m, n, -1, 1, seed=9)
+    Ad = to_dev(A)
+    dt = torch.float16 if precision == "f16acc" else torch.float32
+    out = torch.zeros((d, n), dtype=dt, device=dev())
+    for r0, r1 in [(0, 2500), (2500, 2501), (2501, 9000)]:
+        b.sketch_fused(Ad[r0:r1], d, zeta, 12, precision, row_offset=r0, out=out,
+                       flags=b.SK_ACCUMULATE)
+    sync()
+    ri, v = oracle.meta_ref(12, m, d, zeta)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), oracle.sketch_f64(A, ri, v, d, zeta))
+
+
+def test_fused_large_row_offset():
+    """Global rows past 2^32 use both counter words of the Philox block."""
+    m, n, d, zeta, off = 3000, 128, 64, 4, (1 << 32) + 12345
+    A = inputs.integer_matrix(m, n, -4, 4, seed=2)
+    B = run_fused(A, d, zeta, 99, "f32", row_offset=off)
+    ri, v = oracle.meta_ref(99, m, d, zeta, row_offset=off)
+    assert np.array_equal(B, oracle.sketch_f64(A, ri, v, d, zeta))
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16acc"])
+@pytest.mark.parametrize("m,n,d,zeta,lda", [
+    (4096, 32, 64, 4, 32),      # narrow rows
+    (2048, 128, 128, 64, 128),  # zeta above the fused metadata stage
+    (3001, 128, 40, 4, 128),    # d not a multiple of 16
+    (2048, 128, 64, 4, 130),    # rows not 16-byte aligned (FP16) / fine for FP32
+    (5, 2, 16, 16, 2),          # tiny, zeta = d
+])
+def test_fused_fallback_shapes(precision, m, n, d, zeta, lda):
+    """Shapes the fused kernel does not cover run metadata + LDS apply from
+    the same call and give the same sketch (scales 1/sqrt(zeta) that are
+    powers of two and {-1,0,1} inputs keep every sum exact)."""
+    say(f"fused fallback {precision} m={m} n={n} d={d} zeta={zeta} lda={lda}")
+    A = inputs.integer_matrix(m, lda, -1, 1, seed=3)
+    Ad = to_dev(A)[:, :n]
+    B = run_fused(Ad, d, zeta, 8, precision)
+    ri, v = oracle.meta_ref(8, m, d, zeta)
+    ref = oracle.sketch_f64(np.ascontiguousarray(A[:, :n]), ri, v, d, zeta)
+    assert np.array_equal(B, ref)
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16acc"])
+def test_fused_empty_input(precision):
+    d, n = 64, 128
+    dt = torch.float16 if precision == "f16acc" else torch.float32
+    out = torch.full((d, n), 3.0, dtype=dt, device=dev())
+    A = torch.empty((0, n), dtype=torch.float32, device=dev())
+    b.sketch_fused(A, d, 4, 1, precision, out=out, flags=b.SK_ACCUMULATE)
+    sync()
+    assert torch.all(out == 3.0)
+    b.sketch_fused(A, d, 4, 1, precision, out=out)
+    sync()
+    assert torch.all(out == 0.0)
+
+
+def test_fused_workspace_too_small_is_refused():
+    m, n, d, zeta = 4096, 256, 512, 4
+    Ad = to_dev(inputs.gaussian(m, n))
+    need = b.sk_sketch_workspace_size(b.SK_PRECISION_F16ACC, m, n, d, zeta)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=dev())
+    with pytest.raises(b.SketchError):
+        b.sketch_fused(Ad, d, zeta, 1, "f16acc", ws=ws)
+
+
+def test_fused_equals_meta_plus_apply_f32_exact():
+    """Same seed: the fused call and sk_meta_generate + sk_apply_f32 give the
+    same sketch (exact inputs, so the order of additions cannot matter)."""
+    m, n, d, zeta = 20000, 256, 512, 4
+    A = inputs.integer_matrix(m, n, -8, 8, seed=31)
+    Ad = to_dev(A)
+    Bf = b.sketch_fused(Ad, d, zeta, 77, "f32")
+    Bm = b.sketch(Ad, d, zeta, 77, "f32")
+    sync()
+    assert torch.equal(Bf, Bm)
+
+
+# ------------------------------------------------- scale configuration (C2)
+
+@pytest.fixture(scope="module")
+def scale_case():
+    """A 2^20 x 256 N(0,1) drawn on the device (seeded); zeta = 4, d = 512."""
+    m, n, d, zeta, seed = 1 << 20, 256, 512, 4, 1
+    say("fused scale case: drawing A and the fp64 oracle sketch")
+    Ad = inputs.gaussian_torch(m, n, seed=0)
+    A = Ad.cpu().numpy()
+    ri, v = oracle.meta_ref(seed, m, d, zeta)
+    return Ad, A, d, zeta, seed, oracle.sketch_f64(A, ri, v, d, zeta)
+
+
+@pytest.mark.parametrize("precision,tol", [("f32", 1e-5), ("f16acc", 4e-3)])
+def test_fused_scale(scale_case, precision, tol):
+    """The bench's configuration, in the launch configuration bench.py times."""
+    Ad, A, d, zeta, seed, ref = scale_case
+    assert fused_used(precision, *Ad.shape, Ad.shape[1], d, zeta)
+    B = run_fused(Ad, d, zeta, seed, precision)
+    err = oracle.rel_frob(B, ref)
+    say(f"  fused scale {precision} rel err {err:.3e}")
+    assert err <= tol
+
+
+def test_fused_scale_sampled_rows_exact(scale_case):
+    """At full size, sampled output rows recomputed one by one: with the
+    input rounded to multiples of 1/4 in [-4, 4] every FP32 partial sum is
+    exact, so each sampled row must match the oracle's bit for bit."""
+    Ad, A, d, zeta, seed, _ = scale_case
+    Aq = torch.clamp(torch.round(Ad * 4) / 4, -4, 4)
+    B = run_fused(Aq, d, zeta, seed + 1, "f32")
+    Aq_h = Aq.cpu().numpy().astype(np.float64)
+    ri, v = oracle.meta_ref(seed + 1, Aq_h.shape[0], d, zeta)
+    for r in (0, 1, 127, 128, 255, 300, 511):
+        hit = np.nonzero(ri == r)[0]
+        row = (v[hit].astype(np.float64)[:, None] * Aq_h[hit // zeta]).sum(axis=0)
+        assert np.array_equal(B[r], row), r
