@@ -38,6 +38,13 @@ HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, published
 M_ROWS, N_COLS, D_ROWS, ZETA = 1 << 20, 256, 512, 4
 BP_M, BP_N, BP_D, BP_BLOCKS, BP_KAPPA = 1 << 21, 512, 1024, 64, 4
 SEED = 1
+# HBM bytes one complete fused FP16 step moves, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE passes over bench.py --profile-pass (KiB per
+# dispatch; FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a 1 GiB device
+# copy reads on the same counters).  Valid for the kernels named here only.
+TRAFFIC = {"kernels": ("k_stack_fused<AccF16,32,1>", "k_stack_reduce<AccF16>"),
+           "fetch_kib": (524_567, 32_801), "write_kib": (65_536, 256),
+           "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def sparsestack_bytes(m, n, d, zeta, out_elem):
@@ -52,6 +59,13 @@ def fused_bytes(m, n, d, out_elem):
 
 def blockperm_bytes(m, n, d):
     return 4 * m * n + 4 * d * n
+
+
+def traffic_bytes():
+    """HBM bytes per complete fused step measured by the PMC counters."""
+    t = TRAFFIC
+    kib = t["fetch_scale"] * sum(t["fetch_kib"]) + t["write_scale"] * sum(t["write_kib"])
+    return int(kib * 1024)
 
 
 def timed(fn, steps, warmup, stream):
@@ -260,8 +274,8 @@ def main():
         "blockperm": bp,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": "k_stack_fused<AccF16,32> + k_stack_reduce<AccF16>",
+                     "traffic": traffic_bytes(),
+                     "kernel": "k_stack_fused<AccF16,32,1> + k_stack_reduce<AccF16>",
                      "kernel_ms": round(ms16, 5), "algorithmic_bytes": fbytes16,
                      "apply_atomic_flush_ms": round(ms_kernel_atomic, 5)},
         "cpu_baseline": None,

@@ -51,7 +51,38 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <class T, int R>
+// K floats at global address base + off (base wave-uniform, off per lane),
+// loaded through the global address space so the load takes its
+// scalar-base form.  (The host pass of the compiler only parses kernel
+// bodies; it sees a plain load.)
+template <int K>
+__device__ __forceinline__ FVec<K> load_row(uint64_t base, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(1))) const char gchar;
+    gchar *p = reinterpret_cast<gchar *>(base) + off;
+    typedef __attribute__((address_space(1))) const float2 gfloat2;
+    typedef __attribute__((address_space(1))) const float4 gfloat4;
+#else
+    const char *p = reinterpret_cast<const char *>(base) + off;
+    typedef const float2 gfloat2;
+    typedef const float4 gfloat4;
+#endif
+    FVec<K> r;
+    if constexpr (K == 2) {
+        const float2 v = *reinterpret_cast<gfloat2 *>(p);
+        r.x[0] = v.x;
+        r.x[1] = v.y;
+    } else {
+        const float4 v = *reinterpret_cast<gfloat4 *>(p);
+        r.x[0] = v.x;
+        r.x[1] = v.y;
+        r.x[2] = v.z;
+        r.x[3] = v.w;
+    }
+    return r;
+}
+
+template <class T, int R, int P>
 __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs args) {
     constexpr int K = 2 * T::kCols;     // floats of A per lane per row
     typedef FVec<K> vec_t;
@@ -80,70 +111,84 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
     const int32_t t = lo / (int32_t)db;                  // its stack block
     const uint32_t lob = (uint32_t)(lo - t * (int32_t)db);
     const int64_t r0 = (int64_t)chunk * args.rows_per_chunk;
-    const int64_t r1 = r0 + args.rows_per_chunk < args.m ? r0 + args.rows_per_chunk : args.m;
-    const int32_t nst = (int32_t)((r1 - r0 + S - 1) / S);
+    // rows of this chunk (the plan keeps chunks below 2^30 rows)
+    const int32_t nrows = (int32_t)((r0 + args.rows_per_chunk < args.m ? args.rows_per_chunk
+                                                                        : args.m - r0));
+    const int32_t nst = (nrows + S - 1) / S;
     const int64_t lda = args.lda;
     // the lane's K columns, clamped into the row (lanes past the last column
     // load valid memory; their partial words are never reduced)
     const int32_t col = slice * 64 * K + lane * K;
     const int32_t col_c = col <= args.n - K ? col : args.n - K;
-    const float *__restrict__ A = args.A + col_c;
+    const uint32_t lane_off = (uint32_t)col_c * 4u;        // bytes into a row
+    const char *__restrict__ A = reinterpret_cast<const char *>(args.A);
     const float c = args.scale;
 
     uint32_t acc[R][2];
 #pragma unroll
     for (int k = 0; k < R; ++k) acc[k][0] = acc[k][1] = 0u;
 
-    // rows of stage s owned by this wave, clamped into the chunk
-    vec_t a[D];
-    auto load = [&](int32_t s) {
-        const int64_t base = r0 + (int64_t)s * S + wave * D;
+    // rows [u0, u1) of this wave's share of stage s, clamped into the chunk
+    vec_t a[P][D];
+    // (a row's address is wave-uniform: a scalar base plus the lane's
+    // 32-bit offset, so the loads take the scalar-base form)
+    auto load = [&](int32_t s, vec_t (&av)[D], int u0, int u1) {
+        const int32_t base = s * S + wave * D;
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int64_t row = base + u < r1 ? base + u : r1 - 1;
-            a[u] = load_vec<K>(reinterpret_cast<const char *>(A + row * lda));
+        for (int u = u0; u < u1; ++u) {
+            const int32_t rel = base + u < nrows ? base + u : nrows - 1;
+            const uint64_t rp = (uint64_t)(A + (r0 + rel) * lda * 4);
+            const uint64_t rpu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(rp >> 32)) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)rp);
+            av[u] = load_row<K>(rpu, lane_off);
         }
     };
-    // contributions of the loaded rows into stage buffer hs; metadata of
-    // stage s into me (one wave per stage, rotating)
-    auto stage = [&](int32_t s, uint2 *hs, uint32_t *me) {
+    // contributions of loaded rows [u0, u1) into stage buffer hs
+    auto stage = [&](const vec_t (&av)[D], uint2 *hs, int u0, int u1) {
 #pragma unroll
-        for (int u = 0; u < D; ++u)
+        for (int u = u0; u < u1; ++u)
             hs[(wave * D + u) * 64 + lane] =
-                make_uint2(T::contrib(a[u].x, c), T::contrib(a[u].x + T::kCols, c));
-        if (wave == (s & (kWaves - 1))) {
-            const uint32_t k0 = (uint32_t)args.seed, k1 = (uint32_t)(args.seed >> 32);
+                make_uint2(T::contrib(av[u].x, c), T::contrib(av[u].x + T::kCols, c));
+    };
+    // the metadata of stage s into me: one wave per stage (rotating) draws
+    // the Philox blocks of the stage's rows, one row per lane
+    auto draw = [&](int32_t s, uint32_t *me) {
+        if (wave != (s & (kWaves - 1))) return;
+        const uint32_t k0 = (uint32_t)args.seed, k1 = (uint32_t)(args.seed >> 32);
+        // one lane group at a time keeps the Philox temporaries few
+#pragma unroll 1
+        for (int h = 0; h < NL; ++h) {
+            const uint64_t g = (uint64_t)args.row_offset +
+                               (uint64_t)(r0 + (int64_t)s * S + h * 64 + lane);
+            for (int gq = 0; gq * 4 < zeta; ++gq) {
+                const u32x4 w4 = philox4x32_10(
+                    u32x4{(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)gq, 0u}, k0, k1);
+                const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-            for (int h = 0; h < NL; ++h) {
-                const uint64_t g = (uint64_t)args.row_offset +
-                                   (uint64_t)(r0 + (int64_t)s * S + h * 64 + lane);
-                for (int gq = 0; gq * 4 < zeta; ++gq) {
-                    const u32x4 w4 = philox4x32_10(
-                        u32x4{(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)gq, 0u}, k0, k1);
-                    const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (gq * 4 + j < zeta)
-                            me[(gq * 4 + j) * S + h * 64 + lane] =
-                                mulhi32(ww[j], db) | (ww[j] << 31);
-                }
+                for (int j = 0; j < 4; ++j)
+                    if (gq * 4 + j < zeta)
+                        me[(gq * 4 + j) * S + h * 64 + lane] = mulhi32(ww[j], db) | (ww[j] << 31);
             }
         }
     };
-    // every hit of stage s on this wave's rows
-    auto process = [&](int32_t s, const uint2 *hs, const uint32_t *me) {
-        int32_t rl[NL];
-        uint32_t sg[NL];
+    // this wave's entries of stage s: output row inside its range (-1:
+    // none) and sign, lane j <-> stage row h*64 + j
+    int32_t rl[NL];
+    uint32_t sg[NL];
+    auto scan = [&](int32_t s, const uint32_t *me) {
 #pragma unroll
         for (int h = 0; h < NL; ++h) {
             const uint32_t e = me[t * S + h * 64 + lane];
-            const int64_t row = r0 + (int64_t)s * S + h * 64 + lane;
+            const int32_t rel = s * S + h * 64 + lane;
             const uint32_t rk = (e & 0x7FFFFFFFu) - lob;
-            rl[h] = row < r1 && rk < (uint32_t)R ? (int32_t)rk : -1;
+            rl[h] = rel < nrows && rk < (uint32_t)R ? (int32_t)rk : -1;
             sg[h] = e & 0x80000000u;
         }
+    };
+    // every hit of the scanned stage on this wave's rows [k0, k1)
+    auto process = [&](const uint2 *hs, int k0, int k1) {
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
+        for (int k = k0; k < k1; ++k) {
 #pragma unroll
             for (int h = 0; h < NL; ++h) {
                 uint64_t mk = __ballot(rl[h] == k);
@@ -159,20 +204,32 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
         }
     };
 
-    // stage 0 staged and stage 1 loading, then per stage: apply it, stage
-    // the next one into the other buffer, start loading the one after
-    load(0);
-    stage(0, hs0, me0);
-    load(1);
+    // stage 0 staged and stages 1..P loading; then per stage s: apply s,
+    // stage s+1 into the other buffer from the register set it was loaded
+    // into, draw the metadata of s+1, and reload the set with stage s+1+P.
+    // With P = 1 this is done in two halves (rows and output rows split at
+    // the middle), so the next loads start half a stage earlier.
+    constexpr int NH = (P == 1 && R < 32) ? 2 : 1;
+    load(0, a[0], 0, D);
+    stage(a[0], hs0, 0, D);
+    draw(0, me0);
+#pragma unroll
+    for (int p = 1; p <= P; ++p) load(p, a[p % P], 0, D);
     __syncthreads();
     for (int32_t s0 = 0; s0 < nst; s0 += 2) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int32_t s = s0 + b;
             if (s < nst) {
-                process(s, b ? hs1 : hs0, b ? me1 : me0);
-                stage(s + 1, b ? hs0 : hs1, b ? me0 : me1);
-                load(s + 2);
+                scan(s, b ? me1 : me0);
+#pragma unroll
+                for (int j = 0; j < NH; ++j) {
+                    process(b ? hs1 : hs0, j * R / NH, (j + 1) * R / NH);
+                    stage(a[(b + 1) % P], b ? hs0 : hs1, j * D / NH, (j + 1) * D / NH);
+                    // the Philox work runs while the staged registers are free
+                    if (j == NH - 1) draw(s + 1, b ? me0 : me1);
+                    load(s + 1 + P, a[(b + 1) % P], j * D / NH, (j + 1) * D / NH);
+                }
                 lds_barrier();
             }
         }
@@ -188,21 +245,21 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
         *reinterpret_cast<uint2 *>(dst + k * 128) = make_uint2(acc[k][0], acc[k][1]);
 }
 
+// The built (R, P) pairs: two register sets where the R rows leave room
+// for them (R = 8, 16), one set (loaded in two halves when R = 4) otherwise.
 template <class T>
-const void *pick_fused(int R) {
-    switch (R) {
-        case 4: return (const void *)k_stack_fused<T, 4>;
-        case 8: return (const void *)k_stack_fused<T, 8>;
-        case 16: return (const void *)k_stack_fused<T, 16>;
-        case 32: return (const void *)k_stack_fused<T, 32>;
-        default: return nullptr;
-    }
+const void *pick_fused(int R, int P) {
+    if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 4, 1>;
+    if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 8, 2>;
+    if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 16, 2>;
+    if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 32, 1>;
+    return nullptr;
 }
 
 template <class T>
 hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int64_t ldb_units,
                           int32_t units, int accumulate, hipStream_t s) {
-    const void *kern = pick_fused<T>(p.rows_per_wave);
+    const void *kern = pick_fused<T>(p.rows_per_wave, p.load_sets);
     // the kernel's row ownership must match the plan the workspace was
     // sized for: 16 waves x R rows x groups cover d exactly
     if (kern == nullptr || (int64_t)kWaves * p.rows_per_wave * p.groups != fa.d ||
@@ -241,6 +298,8 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
     if (m < 1 || zeta > kFusedMaxZeta || n % K != 0 || lda % K != 0 || !a_aligned) return false;
     if (n < 32 * K || d % kWaves != 0) return false;
     if (di.max_lds < kFusedLdsBytes) return false;
+    // the kernel indexes rows inside a chunk with 32-bit integers
+    if (m > (int64_t)65535 << 30) return false;
     const int64_t db = d / zeta;
     int R = 0, G = 0;
     for (int g = 1; (int64_t)kWaves * g <= d; g *= 2) {
@@ -257,6 +316,7 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
     if (R == 0) return false;
     p->rows_per_wave = R;
     p->groups = G;
+    p->load_sets = (R == 8 || R == 16) ? 2 : 1;
     p->slices = (n + 64 * K - 1) / (64 * K);
     const int64_t per_chunk = p->slices * G;
     int64_t want = (di.num_cu + per_chunk - 1) / per_chunk;

@@ -79,6 +79,7 @@ struct FusedArgs {
 struct FusedPlan {
     int rows_per_wave;          // R: output rows kept in one wavefront's registers
     int groups;                 // G: output row groups (each reads A once)
+    int load_sets;              // P: stages of rows in flight in registers (1 or 2)
     int64_t slices;             // column slices (256 FP16 / 128 FP32 columns)
     int64_t rows_per_chunk;     // input rows per workgroup (whole 128-row stages)
     int64_t chunks;
