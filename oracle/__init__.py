@@ -13,6 +13,8 @@ definitions on the pages it cites:
 * "FlashSketch: Sketch-Kernel Co-Design for Fast Sparse Sketching on GPUs"
   (the FlashSketch page): BlockPerm-SJLT (§4, Figure 2, App. A.1, App. D),
   the metrics of App. F.1.
+* The FP16 sketching page's conversion variants (§III-D, §V-E):
+  stochastic conversion to FP16 and BF16 accumulation (``lowp``).
 
 Floating point is fp64 unless the page fixes the precision (the FP16
 pipeline).  Every function is pinned by tests against something other than
@@ -26,6 +28,8 @@ from .blockperm import (fmix32, perm_sigma, shift_wiring, blockperm_params,
                         blockperm_hash, blockperm_matrix, blockperm_dense_S,
                         blockperm_f64)
 from .metrics import rel_frob, ose_error, sv_ratio, gram_rel_error
+from .lowp import (sr_words, f16_neighbours, sr_f16, rn_bf16, rn_bf16_add,
+                   sketch_lowp_emul)
 
 __all__ = [
     "philox4x32_10", "philox_scalar", "PHILOX4x32", "PHILOX4x64",
@@ -34,4 +38,5 @@ __all__ = [
     "fmix32", "perm_sigma", "shift_wiring", "blockperm_params",
     "blockperm_hash", "blockperm_matrix", "blockperm_dense_S", "blockperm_f64",
     "rel_frob", "ose_error", "sv_ratio", "gram_rel_error",
+    "sr_words", "f16_neighbours", "sr_f16", "rn_bf16", "rn_bf16_add", "sketch_lowp_emul",
 ]
