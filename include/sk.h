@@ -62,6 +62,12 @@ typedef enum sk_status {
 #define SK_VARIANT_LDS  4u  /* LDS-privatized partial sketches (default when
                                the d x slice partial fits in LDS) */
 
+/* format and convert arguments of sk_apply_lowp */
+#define SK_FORMAT_F16  0
+#define SK_FORMAT_BF16 1
+#define SK_CONVERT_RN  0
+#define SK_CONVERT_SR  1
+
 /* precision argument of sk_apply_workspace_size and sk_sketch_workspace_size */
 #define SK_PRECISION_F32    0
 #define SK_PRECISION_F16ACC 1
@@ -160,6 +166,43 @@ sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *row_idx, const float *val, int32_t zeta,
                           uint16_t *B, int32_t d, int64_t ldb, uint32_t flags,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sk_apply_lowp: the reduced-precision sketch with a choice of contribution
+ * conversion and accumulation format (FP16 sketching page §III-D: the
+ * contribution is converted by one of several rules and fed to the same
+ * packed nearest-even atomic accumulation; §V-E: a BF16 variant).
+ * The page's flat design: one packed global atomic per (row, block, column
+ * pair), so the additions happen in an unspecified order.
+ *
+ *   A, row_idx, val, zeta, d, ldb  as for sk_apply_f16acc (n, lda, ldb
+ *            even; A 8-byte and B 4-byte aligned).
+ *   B        device uint16 bits, d x n: IEEE binary16 (SK_FORMAT_F16) or
+ *            bfloat16 (SK_FORMAT_BF16, 8-bit exponent and significand).
+ *   format, convert
+ *            SK_FORMAT_F16 + SK_CONVERT_RN: nearest-even (the FP16 kernel's
+ *              rule, here without LDS privatization);
+ *            SK_FORMAT_F16 + SK_CONVERT_SR: stochastic conversion.  For a
+ *              contribution q with FP16 neighbours l <= |q| < v, the
+ *              magnitude becomes v when the 32-bit draw r < frac * 2^32,
+ *              frac = (|q| - l)/(v - l), else l; representable q are kept;
+ *              past 65504 the upper neighbour is 2^16 and means +-inf.  The
+ *              draw for global row g = row_offset + i, block t, column c is
+ *              word c mod 4 of Philox-4x32-10 of counter (g lo, g hi,
+ *              c div 4, 3 + 4t) and key (sr_seed lo, sr_seed hi);
+ *            SK_FORMAT_BF16 + SK_CONVERT_RN: nearest-even conversion to
+ *              BF16 and packed BF16 nearest-even additions.
+ *            BF16 with SR is SK_ERR_UNSUPPORTED.
+ *   sr_seed, row_offset  the SR draws' seed and A's first global row
+ *            (ignored by the RN rules; row_offset >= 0).
+ *   flags    SK_ACCUMULATE or 0 (0 zeroes B first, on the stream).
+ * Errors: as sk_apply_f16acc, plus SK_ERR_ARG for an unknown format,
+ * conversion or flag and SK_ERR_UNSUPPORTED for BF16 with SR.
+ */
+sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
+                        const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
+                        int32_t d, int64_t ldb, int32_t format, int32_t convert,
+                        uint64_t sr_seed, int64_t row_offset, uint32_t flags, void *stream);
 
 /*
  * sk_apply_workspace_size: bytes of workspace that sk_apply_f32

@@ -24,6 +24,10 @@ SK_VARIANT_FLAT = 2
 SK_VARIANT_LDS = 4
 SK_PRECISION_F32 = 0
 SK_PRECISION_F16ACC = 1
+SK_FORMAT_F16 = 0
+SK_FORMAT_BF16 = 1
+SK_CONVERT_RN = 0
+SK_CONVERT_SR = 1
 
 _c = ctypes
 _SIGNATURES = {
@@ -54,6 +58,10 @@ _SIGNATURES = {
     "sk_fused_plan_describe": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int64,
                                           _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
                                           _c.c_int32, _c.POINTER(_c.c_int64)]),
+    "sk_apply_lowp": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
+                                 _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
+                                 _c.c_int32, _c.c_int32, _c.c_uint64, _c.c_int64, _c.c_uint32,
+                                 _c.c_void_p]),
     "sk_status_string": (_c.c_char_p, [_c.c_int]),
 }
 
@@ -178,6 +186,13 @@ def sk_lds_plan_describe(precision, m, n, lda, d, zeta, wide_ok, num_cu, max_lds
     return dict(zip(PLAN_FIELDS, list(out)))
 
 
+def sk_apply_lowp(A, m, n, lda, row_idx, val, zeta, B, d, ldb, format, convert, sr_seed=0,
+                  row_offset=0, flags=0, stream=None):
+    _check("sk_apply_lowp", load().sk_apply_lowp(
+        _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, format, convert,
+        sr_seed, row_offset, flags, _stream(stream)))
+
+
 def sk_sketch_f32(seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags=0, workspace=None,
                   workspace_bytes=0, stream=None):
     _check("sk_sketch_f32", load().sk_sketch_f32(
@@ -275,6 +290,29 @@ def sketch(A, d, zeta, seed, precision="f16acc", flags=0, ws=True, stream=None):
     """Complete sketch: metadata generation, output initialization and application."""
     row_idx, val = meta(seed, A.shape[0], d, zeta, device=A.device, stream=stream)
     return apply(A, row_idx, val, zeta, d, precision, flags=flags, ws=ws, stream=stream)
+
+
+def apply_lowp(A, row_idx, val, zeta, d, fmt="f16", conv="rn", sr_seed=0, row_offset=0, out=None,
+               flags=0, stream=None):
+    """Reduced-precision sketch from metadata: fmt "f16" (float16 B) with
+    conv "rn" or "sr", or fmt "bf16" (bfloat16 B) with conv "rn"."""
+    import torch
+    _need_device(A, torch.float32, "A")
+    m, n = A.shape
+    dt = torch.float16 if fmt == "f16" else torch.bfloat16
+    if out is None:
+        out = torch.empty((d, n), dtype=dt, device=A.device)
+    _need_device(out, dt, "out")
+    if m:
+        _need_device(row_idx, torch.int32, "row_idx")
+        _need_device(val, torch.float32, "val")
+        if row_idx.numel() < m * zeta or val.numel() < m * zeta:
+            raise ValueError("metadata shorter than m*zeta")
+    f = SK_FORMAT_F16 if fmt == "f16" else SK_FORMAT_BF16
+    c = SK_CONVERT_RN if conv == "rn" else SK_CONVERT_SR
+    sk_apply_lowp(A, m, n, A.stride(0) if m else n, row_idx if m else None, val if m else None,
+                  zeta, out, d, out.stride(0), f, c, sr_seed, row_offset, flags, stream)
+    return out
 
 
 def sketch_workspace(A, d, zeta, precision="f16acc"):

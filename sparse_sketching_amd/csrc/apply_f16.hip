@@ -8,7 +8,7 @@
 // each half rounded to nearest-even, subnormals kept.  Here that is one
 // no-return global_atomic_pk_add_f16 per (row, block, column pair), 64 lanes
 // on 128 consecutive columns.  The LDS-privatized FP16 apply is in
-// apply_lds.hip.
+// sk_stack_apply.hpp; the conversion variants are in apply_lowp.hip.
 #include "sk_internal.hpp"
 #include "sk_apply_common.hpp"
 

@@ -389,6 +389,32 @@ sk_status sk_lds_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t 
     return SK_OK;
 }
 
+sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
+                        const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
+                        int32_t d, int64_t ldb, int32_t format, int32_t convert,
+                        uint64_t sr_seed, int64_t row_offset, uint32_t flags, void *stream) {
+    if (format != SK_FORMAT_F16 && format != SK_FORMAT_BF16) return SK_ERR_ARG;
+    if (convert != SK_CONVERT_RN && convert != SK_CONVERT_SR) return SK_ERR_ARG;
+    if (flags & ~SK_ACCUMULATE) return SK_ERR_ARG;
+    if (row_offset < 0) return SK_ERR_SHAPE;
+    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 2, d, ldb, flags);
+    if (st != SK_OK) return st;
+    if (n % 2 != 0) return SK_ERR_SHAPE;
+    if (ldb % 2 != 0 || (uintptr_t)B % 4 != 0) return SK_ERR_ALIGN;
+    if (m > 0 && (lda % 2 != 0 || (uintptr_t)A % 8 != 0)) return SK_ERR_ALIGN;
+    if (format == SK_FORMAT_BF16 && convert == SK_CONVERT_SR) return SK_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    if (!(flags & SK_ACCUMULATE)) {
+        const hipError_t e =
+            sk::launch_zero_words(reinterpret_cast<uint32_t *>(B), d, n / 2, ldb / 2, s);
+        if (e != hipSuccess) return SK_ERR_HIP;
+    }
+    if (m == 0) return SK_OK;
+    return hip_status(sk::launch_lowp_flat(A, m, n, lda, row_idx, val, zeta, B, d, ldb,
+                                           format == SK_FORMAT_BF16, convert == SK_CONVERT_SR,
+                                           sr_seed, row_offset, s));
+}
+
 sk_status sk_sketch_f32(uint64_t seed, int64_t row_offset, const float *A, int64_t m, int32_t n,
                         int64_t lda, int32_t d, int32_t zeta, float *B, int64_t ldb,
                         uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {

@@ -49,6 +49,12 @@ hipError_t launch_f32_flat(const float *A, int64_t m, int32_t n, int64_t lda,
 hipError_t launch_f16_flat(const float *A, int64_t m, int32_t n, int64_t lda,
                            const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
                            int32_t d, int64_t ldb, hipStream_t stream);
+// Reduced-precision flat scatter: FP16 (nearest-even or stochastic
+// conversion) or BF16 (nearest-even) contributions, packed global atomics.
+hipError_t launch_lowp_flat(const float *A, int64_t m, int32_t n, int64_t lda,
+                            const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
+                            int32_t d, int64_t ldb, bool bf16, bool sr, uint64_t sr_seed,
+                            int64_t row_offset, hipStream_t stream);
 // LDS-privatized apply.  ws == NULL: the partials are added to B with global
 // atomics (B must hold its start value).  ws != NULL: the partials are
 // stored to ws (plan.ws_bytes) and a reduce kernel writes B (accumulate=0)

@@ -20,7 +20,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"sk_meta_generate", "sk_apply_f32", "sk_apply_f16acc",
                           "sk_apply_workspace_size", "sk_lds_plan_describe",
                           "sk_sketch_f32", "sk_sketch_f16acc", "sk_sketch_workspace_size",
-                          "sk_fused_plan_describe", "sk_apply_blockperm", "sk_status_string"}
+                          "sk_fused_plan_describe", "sk_apply_lowp", "sk_apply_blockperm",
+                          "sk_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -334,3 +335,22 @@ def test_fused_plan_alignment_and_validation(lib):
     assert lib.sk_fused_plan_describe(1, 10, 7, 8, 1, 8, 1, 256, 163840, out) == b.SK_ERR_SHAPE
     assert lib.sk_fused_plan_describe(0, 10, 8, 8, 1, 8, 1, 0, 163840, out) == b.SK_ERR_ARG
     assert lib.sk_fused_plan_describe(0, 10, 8, 8, 1, 8, 1, 256, 163840, None) == b.SK_ERR_NULL
+
+
+# ------------------------------------------------- conversion variants
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 2, 0, 0, 0, 0), b.SK_ERR_ARG),      # unknown format
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 2, 0, 0, 0), b.SK_ERR_ARG),      # unknown conversion
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 0, 0, 0, 2), b.SK_ERR_ARG),      # variant flag
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 1, 0, -1, 0), b.SK_ERR_SHAPE),   # row_offset < 0
+    ((A, 100, 63, 64, RI, V, 4, B, 64, 64, 0, 0, 0, 0, 0), b.SK_ERR_SHAPE),    # odd n
+    ((A, 100, 64, 64, RI, V, 3, B, 64, 64, 0, 0, 0, 0, 0), b.SK_ERR_SHAPE),    # d % zeta
+    ((A, 100, 64, 64, RI, V, 4, B + 2, 64, 64, 0, 0, 0, 0, 0), b.SK_ERR_ALIGN),  # B % 4
+    ((A, 100, 64, 65, RI, V, 4, B, 64, 64, 1, 0, 0, 0, 0), b.SK_ERR_ALIGN),    # odd lda
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 1, 1, 0, 0, 0), b.SK_ERR_UNSUPPORTED),  # BF16 + SR
+    ((A, 100, 64, 64, None, V, 4, B, 64, 64, 0, 0, 0, 0, 0), b.SK_ERR_NULL),
+    ((A, 100, 64, 64, RI, V, 4, A + 256, 64, 64, 0, 0, 0, 0, 0), b.SK_ERR_ARG),  # B inside A
+])
+def test_lowp_validation(lib, args, expect):
+    assert lib.sk_apply_lowp(*args, None) == expect
