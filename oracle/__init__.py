@@ -13,6 +13,8 @@ definitions on the pages it cites:
 * "FlashSketch: Sketch-Kernel Co-Design for Fast Sparse Sketching on GPUs"
   (the FlashSketch page): BlockPerm-SJLT (§4, Figure 2, App. A.1, App. D),
   the metrics of App. F.1.
+* Sketch-and-solve least squares and ridge regression on a sketch (FP16
+  sketching page §V-D, FlashSketch App. F.1.3-F.1.4) (``solve``).
 * The FP16 sketching page's conversion variants (§III-D, §V-E):
   stochastic conversion to FP16 and BF16 accumulation (``lowp``).
 
@@ -28,6 +30,7 @@ from .blockperm import (fmix32, perm_sigma, shift_wiring, blockperm_params,
                         blockperm_hash, blockperm_matrix, blockperm_dense_S,
                         blockperm_f64)
 from .metrics import rel_frob, ose_error, sv_ratio, gram_rel_error
+from .solve import residual, lstsq_qr, sketch_solve, ridge_solve, reference_solution
 from .lowp import (sr_words, f16_neighbours, sr_f16, rn_bf16, rn_bf16_add,
                    sketch_lowp_emul)
 
@@ -38,5 +41,6 @@ __all__ = [
     "fmix32", "perm_sigma", "shift_wiring", "blockperm_params",
     "blockperm_hash", "blockperm_matrix", "blockperm_dense_S", "blockperm_f64",
     "rel_frob", "ose_error", "sv_ratio", "gram_rel_error",
+    "residual", "lstsq_qr", "sketch_solve", "ridge_solve", "reference_solution",
     "sr_words", "f16_neighbours", "sr_f16", "rn_bf16", "rn_bf16_add", "sketch_lowp_emul",
 ]
