@@ -219,6 +219,25 @@ def main():
     print(f"[bench] apply+reduce {ms_kernel:.4f} ms, apply(atomic flush) {ms_kernel_atomic:.4f} ms, "
           f"meta {ms_meta:.4f} ms, copy {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # downstream: complete sketch-and-solve (shared-map SA and Sb, FP32 QR,
+    # projection, triangular solve) with FP16 and FP32 sketches, d = 2n
+    from sparse_sketching_amd import solve
+    g = torch.Generator(device=dev).manual_seed(5)
+    x0 = torch.randn(n, device=dev, generator=g)
+    rhs = A @ x0 + 0.1 * torch.randn(m, device=dev, generator=g)
+    ls = {}
+    for prec in ("f16acc", "f32"):
+        ls[prec] = timed(lambda: solve.solve_sketched(*solve.sketch_pair(A, rhs, d, zeta, SEED, prec)),
+                         K, W, stream)
+    res = {p: solve.sketch_and_solve(A, rhs, d, zeta, SEED, p)[1] for p in ("f16acc", "f32")}
+    ls_out = {"workload": f"least squares A 2^20 x {n}, b = A x0 + 0.1 N(0,1), d = {d}, zeta = {zeta}",
+              "fp16_ms": round(ls["f16acc"], 4), "fp32_ms": round(ls["f32"], 4),
+              "speedup": round(ls["f32"] / ls["f16acc"], 3),
+              "fp16_residual": round(res["f16acc"], 6), "fp32_residual": round(res["f32"], 6)}
+    print(f"[bench] sketch-and-solve fp16 {ls['f16acc']:.4f} ms fp32 {ls['f32']:.4f} ms, "
+          f"residuals {res['f16acc']:.6f} / {res['f32']:.6f}", file=sys.stderr, flush=True)
+    del rhs, x0
+
     A_host = None if args.no_cpu_baseline else A.cpu().numpy()
     bp = None
     if not args.no_blockperm:
@@ -272,6 +291,7 @@ def main():
         "meta_ms": round(ms_meta, 5),
         "copy_GBps": round(copy_gbs, 1),
         "blockperm": bp,
+        "sketch_and_solve": ls_out,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_bytes(),
