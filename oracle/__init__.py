@@ -27,8 +27,8 @@ from .philox import philox4x32_10, philox_scalar, PHILOX4x32, PHILOX4x64
 from .sparsestack import (scale_f32, meta_ref, sketch_matrix, dense_S, sketch_f64,
                           countsketch_f64, sketch_f16_rn_emul, rn_f16_add)
 from .blockperm import (fmix32, perm_sigma, shift_wiring, blockperm_params,
-                        blockperm_hash, blockperm_matrix, blockperm_dense_S,
-                        blockperm_f64)
+                        blockperm_hash, blockperm_hash_s, blockperm_matrix, blockperm_dense_S,
+                        blockperm_f64, affine_params, affine_wiring, wiring, prime_factors)
 from .metrics import rel_frob, ose_error, sv_ratio, gram_rel_error
 from .solve import residual, lstsq_qr, sketch_solve, ridge_solve, reference_solution
 from .lowp import (sr_words, f16_neighbours, sr_f16, rn_bf16, rn_bf16_add,
@@ -40,6 +40,7 @@ __all__ = [
     "countsketch_f64", "sketch_f16_rn_emul", "rn_f16_add",
     "fmix32", "perm_sigma", "shift_wiring", "blockperm_params",
     "blockperm_hash", "blockperm_matrix", "blockperm_dense_S", "blockperm_f64",
+    "blockperm_hash_s", "affine_params", "affine_wiring", "wiring", "prime_factors",
     "rel_frob", "ose_error", "sv_ratio", "gram_rel_error",
     "residual", "lstsq_qr", "sketch_solve", "ridge_solve", "reference_solution",
     "sr_words", "f16_neighbours", "sr_f16", "rn_bf16", "rn_bf16_add", "sketch_lowp_emul",

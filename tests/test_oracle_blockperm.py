@@ -179,5 +179,92 @@ def test_invalid_shapes():
         blockperm_params(1000, 64, 64, 4, 1)
     with pytest.raises(ValueError):
         blockperm_params(1024, 64, 64, 3, 1)
-    with pytest.raises(NotImplementedError):
-        blockperm_matrix(1024, 64, 8, 4, 2, 1)
+    with pytest.raises(ValueError):
+        blockperm_params(1024, 96, 8, 4, 2)        # s > 1 needs a power-of-two B_r
+    with pytest.raises(ValueError):
+        blockperm_params(1024, 64, 8, 9, 1, "affine")   # kappa > M
+
+
+# --------------------------------------------- affine wiring and s > 1
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 12, 60, 64, 97, 100, 128, 1024])
+@pytest.mark.parametrize("seed", [0, 1, 12345678901])
+def test_affine_map_is_a_full_cycle(M, seed):
+    """Hull-Dobell: the drawn (a, b) make f(x) = (a x + b) mod M visit all of
+    [M] from any start (checked by walking the orbit)."""
+    import oracle
+    a, b = oracle.affine_params(seed, M)
+    assert 0 <= a < max(M, 2) and 0 <= b < max(M, 1)
+    x, seen = 0, set()
+    for _ in range(M):
+        seen.add(x)
+        x = (a * x + b) % M
+    assert len(seen) == M and x == 0
+    if M > 1:
+        assert math.gcd(b, M) == 1
+        for p in oracle.prime_factors(M):
+            assert (a - 1) % p == 0
+        if M % 4 == 0:
+            assert (a - 1) % 4 == 0
+
+
+@pytest.mark.parametrize("M,kappa", [(64, 4), (60, 7), (12, 12), (97, 3), (8, 1)])
+def test_affine_wiring_biregular_edge_disjoint(M, kappa):
+    import oracle
+    N = oracle.wiring(5, M, kappa, "affine")
+    for l in range(kappa):
+        assert sorted(N[:, l].tolist()) == list(range(M))      # each pi_l a permutation
+    assert all(len(set(N[g].tolist())) == kappa for g in range(M))   # edge-disjoint
+    counts = np.bincount(N.ravel(), minlength=M)
+    assert np.all(counts == kappa)
+
+
+def test_affine_wiring_is_powers_of_f():
+    import oracle
+    a, b = oracle.affine_params(3, 64)
+    N = oracle.affine_wiring(a, b, 64, 5)
+    for g in (0, 17, 63):
+        x = g
+        for l in range(5):
+            x = (a * x + b) % 64
+            assert N[g, l] == x
+
+
+@pytest.mark.parametrize("B_r,s", [(16, 1), (16, 2), (16, 4), (8, 8), (64, 3), (1, 1)])
+def test_s_rows_distinct_and_s1_unchanged(B_r, s):
+    import oracle
+    r = np.arange(3000)
+    rows, signs = oracle.blockperm_hash_s(9, 3, 5, r, B_r, s)
+    assert rows.shape == (3000, s) and np.all((rows >= 0) & (rows < B_r))
+    assert all(len(set(rows[i].tolist())) == s for i in range(0, 3000, 7))
+    assert set(np.unique(signs).tolist()) <= {-1.0, 1.0}
+    b1, s1 = blockperm_hash(9, 3, 5, r, B_r)
+    assert np.array_equal(rows[:, 0], b1) and np.array_equal(signs[:, 0], s1)
+
+
+@pytest.mark.parametrize("kind,kappa,s", [("affine", 3, 1), ("affine", 4, 2), ("shift", 4, 4),
+                                          ("shift", 2, 2)])
+def test_dense_brute_force_general(kind, kappa, s):
+    """S built nonzero by nonzero equals the sparse construction; every
+    column holds exactly kappa*s nonzeros of magnitude float32(1/sqrt(kappa s))."""
+    import oracle
+    m, d, M = 96, 64, 8
+    Sd = oracle.blockperm_dense_S(m, d, M, kappa, s, 7, kind)
+    Ss = oracle.blockperm_matrix(m, d, M, kappa, s, 7, kind=kind).toarray()
+    assert np.array_equal(Sd, Ss)
+    c = float(np.float32(1 / math.sqrt(kappa * s)))
+    nnz = (Sd != 0).sum(axis=0)
+    assert np.all(nnz == kappa * s)
+    assert np.allclose(np.abs(Sd[Sd != 0]), c)
+    A = np.random.default_rng(1).standard_normal((m, 5))
+    assert np.allclose(oracle.blockperm_f64(A, d, M, kappa, s, 7, kind), Sd @ A, rtol=1e-12,
+                       atol=1e-12)
+
+
+def test_unbiased_norm_affine_s2():
+    import oracle
+    m, d, M, kappa, s = 256, 64, 8, 3, 2
+    x = np.random.default_rng(2).standard_normal((m, 1))
+    r = np.array([float((oracle.blockperm_f64(x, d, M, kappa, s, seed, "affine") ** 2).sum()
+                        / (x ** 2).sum()) for seed in range(300)])
+    assert abs(r.mean() - 1) < 5 * r.std(ddof=1) / math.sqrt(r.size)
