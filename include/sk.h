@@ -62,6 +62,10 @@ typedef enum sk_status {
 #define SK_VARIANT_LDS  4u  /* LDS-privatized partial sketches (default when
                                the d x slice partial fits in LDS) */
 
+/* wiring argument of sk_apply_blockperm_ex */
+#define SK_WIRING_SHIFT  0
+#define SK_WIRING_AFFINE 1
+
 /* format and convert arguments of sk_apply_lowp */
 #define SK_FORMAT_F16  0
 #define SK_FORMAT_BF16 1
@@ -321,6 +325,61 @@ sk_status sk_apply_blockperm(const float *A, int64_t m, int32_t n, int64_t lda,
                              int32_t d, int32_t M, int32_t kappa, int32_t s,
                              uint64_t seed, float *Y, int64_t ldy, uint32_t flags,
                              void *stream);
+
+/*
+ * sk_apply_blockperm_ex: BlockPerm-SJLT with the general options.
+ * (FlashSketch page §4, §5, App. B.1 split-B_c, App. D wiring and
+ * within-block hashing.)
+ *
+ *   wiring  SK_WIRING_SHIFT: sk_apply_blockperm's family (kappa | M);
+ *           SK_WIRING_AFFINE: pi_l = f^l, l = 1..kappa (kappa <= M), for the
+ *           full-cycle map f(x) = (a x + b) mod M: with L the product of the
+ *           distinct primes of M (times 2 when 4 | M and 4 does not divide
+ *           it yet), a = 1 + L*floor(w0*(M/L)/2^32) (a = 1 when L >= M) and b
+ *           the floor(w1*phi(M)/2^32)-th integer in [1, M) coprime to M,
+ *           (w0, w1) the first words of Philox-4x32-10 of counter
+ *           (0, 0, 0, 1) and key (seed lo, seed hi).
+ *   s       nonzeros per column inside a block (1 <= s <= min(32, B_r);
+ *           s > 1 needs B_r a power of two): with v and beta as for s = 1,
+ *           w = fmix32(v + 0x9E3779B9) and alpha = 2*floor(w*(B_r/2)/2^32) + 1,
+ *           row j = (beta + j*alpha) mod B_r, sign negative when bit j of v
+ *           is set.  Each nonzero is +-1/sqrt(kappa*s).
+ *   kappa   <= 32.
+ *   workspace, workspace_bytes
+ *           device scratch (4-byte aligned, disjoint from A and Y) of
+ *           sk_blockperm_workspace_size bytes; NULL is accepted when that
+ *           size is 0 (the shift/s = 1 kernel with enough components runs,
+ *           as sk_apply_blockperm).  Otherwise a kernel per (input block,
+ *           row slice, 32-column tile) writes kappa partial tiles once, and
+ *           a second kernel writes each Y element once as their sum in a
+ *           fixed order (neighbour, then slice): no atomics.
+ *   flags   SK_ACCUMULATE only.
+ * Errors: as sk_apply_blockperm, plus SK_ERR_ARG (unknown wiring, small
+ * workspace), SK_ERR_NULL (missing workspace), SK_ERR_UNSUPPORTED (s or
+ * kappa above 32, s > 1 with B_r not a power of two, tiles too large for LDS).
+ */
+sk_status sk_apply_blockperm_ex(const float *A, int64_t m, int32_t n, int64_t lda, int32_t d,
+                                int32_t M, int32_t kappa, int32_t s, int32_t wiring,
+                                uint64_t seed, float *Y, int64_t ldy, uint32_t flags,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sk_blockperm_workspace_size: workspace bytes sk_apply_blockperm_ex needs
+ * for these sizes on the current device (0: none).
+ */
+sk_status sk_blockperm_workspace_size(int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa,
+                                      int32_t s, int32_t wiring, size_t *bytes);
+
+/*
+ * sk_blockperm_plan_describe: sk_apply_blockperm_ex's plan, computed on the
+ * host (no HIP call): out int64[SK_BLOCKPERM_PLAN_FIELDS] = {general kernel
+ * used, row slices Q, rows per slice, workspace bytes, affine a, affine b,
+ * a^-1 mod M} (a, b, a^-1 are 0 for the shift wiring).
+ */
+#define SK_BLOCKPERM_PLAN_FIELDS 7
+sk_status sk_blockperm_plan_describe(int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa,
+                                     int32_t s, int32_t wiring, uint64_t seed, int32_t num_cu,
+                                     int32_t max_lds, int64_t *out);
 
 /*
  * sk_lds_plan_describe: the launch plan sk_apply_f32 (precision

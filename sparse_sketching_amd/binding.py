@@ -28,6 +28,8 @@ SK_FORMAT_F16 = 0
 SK_FORMAT_BF16 = 1
 SK_CONVERT_RN = 0
 SK_CONVERT_SR = 1
+SK_WIRING_SHIFT = 0
+SK_WIRING_AFFINE = 1
 
 _c = ctypes
 _SIGNATURES = {
@@ -62,6 +64,16 @@ _SIGNATURES = {
                                  _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
                                  _c.c_int32, _c.c_int32, _c.c_uint64, _c.c_int64, _c.c_uint32,
                                  _c.c_void_p]),
+    "sk_apply_blockperm_ex": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64,
+                                         _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
+                                         _c.c_int32, _c.c_uint64, _c.c_void_p, _c.c_int64,
+                                         _c.c_uint32, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "sk_blockperm_workspace_size": (_c.c_int, [_c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32,
+                                               _c.c_int32, _c.c_int32, _c.c_int32,
+                                               _c.POINTER(_c.c_size_t)]),
+    "sk_blockperm_plan_describe": (_c.c_int, [_c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32,
+                                              _c.c_int32, _c.c_int32, _c.c_int32, _c.c_uint64,
+                                              _c.c_int32, _c.c_int32, _c.POINTER(_c.c_int64)]),
     "sk_status_string": (_c.c_char_p, [_c.c_int]),
 }
 
@@ -184,6 +196,30 @@ def sk_lds_plan_describe(precision, m, n, lda, d, zeta, wide_ok, num_cu, max_lds
     _check("sk_lds_plan_describe", load().sk_lds_plan_describe(
         precision, m, n, lda, d, zeta, int(bool(wide_ok)), num_cu, max_lds, out))
     return dict(zip(PLAN_FIELDS, list(out)))
+
+
+def sk_apply_blockperm_ex(A, m, n, lda, d, M, kappa, s, wiring, seed, Y, ldy, flags=0,
+                          workspace=None, workspace_bytes=0, stream=None):
+    _check("sk_apply_blockperm_ex", load().sk_apply_blockperm_ex(
+        _ptr(A), m, n, lda, d, M, kappa, s, wiring, seed, _ptr(Y), ldy, flags, _ptr(workspace),
+        _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def sk_blockperm_workspace_size(m, n, d, M, kappa, s, wiring):
+    out = ctypes.c_size_t(0)
+    _check("sk_blockperm_workspace_size", load().sk_blockperm_workspace_size(
+        m, n, d, M, kappa, s, wiring, ctypes.byref(out)))
+    return out.value
+
+
+BLOCKPERM_PLAN_FIELDS = ("general", "Q", "rows_per_slice", "ws_bytes", "a", "b", "ainv")
+
+
+def sk_blockperm_plan_describe(m, n, d, M, kappa, s, wiring, seed, num_cu, max_lds):
+    out = (ctypes.c_int64 * len(BLOCKPERM_PLAN_FIELDS))()
+    _check("sk_blockperm_plan_describe", load().sk_blockperm_plan_describe(
+        m, n, d, M, kappa, s, wiring, seed, num_cu, max_lds, out))
+    return dict(zip(BLOCKPERM_PLAN_FIELDS, list(out)))
 
 
 def sk_apply_lowp(A, m, n, lda, row_idx, val, zeta, B, d, ldb, format, convert, sr_seed=0,
@@ -345,14 +381,22 @@ def sketch_fused(A, d, zeta, seed, precision="f16acc", row_offset=0, out=None, f
     return out
 
 
-def blockperm(A, d, M, kappa, seed, s=1, out=None, flags=0, stream=None):
-    """Y = S A for S ~ BlockPerm-SJLT (float32)."""
+def blockperm(A, d, M, kappa, seed, s=1, out=None, flags=0, wiring="shift", ws=None,
+              stream=None):
+    """Y = S A for S ~ BlockPerm-SJLT (float32).  wiring "shift" or "affine";
+    ws: a byte tensor for the general kernel's partials (allocated when
+    needed and not given)."""
     import torch
     _need_device(A, torch.float32, "A")
     m, n = A.shape
     if out is None:
         out = torch.empty((d, n), dtype=torch.float32, device=A.device)
     _need_device(out, torch.float32, "out")
-    sk_apply_blockperm(A, m, n, A.stride(0), d, M, kappa, s, seed, out, out.stride(0), flags,
-                       stream)
+    w = SK_WIRING_SHIFT if wiring == "shift" else SK_WIRING_AFFINE
+    if ws is None:
+        nbytes = sk_blockperm_workspace_size(m, n, d, M, kappa, s, w)
+        if nbytes:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=A.device)
+    sk_apply_blockperm_ex(A, m, n, A.stride(0), d, M, kappa, s, w, seed, out, out.stride(0),
+                          flags, ws, 0, stream)
     return out

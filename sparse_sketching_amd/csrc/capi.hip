@@ -282,6 +282,122 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
                           w + 2 * meta, workspace_bytes - 2 * meta, s);
 }
 
+// BlockPerm launch plan: the component kernel (shift wiring, s = 1, kappa
+// in {1, 2, 4, 8}, enough components x tiles to fill the device) or the
+// general kernel with Q row slices and a workspace of Q*kappa*d*n floats.
+struct BpPlan {
+    bool general;
+    int32_t Q;
+    int64_t rows_per_slice;
+    size_t ws_bytes;
+    uint32_t a, ainv, b;        // affine wiring parameters
+};
+
+uint32_t gcd_u32(uint32_t x, uint32_t y) {
+    while (y) {
+        const uint32_t t = x % y;
+        x = y;
+        y = t;
+    }
+    return x;
+}
+
+// f(x) = (a x + b) mod M, a full cycle (Hull-Dobell), drawn from the seed:
+// L = product of M's distinct primes (times 2 more when 4 | M and L is not
+// already a multiple of 4), a = 1 + L*mulhi(w0, M/L) (1 when L >= M), b = the
+// mulhi(w1, phi(M))-th unit below M; (w0, w1) = Philox(0, 0, 0, 1).
+void affine_params(uint64_t seed, int32_t M, uint32_t *a, uint32_t *b, uint32_t *ainv) {
+    if (M <= 1) {
+        *a = 1;
+        *b = 0;
+        *ainv = 1;
+        return;
+    }
+    const sk::u32x4 w = sk::philox4x32_10(sk::u32x4{0u, 0u, 0u, 1u}, (uint32_t)seed,
+                                          (uint32_t)(seed >> 32));
+    uint32_t L = 1, x = (uint32_t)M;
+    for (uint32_t p = 2; p * p <= x; ++p) {
+        if (x % p == 0) {
+            L *= p;
+            while (x % p == 0) x /= p;
+        }
+    }
+    if (x > 1) L *= x;
+    if (M % 4 == 0 && L % 4 != 0) L *= 2;
+    *a = L < (uint32_t)M ? 1u + L * sk::mulhi32(w.x, (uint32_t)M / L) : 1u;
+    uint32_t phi = 0;
+    for (uint32_t u = 1; u < (uint32_t)M; ++u) phi += gcd_u32(u, (uint32_t)M) == 1;
+    const uint32_t k = sk::mulhi32(w.y, phi);
+    uint32_t seen = 0;
+    *b = 1;
+    for (uint32_t u = 1; u < (uint32_t)M; ++u) {
+        if (gcd_u32(u, (uint32_t)M) != 1) continue;
+        if (seen++ == k) {
+            *b = u;
+            break;
+        }
+    }
+    *ainv = 1;
+    for (uint32_t v = 1; v < (uint32_t)M; ++v)
+        if ((uint64_t)*a * v % (uint32_t)M == 1) {
+            *ainv = v;
+            break;
+        }
+}
+
+// Validation shared by the BlockPerm entry points.
+sk_status check_blockperm(int64_t m, int32_t n, int64_t lda, int32_t d, int32_t M, int32_t kappa,
+                          int32_t s, int32_t wiring, int64_t ldy) {
+    if (m < 1 || n < 1 || d < 1 || M < 1 || kappa < 1 || s < 1) return SK_ERR_SHAPE;
+    if (wiring != SK_WIRING_SHIFT && wiring != SK_WIRING_AFFINE) return SK_ERR_ARG;
+    if (M > sk::kBlockPermMaxM) return SK_ERR_UNSUPPORTED;
+    if (m % M != 0 || d % M != 0 || lda < n || ldy < n) return SK_ERR_SHAPE;
+    if (wiring == SK_WIRING_SHIFT && M % kappa != 0) return SK_ERR_SHAPE;
+    if (kappa > M) return SK_ERR_SHAPE;
+    const int32_t Br = d / M;
+    if (s > Br) return SK_ERR_SHAPE;
+    if (m > INT64_MAX / 8 / lda) return SK_ERR_SHAPE;
+    if (s > 1 && (Br & (Br - 1)) != 0) return SK_ERR_UNSUPPORTED;
+    if (s > 32 || kappa > sk::kBlockPermGenMaxKappa) return SK_ERR_UNSUPPORTED;
+    return SK_OK;
+}
+
+bool plan_blockperm(const sk::DevInfo &di, int64_t m, int32_t n, int32_t d, int32_t M,
+                    int32_t kappa, int32_t s, int32_t wiring, uint64_t seed, BpPlan *p) {
+    const int32_t Br = d / M;
+    const int64_t Bc = m / M;
+    const int64_t tiles = (n + 31) / 32;
+    memset(p, 0, sizeof(*p));
+    const bool comp_ok = wiring == SK_WIRING_SHIFT && s == 1 &&
+                         (kappa == 1 || kappa == 2 || kappa == 4 || kappa == 8) &&
+                         (int64_t)kappa * Br <= sk::blockperm_max_rows(di);
+    if (comp_ok && tiles * (M / kappa) >= di.num_cu) return true;
+    if ((int64_t)kappa * Br > sk::blockperm_general_max_rows(di)) return false;
+    p->general = true;
+    int64_t Q = (2 * (int64_t)di.num_cu + tiles * M - 1) / (tiles * M);
+    const int64_t qmax = Bc / 64 > 1 ? Bc / 64 : 1;
+    if (Q > qmax) Q = qmax;
+    if (Q < 1) Q = 1;
+    if (Q * M > 65535) Q = 65535 / M;
+    p->Q = (int32_t)Q;
+    p->rows_per_slice = (Bc + Q - 1) / Q;
+    p->ws_bytes = (size_t)Q * (size_t)kappa * (size_t)d * (size_t)n * 4;
+    if (wiring == SK_WIRING_AFFINE) affine_params(seed, M, &p->a, &p->b, &p->ainv);
+    return true;
+}
+
+void sigma_table(uint64_t seed, int32_t M, uint16_t *sigma) {
+    for (int k = 0; k < M; ++k) sigma[k] = (uint16_t)k;
+    for (int k = M - 1; k >= 1; --k) {
+        const sk::u32x4 w = sk::philox4x32_10(sk::u32x4{(uint32_t)k, 0u, 0u, 2u}, (uint32_t)seed,
+                                              (uint32_t)(seed >> 32));
+        const uint32_t j = sk::mulhi32(w.x, (uint32_t)(k + 1));
+        const uint16_t t = sigma[k];
+        sigma[k] = sigma[j];
+        sigma[j] = t;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -462,6 +578,91 @@ sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_
                                              p.rows_per_chunk, p.chunks, p.grid,
                                              (int64_t)p.ws_bytes};
     for (int i = 0; i < SK_FUSED_PLAN_FIELDS; ++i) out[i] = v[i];
+    return SK_OK;
+}
+
+sk_status sk_apply_blockperm_ex(const float *A, int64_t m, int32_t n, int64_t lda, int32_t d,
+                                int32_t M, int32_t kappa, int32_t s, int32_t wiring,
+                                uint64_t seed, float *Y, int64_t ldy, uint32_t flags,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    sk_status st = check_blockperm(m, n, lda, d, M, kappa, s, wiring, ldy);
+    if (st != SK_OK) return st;
+    if (flags & ~SK_ACCUMULATE) return SK_ERR_ARG;
+    if (A == nullptr || Y == nullptr) return SK_ERR_NULL;
+    const size_t aspan = span_bytes(m, n, lda, 4), yspan = span_bytes(d, n, ldy, 4);
+    if (overlaps(A, aspan, Y, yspan)) return SK_ERR_ARG;
+    sk::DevInfo di;
+    if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
+    BpPlan p;
+    if (!plan_blockperm(di, m, n, d, M, kappa, s, wiring, seed, &p)) return SK_ERR_UNSUPPORTED;
+    if (!p.general)
+        return sk_apply_blockperm(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags, stream);
+    if (workspace == nullptr) return SK_ERR_NULL;
+    if ((uintptr_t)workspace % 4 != 0) return SK_ERR_ALIGN;
+    if (workspace_bytes < p.ws_bytes) return SK_ERR_ARG;
+    if (overlaps(workspace, workspace_bytes, A, aspan) ||
+        overlaps(workspace, workspace_bytes, Y, yspan))
+        return SK_ERR_ARG;
+    sk::BlockPermGenArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A = A;
+    g.ws = static_cast<float *>(workspace);
+    g.lda = lda;
+    g.Bc = m / M;
+    g.rows_per_slice = p.rows_per_slice;
+    g.n = n;
+    g.Br = d / M;
+    g.M = M;
+    g.kappa = kappa;
+    g.s = s;
+    g.Q = p.Q;
+    g.wiring = wiring;
+    g.C = wiring == SK_WIRING_SHIFT ? M / kappa : 0;
+    g.a = p.a;
+    g.ainv = p.ainv;
+    g.b = p.b;
+    g.scale = scale_of((int64_t)kappa * s);
+    g.seed = seed;
+    sk::BlockPermTable ginv, fwd;
+    memset(&ginv, 0, sizeof(ginv));
+    memset(&fwd, 0, sizeof(fwd));
+    if (wiring == SK_WIRING_SHIFT) {
+        sigma_table(seed, M, fwd.tab);
+        for (int k = 0; k < M; ++k) ginv.tab[fwd.tab[k]] = (uint16_t)k;
+    }
+    return hip_status(sk::launch_blockperm_general(g, ginv, fwd, Y, ldy,
+                                                   (flags & SK_ACCUMULATE) ? 1 : 0,
+                                                   (hipStream_t)stream));
+}
+
+sk_status sk_blockperm_workspace_size(int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa,
+                                      int32_t s, int32_t wiring, size_t *bytes) {
+    if (bytes == nullptr) return SK_ERR_NULL;
+    *bytes = 0;
+    sk_status st = check_blockperm(m, n, n, d, M, kappa, s, wiring, n);
+    if (st != SK_OK) return st;
+    sk::DevInfo di;
+    if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
+    BpPlan p;
+    if (!plan_blockperm(di, m, n, d, M, kappa, s, wiring, 0, &p)) return SK_ERR_UNSUPPORTED;
+    *bytes = p.ws_bytes;
+    return SK_OK;
+}
+
+sk_status sk_blockperm_plan_describe(int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa,
+                                     int32_t s, int32_t wiring, uint64_t seed, int32_t num_cu,
+                                     int32_t max_lds, int64_t *out) {
+    if (out == nullptr) return SK_ERR_NULL;
+    for (int i = 0; i < SK_BLOCKPERM_PLAN_FIELDS; ++i) out[i] = 0;
+    sk_status st = check_blockperm(m, n, n, d, M, kappa, s, wiring, n);
+    if (st != SK_OK) return st;
+    if (num_cu < 1 || max_lds < 1) return SK_ERR_ARG;
+    sk::DevInfo di{num_cu, max_lds};
+    BpPlan p;
+    if (!plan_blockperm(di, m, n, d, M, kappa, s, wiring, seed, &p)) return SK_ERR_UNSUPPORTED;
+    const int64_t v[SK_BLOCKPERM_PLAN_FIELDS] = {p.general ? 1 : 0, p.Q, p.rows_per_slice,
+                                                 (int64_t)p.ws_bytes, p.a, p.b, p.ainv};
+    for (int i = 0; i < SK_BLOCKPERM_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }
 

@@ -119,6 +119,32 @@ struct BlockPermArgs {
 };
 // Largest kappa*B_r the LDS tile allows.
 int blockperm_max_rows(const DevInfo &di);
+
+// General BlockPerm (blockperm_general.hip): any kappa <= 32, s <= 32 unique
+// rows, shift or affine wiring, input blocks in Q row slices; partial tiles
+// to ws, then a fixed-order reduce into Y.
+constexpr int kBlockPermGenMaxKappa = 32;
+struct BlockPermTable {
+    uint16_t tab[kBlockPermMaxM];
+};
+struct BlockPermGenArgs {
+    const float *A;
+    float *ws;                  // [M][Q][kappa][B_r][n] partials
+    int64_t lda;
+    int64_t Bc;                 // input rows per block
+    int64_t rows_per_slice;     // rows per slice (the last may be short)
+    int32_t n, Br, M, kappa, s, Q;
+    int32_t wiring;             // 0: shift, 1: affine
+    int32_t C;                  // shift: M / kappa
+    uint32_t a, ainv, b;        // affine: f(x) = (a x + b) mod M, a^-1 mod M
+    float scale;                // float32(1/sqrt(kappa*s))
+    uint64_t seed;
+};
+int blockperm_general_max_rows(const DevInfo &di);
+// ginv: shift wiring's sigma^-1 (readers); fwd: its sigma (neighbours).
+hipError_t launch_blockperm_general(const BlockPermGenArgs &args, const BlockPermTable &ginv,
+                                    const BlockPermTable &fwd, float *Y, int64_t ldy,
+                                    int accumulate, hipStream_t stream);
 hipError_t launch_blockperm(const BlockPermArgs &args, int32_t kappa, hipStream_t stream);
 
 }  // namespace sk

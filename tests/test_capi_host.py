@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol(lib):
                           "sk_apply_workspace_size", "sk_lds_plan_describe",
                           "sk_sketch_f32", "sk_sketch_f16acc", "sk_sketch_workspace_size",
                           "sk_fused_plan_describe", "sk_apply_lowp", "sk_apply_blockperm",
-                          "sk_status_string"}
+                          "sk_apply_blockperm_ex", "sk_blockperm_workspace_size",
+                          "sk_blockperm_plan_describe", "sk_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -354,3 +355,56 @@ def test_fused_plan_alignment_and_validation(lib):
 ])
 def test_lowp_validation(lib, args, expect):
     assert lib.sk_apply_lowp(*args, None) == expect
+
+
+# ------------------------------------------------------- general BlockPerm
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 12, 60, 64, 97, 100, 128, 1024])
+@pytest.mark.parametrize("seed", [0, 1, 12345678901])
+def test_blockperm_affine_params_match_oracle(M, seed):
+    """The host's affine wiring parameters are the oracle's (independent
+    implementations of the same drawing rule), and a^-1 inverts a."""
+    import oracle
+    p = b.sk_blockperm_plan_describe(M * 64, 32, M * 4, M, 1, 1, b.SK_WIRING_AFFINE, seed,
+                                     num_cu=256, max_lds=160 * 1024)
+    a, bb = oracle.affine_params(seed, M)
+    assert p["general"] == 1 and (p["a"], p["b"]) == (a % max(M, 1) if M > 1 else 1, bb)
+    if M > 1:
+        assert (p["a"] * p["ainv"]) % M == 1
+
+
+@pytest.mark.parametrize("m,n,d,M,kappa,s,wiring", [
+    (1 << 21, 512, 1024, 64, 4, 1, 0),      # the bench workload: component kernel
+    (1 << 21, 512, 1024, 64, 4, 2, 0),      # s > 1: general kernel
+    (1 << 21, 512, 1024, 64, 4, 1, 1),      # affine wiring
+    (1 << 16, 64, 1024, 64, 4, 1, 0),       # few components: split slices
+    (4096, 32, 256, 16, 5, 3, 1),
+])
+def test_blockperm_plan_bounds(m, n, d, M, kappa, s, wiring):
+    p = b.sk_blockperm_plan_describe(m, n, d, M, kappa, s, wiring, 7, num_cu=256,
+                                     max_lds=160 * 1024)
+    Bc = m // M
+    if not p["general"]:
+        assert wiring == 0 and s == 1 and p["ws_bytes"] == 0
+        return
+    Q, rps = p["Q"], p["rows_per_slice"]
+    assert Q >= 1 and rps * Q >= Bc > rps * (Q - 1)
+    assert Q * M <= 65535
+    assert p["ws_bytes"] == Q * kappa * d * n * 4
+    # the largest partial index the scatter kernel writes stays inside it
+    last = ((((M - 1) * Q + Q - 1) * kappa + kappa - 1) * (d // M) + d // M - 1) * n + n - 1
+    assert (last + 1) * 4 <= p["ws_bytes"]
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 4096, 32, 32, 256, 16, 4, 1, 2, 1, B, 32, 0, WSF, 1 << 30), b.SK_ERR_ARG),    # wiring
+    ((A, 4096, 32, 32, 256, 16, 3, 1, 0, 1, B, 32, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),  # kappa !| M (shift)
+    ((A, 4096, 32, 32, 256, 16, 17, 1, 1, 1, B, 32, 0, WSF, 1 << 30), b.SK_ERR_SHAPE), # kappa > M
+    ((A, 4096, 32, 32, 192, 16, 4, 2, 1, 1, B, 32, 0, WSF, 1 << 30), b.SK_ERR_UNSUPPORTED),  # B_r = 12, s > 1
+    ((A, 4096, 32, 32, 256, 16, 4, 17, 1, 1, B, 32, 0, WSF, 1 << 30), b.SK_ERR_SHAPE),  # s > B_r
+    ((A, 4096, 32, 32, 256, 16, 4, 1, 1, 1, B, 32, 2, WSF, 1 << 30), b.SK_ERR_ARG),     # flag
+    ((None, 4096, 32, 32, 256, 16, 4, 1, 1, 1, B, 32, 0, WSF, 1 << 30), b.SK_ERR_NULL),
+    ((A, 4096, 32, 32, 256, 16, 4, 1, 1, 1, A + 64, 32, 0, WSF, 1 << 30), b.SK_ERR_ARG),  # Y in A
+])
+def test_blockperm_ex_validation(lib, args, expect):
+    assert lib.sk_apply_blockperm_ex(*args, None) == expect

@@ -74,3 +74,69 @@ def test_full_configuration_sampled_columns():
     assert err <= 1e-5
     # unbiased norm: E||Sx||^2 = ||x||^2 holds for the whole output
     assert abs(float((Y.double() ** 2).sum() / (Ad.double() ** 2).sum()) - 1) < 0.05
+
+
+# ------------------------------------------------------- general BlockPerm
+
+MI355X = dict(num_cu=256, max_lds=160 * 1024)
+
+
+@pytest.mark.parametrize("kind,m,n,d,M,kappa,s,seed", [
+    ("affine", 512, 33, 64, 8, 3, 1, 5),      # kappa not dividing M
+    ("affine", 1024, 40, 128, 16, 4, 2, 6),   # s = 2
+    ("affine", 768, 7, 96, 12, 5, 1, 7),      # M = 12 (Hull-Dobell with 4 | M)
+    ("affine", 640, 64, 320, 5, 2, 4, 8),     # M prime: a = 1; s = 4 of B_r = 64
+    ("shift", 1024, 36, 128, 8, 4, 2, 9),     # shift wiring with s = 2
+    ("shift", 6 * 100, 7, 6 * 3, 6, 2, 1, 4), # B_c = 100, B_r = 3
+])
+def test_general_vs_dense(kind, m, n, d, M, kappa, s, seed):
+    say(f"blockperm general {kind} m={m} n={n} d={d} M={M} kappa={kappa} s={s}")
+    A = inputs.gaussian(m, n, seed=seed)
+    Y = b.blockperm(to_dev(A), d, M, kappa, seed, s=s, wiring=kind)
+    sync()
+    ref = oracle.blockperm_dense_S(m, d, M, kappa, s, seed, kind) @ A.astype(np.float64)
+    assert oracle.rel_frob(Y.cpu().numpy(), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("kind,kappa,s", [("affine", 4, 1), ("affine", 2, 2), ("shift", 4, 4),
+                                          ("affine", 16, 1)])
+def test_general_integer_exact(kind, kappa, s):
+    """kappa*s a power of 4: the scale is an exact power of two and integer
+    inputs give exact sums in any order, so Y must equal fp64 bit for bit."""
+    m, n, d, M = 8192, 64, 512, 16
+    A = inputs.integer_matrix(m, n, -8, 8, seed=3)
+    ref = oracle.blockperm_f64(A, d, M, kappa, s, 21, kind)
+    Y = b.blockperm(to_dev(A), d, M, kappa, 21, s=s, wiring=kind)
+    sync()
+    assert np.array_equal(Y.cpu().numpy().astype(np.float64), ref)
+
+
+def test_split_slices_and_accumulate():
+    """Few components x tiles: the plan splits input blocks into row slices
+    (the page's split-B_c) and the fixed-order reduce sums them; with
+    SK_ACCUMULATE the result adds onto Y."""
+    m, n, d, M, kappa = 1 << 16, 64, 1024, 64, 4
+    p = b.sk_blockperm_plan_describe(m, n, d, M, kappa, 1, b.SK_WIRING_SHIFT, 5, **MI355X)
+    assert p["general"] == 1 and p["Q"] > 1
+    A = inputs.integer_matrix(m, n, -4, 4, seed=6)
+    Ad = to_dev(A)
+    ref = oracle.blockperm_f64(A, d, M, kappa, 1, 5)
+    Y = torch.full((d, n), 2.0, dtype=torch.float32, device=dev())
+    b.blockperm(Ad, d, M, kappa, 5, out=Y, flags=b.SK_ACCUMULATE)
+    sync()
+    assert np.array_equal(Y.cpu().numpy().astype(np.float64), ref + 2.0)
+
+
+def test_component_kernel_direct_small():
+    """sk_apply_blockperm always takes the component kernel; on a small
+    shape it must agree with the general kernel and the oracle exactly."""
+    m, n, d, M, kappa = 4096, 64, 256, 16, 4
+    A = inputs.integer_matrix(m, n, -8, 8, seed=2)
+    Ad = to_dev(A)
+    Y1 = torch.empty((d, n), dtype=torch.float32, device=dev())
+    b.sk_apply_blockperm(Ad, m, n, n, d, M, kappa, 1, 31, Y1, n)
+    Y2 = b.blockperm(Ad, d, M, kappa, 31)
+    sync()
+    ref = oracle.blockperm_f64(A, d, M, kappa, 1, 31)
+    assert np.array_equal(Y1.cpu().numpy().astype(np.float64), ref)
+    assert torch.equal(Y1, Y2)
