@@ -66,6 +66,11 @@ typedef enum sk_status {
 #define SK_WIRING_SHIFT  0
 #define SK_WIRING_AFFINE 1
 
+/* BlockPerm kernels, as sk_blockperm_plan_describe reports them */
+#define SK_BLOCKPERM_KERNEL_COMPONENT 0  /* LDS tiles per component, no workspace */
+#define SK_BLOCKPERM_KERNEL_SLICE     1  /* LDS tiles per (input block, row slice) */
+#define SK_BLOCKPERM_KERNEL_REGISTER  2  /* partial rows in registers */
+
 /* format and convert arguments of sk_apply_lowp */
 #define SK_FORMAT_F16  0
 #define SK_FORMAT_BF16 1
@@ -346,17 +351,25 @@ sk_status sk_apply_blockperm(const float *A, int64_t m, int32_t n, int64_t lda,
  *           is set.  Each nonzero is +-1/sqrt(kappa*s).
  *   kappa   <= 32.
  *   workspace, workspace_bytes
- *           device scratch (4-byte aligned, disjoint from A and Y) of
- *           sk_blockperm_workspace_size bytes; NULL is accepted when that
- *           size is 0 (the shift/s = 1 kernel with enough components runs,
- *           as sk_apply_blockperm).  Otherwise a kernel per (input block,
- *           row slice, 32-column tile) writes kappa partial tiles once, and
- *           a second kernel writes each Y element once as their sum in a
- *           fixed order (neighbour, then slice): no atomics.
+ *           device scratch (16-byte aligned, disjoint from A and Y) of
+ *           sk_blockperm_workspace_size bytes.  A kernel per (input block h,
+ *           row slice, column slice) writes the kappa*B_r partial rows of h
+ *           (its kappa readers' blocks) once, and a second kernel writes each
+ *           Y element once as their sum in a fixed order (neighbour, then
+ *           slice): no atomics, deterministic.  The partials are kept in
+ *           registers (SK_BLOCKPERM_KERNEL_REGISTER) when n % 4 == 0,
+ *           lda % 4 == 0, A is 16-byte aligned and kappa*B_r is 16 R G for
+ *           some R in {1, 2, 4, 8, 16} dividing B_r and G <= 8; otherwise in
+ *           LDS tiles of 32 columns (SK_BLOCKPERM_KERNEL_SLICE, kappa*B_r up
+ *           to what one wavefront tile of LDS holds).  NULL is accepted where
+ *           sk_apply_blockperm's component kernel applies (shift wiring,
+ *           s = 1, kappa in {1, 2, 4, 8}): that kernel then runs.
  *   flags   SK_ACCUMULATE only.
  * Errors: as sk_apply_blockperm, plus SK_ERR_ARG (unknown wiring, small
- * workspace), SK_ERR_NULL (missing workspace), SK_ERR_UNSUPPORTED (s or
- * kappa above 32, s > 1 with B_r not a power of two, tiles too large for LDS).
+ * workspace), SK_ERR_NULL (missing workspace), SK_ERR_ALIGN (workspace not
+ * 16-byte aligned; A or lda unaligned where only the register kernel fits),
+ * SK_ERR_UNSUPPORTED (s or kappa above 32, s > 1 with B_r not a power of
+ * two, partial rows that neither kernel holds).
  */
 sk_status sk_apply_blockperm_ex(const float *A, int64_t m, int32_t n, int64_t lda, int32_t d,
                                 int32_t M, int32_t kappa, int32_t s, int32_t wiring,
@@ -365,18 +378,22 @@ sk_status sk_apply_blockperm_ex(const float *A, int64_t m, int32_t n, int64_t ld
 
 /*
  * sk_blockperm_workspace_size: workspace bytes sk_apply_blockperm_ex needs
- * for these sizes on the current device (0: none).
+ * for these sizes on the current device, whatever A's alignment (the
+ * larger of the register and slice kernels' needs where both apply).
  */
 sk_status sk_blockperm_workspace_size(int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa,
                                       int32_t s, int32_t wiring, size_t *bytes);
 
 /*
- * sk_blockperm_plan_describe: sk_apply_blockperm_ex's plan, computed on the
- * host (no HIP call): out int64[SK_BLOCKPERM_PLAN_FIELDS] = {general kernel
- * used, row slices Q, rows per slice, workspace bytes, affine a, affine b,
- * a^-1 mod M} (a, b, a^-1 are 0 for the shift wiring).
+ * sk_blockperm_plan_describe: sk_apply_blockperm_ex's plan for A with
+ * lda = n and a 16-byte aligned base, computed on the host (no HIP call):
+ * out int64[SK_BLOCKPERM_PLAN_FIELDS] = {kernel (SK_BLOCKPERM_KERNEL_*), row
+ * slices Q, rows per slice, workspace bytes, affine a, affine b, a^-1 mod M,
+ * partial rows per wavefront R, row groups G, column slices} (a, b, a^-1 are
+ * 0 for the shift wiring; R, G and column slices 0 unless the register
+ * kernel runs).
  */
-#define SK_BLOCKPERM_PLAN_FIELDS 7
+#define SK_BLOCKPERM_PLAN_FIELDS 10
 sk_status sk_blockperm_plan_describe(int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa,
                                      int32_t s, int32_t wiring, uint64_t seed, int32_t num_cu,
                                      int32_t max_lds, int64_t *out);

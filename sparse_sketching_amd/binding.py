@@ -30,6 +30,9 @@ SK_CONVERT_RN = 0
 SK_CONVERT_SR = 1
 SK_WIRING_SHIFT = 0
 SK_WIRING_AFFINE = 1
+SK_BLOCKPERM_KERNEL_COMPONENT = 0
+SK_BLOCKPERM_KERNEL_SLICE = 1
+SK_BLOCKPERM_KERNEL_REGISTER = 2
 
 _c = ctypes
 _SIGNATURES = {
@@ -212,7 +215,8 @@ def sk_blockperm_workspace_size(m, n, d, M, kappa, s, wiring):
     return out.value
 
 
-BLOCKPERM_PLAN_FIELDS = ("general", "Q", "rows_per_slice", "ws_bytes", "a", "b", "ainv")
+BLOCKPERM_PLAN_FIELDS = ("kernel", "Q", "rows_per_slice", "ws_bytes", "a", "b", "ainv",
+                         "rows_per_wave", "groups", "slices")
 
 
 def sk_blockperm_plan_describe(m, n, d, M, kappa, s, wiring, seed, num_cu, max_lds):

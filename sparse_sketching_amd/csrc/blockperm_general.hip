@@ -24,6 +24,7 @@
 #include "sk_internal.hpp"
 #include "sk_apply_common.hpp"
 #include "sk_rng.hpp"
+#include "sk_blockperm.hpp"
 
 namespace sk {
 namespace {
@@ -31,27 +32,6 @@ namespace {
 constexpr int kTileG = 32;          // columns per workgroup
 constexpr int kBatchG = 64;         // rows per wavefront batch
 constexpr int kMaxWavesG = 8;
-
-__device__ __forceinline__ uint32_t mod_mul(uint32_t x, uint32_t y, uint32_t M) {
-    return (uint32_t)(((uint64_t)x * y) % M);
-}
-
-// The l-th reader of input block h (0 <= l < kappa): the output block g
-// whose l-th neighbour is h.
-__device__ __forceinline__ uint32_t reader(const BlockPermGenArgs &a, const BlockPermTable &ginv,
-                                           uint32_t h, int l) {
-    if (a.wiring == 0) {
-        // shift: pi_l(g) = (sigma(g) + l C) mod M, so g = sigma^-1(h - l C)
-        const uint32_t M = (uint32_t)a.M;
-        const uint32_t x = (h + M - (uint32_t)((int64_t)l * a.C % M)) % M;
-        return ginv.tab[x];
-    }
-    // affine: pi_l = f^(l+1), so g = f^-(l+1)(h), f^-1(x) = a^-1 (x - b)
-    uint32_t x = h;
-    for (int i = 0; i <= l; ++i) x = mod_mul(a.ainv, (x + (uint32_t)a.M - a.b) % (uint32_t)a.M,
-                                             (uint32_t)a.M);
-    return x;
-}
 
 __global__ __launch_bounds__(kMaxWavesG * 64) void k_bp_general(const BlockPermGenArgs args,
                                                                  const BlockPermTable ginv) {
@@ -77,7 +57,7 @@ __global__ __launch_bounds__(kMaxWavesG * 64) void k_bp_general(const BlockPermG
 
     for (int k = threadIdx.x; k < nw * trows * 64; k += nthr) acc[k] = 0.f;
     if (threadIdx.x < kappa)
-        keys[threadIdx.x] = blockperm_key(args.seed, reader(args, ginv, h, threadIdx.x), h);
+        keys[threadIdx.x] = blockperm_key(args.seed, bp_reader(args, ginv, h, threadIdx.x), h);
     __syncthreads();
 
     const float scale = args.scale;
@@ -203,6 +183,11 @@ hipError_t launch_blockperm_general(const BlockPermGenArgs &args, const BlockPer
     kern<<<grid, dim3(nw * 64), lds, s>>>(args, ginv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return launch_bp_reduce(args, fwd, Y, ldy, accumulate, s);
+}
+
+hipError_t launch_bp_reduce(const BlockPermGenArgs &args, const BlockPermTable &fwd, float *Y,
+                            int64_t ldy, int accumulate, hipStream_t s) {
     const int64_t total = (int64_t)args.M * args.Br * args.n;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65535) blocks = 65535;

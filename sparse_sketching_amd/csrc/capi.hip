@@ -282,13 +282,21 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
                           w + 2 * meta, workspace_bytes - 2 * meta, s);
 }
 
-// BlockPerm launch plan: the component kernel (shift wiring, s = 1, kappa
-// in {1, 2, 4, 8}, enough components x tiles to fill the device) or the
-// general kernel with Q row slices and a workspace of Q*kappa*d*n floats.
+// BlockPerm launch plan: the register kernel where its shape rules hold;
+// else the component kernel (shift wiring, s = 1, kappa in {1, 2, 4, 8},
+// enough components x tiles to fill the device); else the slice kernel with
+// Qs row slices.  The register and slice kernels take a workspace of
+// Q*kappa*d*n floats for their own Q; where the register kernel is planned
+// the slice kernel stays the fallback for an unaligned A, so the workspace
+// covers both.
 struct BpPlan {
-    bool general;
-    int32_t Q;
-    int64_t rows_per_slice;
+    int kernel;                 // SK_BLOCKPERM_KERNEL_*
+    bool comp_ok;               // the component kernel applies (NULL workspace)
+    bool slice_ok;
+    int32_t Qs;                 // slice kernel: row slices, rows per slice
+    int64_t rps_s;
+    size_t ws_s;
+    sk::BpRegsPlan regs;        // register kernel (kernel == REGISTER)
     size_t ws_bytes;
     uint32_t a, ainv, b;        // affine wiring parameters
 };
@@ -368,20 +376,31 @@ bool plan_blockperm(const sk::DevInfo &di, int64_t m, int32_t n, int32_t d, int3
     const int64_t Bc = m / M;
     const int64_t tiles = (n + 31) / 32;
     memset(p, 0, sizeof(*p));
-    const bool comp_ok = wiring == SK_WIRING_SHIFT && s == 1 &&
-                         (kappa == 1 || kappa == 2 || kappa == 4 || kappa == 8) &&
-                         (int64_t)kappa * Br <= sk::blockperm_max_rows(di);
-    if (comp_ok && tiles * (M / kappa) >= di.num_cu) return true;
-    if ((int64_t)kappa * Br > sk::blockperm_general_max_rows(di)) return false;
-    p->general = true;
-    int64_t Q = (2 * (int64_t)di.num_cu + tiles * M - 1) / (tiles * M);
-    const int64_t qmax = Bc / 64 > 1 ? Bc / 64 : 1;
-    if (Q > qmax) Q = qmax;
-    if (Q < 1) Q = 1;
-    if (Q * M > 65535) Q = 65535 / M;
-    p->Q = (int32_t)Q;
-    p->rows_per_slice = (Bc + Q - 1) / Q;
-    p->ws_bytes = (size_t)Q * (size_t)kappa * (size_t)d * (size_t)n * 4;
+    p->comp_ok = wiring == SK_WIRING_SHIFT && s == 1 &&
+                 (kappa == 1 || kappa == 2 || kappa == 4 || kappa == 8) &&
+                 (int64_t)kappa * Br <= sk::blockperm_max_rows(di);
+    p->slice_ok = (int64_t)kappa * Br <= sk::blockperm_general_max_rows(di);
+    if (p->slice_ok) {
+        int64_t Q = (2 * (int64_t)di.num_cu + tiles * M - 1) / (tiles * M);
+        const int64_t qmax = Bc / 64 > 1 ? Bc / 64 : 1;
+        if (Q > qmax) Q = qmax;
+        if (Q < 1) Q = 1;
+        if (Q * M > 65535) Q = 65535 / M;
+        p->Qs = (int32_t)Q;
+        p->rps_s = (Bc + Q - 1) / Q;
+        p->ws_s = (size_t)Q * (size_t)kappa * (size_t)d * (size_t)n * 4;
+    }
+    if (sk::plan_bp_regs(di, m, n, d, M, kappa, s, &p->regs)) {
+        p->kernel = SK_BLOCKPERM_KERNEL_REGISTER;
+        p->ws_bytes = p->regs.ws_bytes > p->ws_s ? p->regs.ws_bytes : p->ws_s;
+    } else if (p->comp_ok && tiles * (M / kappa) >= di.num_cu) {
+        p->kernel = SK_BLOCKPERM_KERNEL_COMPONENT;
+    } else if (p->slice_ok) {
+        p->kernel = SK_BLOCKPERM_KERNEL_SLICE;
+        p->ws_bytes = p->ws_s;
+    } else {
+        return false;
+    }
     if (wiring == SK_WIRING_AFFINE) affine_params(seed, M, &p->a, &p->b, &p->ainv);
     return true;
 }
@@ -595,27 +614,30 @@ sk_status sk_apply_blockperm_ex(const float *A, int64_t m, int32_t n, int64_t ld
     if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
     BpPlan p;
     if (!plan_blockperm(di, m, n, d, M, kappa, s, wiring, seed, &p)) return SK_ERR_UNSUPPORTED;
-    if (!p.general)
+    if (p.kernel == SK_BLOCKPERM_KERNEL_COMPONENT || (workspace == nullptr && p.comp_ok))
         return sk_apply_blockperm(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags, stream);
     if (workspace == nullptr) return SK_ERR_NULL;
-    if ((uintptr_t)workspace % 4 != 0) return SK_ERR_ALIGN;
+    if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
     if (workspace_bytes < p.ws_bytes) return SK_ERR_ARG;
     if (overlaps(workspace, workspace_bytes, A, aspan) ||
         overlaps(workspace, workspace_bytes, Y, yspan))
         return SK_ERR_ARG;
+    const bool regs = p.kernel == SK_BLOCKPERM_KERNEL_REGISTER && lda % 4 == 0 &&
+                      (uintptr_t)A % 16 == 0;
+    if (!regs && !p.slice_ok) return SK_ERR_ALIGN;
     sk::BlockPermGenArgs g;
     memset(&g, 0, sizeof(g));
     g.A = A;
     g.ws = static_cast<float *>(workspace);
     g.lda = lda;
     g.Bc = m / M;
-    g.rows_per_slice = p.rows_per_slice;
+    g.rows_per_slice = regs ? p.regs.rows_per_slice : p.rps_s;
     g.n = n;
     g.Br = d / M;
     g.M = M;
     g.kappa = kappa;
     g.s = s;
-    g.Q = p.Q;
+    g.Q = regs ? p.regs.Q : p.Qs;
     g.wiring = wiring;
     g.C = wiring == SK_WIRING_SHIFT ? M / kappa : 0;
     g.a = p.a;
@@ -623,6 +645,8 @@ sk_status sk_apply_blockperm_ex(const float *A, int64_t m, int32_t n, int64_t ld
     g.b = p.b;
     g.scale = scale_of((int64_t)kappa * s);
     g.seed = seed;
+    g.slices = regs ? p.regs.slices : 0;
+    g.groups = regs ? p.regs.groups : 0;
     sk::BlockPermTable ginv, fwd;
     memset(&ginv, 0, sizeof(ginv));
     memset(&fwd, 0, sizeof(fwd));
@@ -630,8 +654,11 @@ sk_status sk_apply_blockperm_ex(const float *A, int64_t m, int32_t n, int64_t ld
         sigma_table(seed, M, fwd.tab);
         for (int k = 0; k < M; ++k) ginv.tab[fwd.tab[k]] = (uint16_t)k;
     }
-    return hip_status(sk::launch_blockperm_general(g, ginv, fwd, Y, ldy,
-                                                   (flags & SK_ACCUMULATE) ? 1 : 0,
+    const int acc = (flags & SK_ACCUMULATE) ? 1 : 0;
+    if (regs)
+        return hip_status(sk::launch_bp_regs(p.regs, g, ginv, fwd, Y, ldy, acc,
+                                             (hipStream_t)stream));
+    return hip_status(sk::launch_blockperm_general(g, ginv, fwd, Y, ldy, acc,
                                                    (hipStream_t)stream));
 }
 
@@ -660,8 +687,13 @@ sk_status sk_blockperm_plan_describe(int64_t m, int32_t n, int32_t d, int32_t M,
     sk::DevInfo di{num_cu, max_lds};
     BpPlan p;
     if (!plan_blockperm(di, m, n, d, M, kappa, s, wiring, seed, &p)) return SK_ERR_UNSUPPORTED;
-    const int64_t v[SK_BLOCKPERM_PLAN_FIELDS] = {p.general ? 1 : 0, p.Q, p.rows_per_slice,
-                                                 (int64_t)p.ws_bytes, p.a, p.b, p.ainv};
+    const bool regs = p.kernel == SK_BLOCKPERM_KERNEL_REGISTER;
+    const bool comp = p.kernel == SK_BLOCKPERM_KERNEL_COMPONENT;
+    const int64_t v[SK_BLOCKPERM_PLAN_FIELDS] = {
+        p.kernel, regs ? p.regs.Q : (comp ? 0 : p.Qs),
+        regs ? p.regs.rows_per_slice : (comp ? 0 : p.rps_s), (int64_t)p.ws_bytes, p.a, p.b,
+        p.ainv, regs ? p.regs.rows_per_wave : 0, regs ? p.regs.groups : 0,
+        regs ? p.regs.slices : 0};
     for (int i = 0; i < SK_BLOCKPERM_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }

@@ -139,6 +139,7 @@ struct BlockPermGenArgs {
     uint32_t a, ainv, b;        // affine: f(x) = (a x + b) mod M, a^-1 mod M
     float scale;                // float32(1/sqrt(kappa*s))
     uint64_t seed;
+    int32_t slices, groups;     // register kernel: column slices, row groups
 };
 int blockperm_general_max_rows(const DevInfo &di);
 // ginv: shift wiring's sigma^-1 (readers); fwd: its sigma (neighbours).
@@ -146,5 +147,33 @@ hipError_t launch_blockperm_general(const BlockPermGenArgs &args, const BlockPer
                                     const BlockPermTable &fwd, float *Y, int64_t ldy,
                                     int accumulate, hipStream_t stream);
 hipError_t launch_blockperm(const BlockPermArgs &args, int32_t kappa, hipStream_t stream);
+// Y (=|+=) the fixed-order sum of the [M][Q][kappa][B_r][n] partials.
+hipError_t launch_bp_reduce(const BlockPermGenArgs &args, const BlockPermTable &fwd, float *Y,
+                            int64_t ldy, int accumulate, hipStream_t stream);
+
+// Register BlockPerm apply (blockperm_regs.hip): a workgroup per (input
+// block, row slice, 256-column slice, row group) keeps its share of the
+// kappa*B_r partial rows in registers, rows streaming through LDS stages.
+constexpr int kBpRegsCols = 256;            // columns per slice (64 lanes x 4)
+constexpr int kBpRegsStage = 64;            // input rows per LDS stage
+constexpr int kBpRegsLdsBytes = 2 * kBpRegsStage * kBpRegsCols * 4 +
+                                2 * kBlockPermGenMaxKappa * kBpRegsStage * 4 +
+                                kBlockPermGenMaxKappa * 4;
+struct BpRegsPlan {
+    int32_t rows_per_wave;      // R: partial rows a wavefront keeps
+    int32_t groups;             // G: row groups (16 R G = kappa B_r)
+    int32_t slices;             // column slices of 256
+    int32_t Q;                  // row slices per input block
+    int64_t rows_per_slice;     // a multiple of the stage (the last may be short)
+    int64_t grid;               // workgroups
+    size_t ws_bytes;            // partials: Q kappa d n floats
+};
+// Shape eligibility and plan; A must also have lda % 4 == 0 and a 16-byte
+// aligned base (checked by the caller).
+bool plan_bp_regs(const DevInfo &di, int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa,
+                  int32_t s, BpRegsPlan *p);
+hipError_t launch_bp_regs(const BpRegsPlan &p, const BlockPermGenArgs &args,
+                          const BlockPermTable &ginv, const BlockPermTable &fwd, float *Y,
+                          int64_t ldy, int accumulate, hipStream_t stream);
 
 }  // namespace sk

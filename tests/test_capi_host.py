@@ -368,32 +368,70 @@ def test_blockperm_affine_params_match_oracle(M, seed):
     p = b.sk_blockperm_plan_describe(M * 64, 32, M * 4, M, 1, 1, b.SK_WIRING_AFFINE, seed,
                                      num_cu=256, max_lds=160 * 1024)
     a, bb = oracle.affine_params(seed, M)
-    assert p["general"] == 1 and (p["a"], p["b"]) == (a % max(M, 1) if M > 1 else 1, bb)
+    assert p["kernel"] == b.SK_BLOCKPERM_KERNEL_SLICE
+    assert (p["a"], p["b"]) == (a % max(M, 1) if M > 1 else 1, bb)
     if M > 1:
         assert (p["a"] * p["ainv"]) % M == 1
 
 
-@pytest.mark.parametrize("m,n,d,M,kappa,s,wiring", [
-    (1 << 21, 512, 1024, 64, 4, 1, 0),      # the bench workload: component kernel
-    (1 << 21, 512, 1024, 64, 4, 2, 0),      # s > 1: general kernel
-    (1 << 21, 512, 1024, 64, 4, 1, 1),      # affine wiring
-    (1 << 16, 64, 1024, 64, 4, 1, 0),       # few components: split slices
-    (4096, 32, 256, 16, 5, 3, 1),
+@pytest.mark.parametrize("m,n,d,M,kappa,s,wiring,kernel,R,G", [
+    (1 << 21, 512, 1024, 64, 4, 1, 0, 2, 4, 1),     # the bench workload
+    (1 << 21, 512, 1024, 64, 4, 2, 0, 2, 4, 1),     # s > 1
+    (1 << 21, 512, 1024, 64, 4, 1, 1, 2, 4, 1),     # affine wiring
+    (1 << 16, 64, 1024, 64, 4, 1, 0, 2, 4, 1),      # few workgroups: row slices
+    (1 << 16, 300, 1024, 64, 32, 1, 1, 2, 16, 2),   # kappa*B_r = 512: two row groups
+    (1 << 16, 300, 4096, 64, 32, 1, 1, 2, 16, 8),   # kappa*B_r = 2048: eight
+    (1 << 12, 8, 64, 8, 2, 1, 0, 2, 1, 1),          # kappa*B_r = 16: R = 1
+    (4096, 32, 256, 16, 5, 3, 1, 1, 0, 0),          # B_r = 16, kappa*B_r = 80: slice kernel
+    (4096, 30, 256, 16, 4, 1, 1, 1, 0, 0),          # n % 4 != 0: slice kernel
+    (1 << 16, 1022, 1024, 64, 4, 1, 0, 0, 0, 0),    # shift, n % 4 != 0, 32 tiles x 16: component
 ])
-def test_blockperm_plan_bounds(m, n, d, M, kappa, s, wiring):
+def test_blockperm_plan_bounds(m, n, d, M, kappa, s, wiring, kernel, R, G):
     p = b.sk_blockperm_plan_describe(m, n, d, M, kappa, s, wiring, 7, num_cu=256,
                                      max_lds=160 * 1024)
-    Bc = m // M
-    if not p["general"]:
+    Bc, Br = m // M, d // M
+    assert p["kernel"] == kernel
+    if kernel == b.SK_BLOCKPERM_KERNEL_COMPONENT:
         assert wiring == 0 and s == 1 and p["ws_bytes"] == 0
         return
     Q, rps = p["Q"], p["rows_per_slice"]
     assert Q >= 1 and rps * Q >= Bc > rps * (Q - 1)
-    assert Q * M <= 65535
-    assert p["ws_bytes"] == Q * kappa * d * n * 4
-    # the largest partial index the scatter kernel writes stays inside it
-    last = ((((M - 1) * Q + Q - 1) * kappa + kappa - 1) * (d // M) + d // M - 1) * n + n - 1
+    assert p["ws_bytes"] >= Q * kappa * d * n * 4
+    # the largest partial index either kernel writes stays inside it
+    last = ((((M - 1) * Q + Q - 1) * kappa + kappa - 1) * Br + Br - 1) * n + n - 1
     assert (last + 1) * 4 <= p["ws_bytes"]
+    if kernel == b.SK_BLOCKPERM_KERNEL_SLICE:
+        assert Q * M <= 65535 and p["rows_per_wave"] == 0
+        return
+    # register kernel: 16 wavefronts x R rows x G groups cover kappa*B_r,
+    # a wavefront's rows inside one reader's block, whole stages per slice
+    assert (p["rows_per_wave"], p["groups"]) == (R, G)
+    assert 16 * R * G == kappa * Br and Br % R == 0 and rps % 64 == 0
+    assert p["slices"] * 256 >= n > (p["slices"] - 1) * 256
+
+
+def test_blockperm_register_grid_covers_every_unit_once():
+    """Replays the kernel's workgroup -> (unit, row group) mapping on the
+    host: every (input block, row slice, column slice, group) is owned by
+    exactly one workgroup and the rest of the grid exits."""
+    for (m, n, d, M, kappa) in [(1 << 21, 512, 1024, 64, 4), (1 << 16, 300, 4096, 64, 32),
+                                (1 << 12, 8, 64, 8, 2), (3 * 1000, 520, 3 * 16, 3, 2)]:
+        p = b.sk_blockperm_plan_describe(m, n, d, M, kappa, 1, 1, 7, num_cu=256,
+                                         max_lds=160 * 1024)
+        assert p["kernel"] == b.SK_BLOCKPERM_KERNEL_REGISTER
+        G, Q, slices = p["groups"], p["Q"], p["slices"]
+        units = M * Q * slices
+        grid = (units + 7) // 8 * 8 * G
+        seen = set()
+        for wg in range(grid):
+            qq = wg >> 3
+            unit = (qq // G) * 8 + (wg & 7)
+            if unit >= units:
+                continue
+            key = (unit, qq % G)
+            assert key not in seen
+            seen.add(key)
+        assert len(seen) == units * G
 
 
 @pytest.mark.parametrize("args,expect", [

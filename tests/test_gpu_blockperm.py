@@ -56,16 +56,25 @@ def test_padded_strides():
     assert oracle.rel_frob(Y[:, :n], ref) <= 1e-5
 
 
-def test_full_configuration_sampled_columns():
+@pytest.mark.parametrize("path", ["ex", "component"])
+def test_full_configuration_sampled_columns(path):
     """A 2^21 x 512 N(0,1) (drawn on the device, seeded), d = 1024, M = 64,
-    kappa = 4, s = 1.  Every output row is checked on 24 columns spread over
-    all 16 column tiles, against the fp64 oracle on those columns."""
+    kappa = 4, s = 1, through sk_apply_blockperm_ex (the register kernel,
+    as the benchmark runs it) and sk_apply_blockperm (the component
+    kernel).  Every output row is checked on 24 columns spread over all
+    column slices and tiles, against the fp64 oracle on those columns."""
     m, n, d, M, kappa, seed = 1 << 21, 512, 1024, 64, 4, 1
-    say("blockperm full configuration")
+    say(f"blockperm full configuration, {path}")
     Ad = inputs.gaussian_torch(m, n, seed=0)
-    Y = b.blockperm(Ad, d, M, kappa, seed)
+    if path == "ex":
+        assert _plan(m, n, d, M, kappa, 1, "shift", seed)["kernel"] == \
+            b.SK_BLOCKPERM_KERNEL_REGISTER
+        Y = b.blockperm(Ad, d, M, kappa, seed)
+    else:
+        Y = torch.empty((d, n), dtype=torch.float32, device=Ad.device)
+        b.sk_apply_blockperm(Ad, m, n, n, d, M, kappa, 1, seed, Y, n)
     sync()
-    cols = np.unique(np.concatenate([np.arange(0, n, 23), [1, 31, 32, 255, 480, 511]]))
+    cols = np.unique(np.concatenate([np.arange(0, n, 23), [1, 31, 32, 255, 256, 480, 511]]))
     A_cols = Ad[:, torch.from_numpy(cols).to(Ad.device)].cpu().numpy()
     ref = oracle.blockperm_f64(A_cols, d, M, kappa, 1, seed)
     got = Y.cpu().numpy()[:, cols]
@@ -117,7 +126,7 @@ def test_split_slices_and_accumulate():
     SK_ACCUMULATE the result adds onto Y."""
     m, n, d, M, kappa = 1 << 16, 64, 1024, 64, 4
     p = b.sk_blockperm_plan_describe(m, n, d, M, kappa, 1, b.SK_WIRING_SHIFT, 5, **MI355X)
-    assert p["general"] == 1 and p["Q"] > 1
+    assert p["kernel"] != b.SK_BLOCKPERM_KERNEL_COMPONENT and p["Q"] > 1
     A = inputs.integer_matrix(m, n, -4, 4, seed=6)
     Ad = to_dev(A)
     ref = oracle.blockperm_f64(A, d, M, kappa, 1, 5)
@@ -140,3 +149,89 @@ def test_component_kernel_direct_small():
     ref = oracle.blockperm_f64(A, d, M, kappa, 1, 31)
     assert np.array_equal(Y1.cpu().numpy().astype(np.float64), ref)
     assert torch.equal(Y1, Y2)
+
+
+# ------------------------------------------------------- register kernel
+
+def _plan(m, n, d, M, kappa, s, kind, seed):
+    w = b.SK_WIRING_SHIFT if kind == "shift" else b.SK_WIRING_AFFINE
+    return b.sk_blockperm_plan_describe(m, n, d, M, kappa, s, w, seed, **MI355X)
+
+
+@pytest.mark.parametrize("kind,m,n,d,M,kappa,s,R,G", [
+    ("shift", 8 * 1000, 8, 64, 8, 2, 1, 1, 1),       # R = 1; B_c = 1000: a short last stage
+    ("affine", 8 * 640, 36, 64, 8, 4, 1, 2, 1),      # R = 2; 36 of 256 columns
+    ("shift", 16 * 512, 300, 256, 16, 4, 1, 4, 1),   # R = 4; two column slices, ragged
+    ("affine", 16 * 512, 64, 256, 16, 8, 2, 8, 1),   # R = 8; s = 2
+    ("shift", 16 * 256, 520, 256, 16, 16, 1, 16, 1), # R = 16; three column slices
+    ("affine", 32 * 256, 32, 512, 32, 32, 4, 16, 2), # two row groups; s = 4
+    ("affine", 32 * 128, 16, 2048, 32, 32, 1, 16, 8),# eight row groups (B_r = 64)
+    ("shift", 64 * 461, 512, 1024, 64, 4, 1, 4, 1),  # row slices of 4 stages, the last 13 rows short
+])
+def test_register_kernel_vs_oracle(kind, m, n, d, M, kappa, s, R, G):
+    """Every built rows-per-wavefront R, row groups, s > 1, both wirings,
+    ragged column slices and short last stages, against the fp64 oracle;
+    the plan must pick the register kernel with the expected R and G."""
+    seed = 11
+    p = _plan(m, n, d, M, kappa, s, kind, seed)
+    say(f"blockperm register {kind} m={m} n={n} d={d} M={M} kappa={kappa} s={s} plan={p}")
+    assert p["kernel"] == b.SK_BLOCKPERM_KERNEL_REGISTER
+    assert (p["rows_per_wave"], p["groups"]) == (R, G)
+    A = inputs.gaussian(m, n, seed=4)
+    Y = b.blockperm(to_dev(A), d, M, kappa, seed, s=s, wiring=kind)
+    sync()
+    ref = oracle.blockperm_f64(A, d, M, kappa, s, seed, kind)
+    assert oracle.rel_frob(Y.cpu().numpy(), ref) <= 1e-5
+
+
+def test_register_kernel_dense_brute_force():
+    """A tiny register-kernel case against the dense S the oracle builds
+    entry by entry (not the block-wise apply)."""
+    m, n, d, M, kappa, s, seed = 16 * 100, 12, 256, 16, 4, 2, 3
+    assert _plan(m, n, d, M, kappa, s, "affine", seed)["kernel"] == b.SK_BLOCKPERM_KERNEL_REGISTER
+    A = inputs.gaussian(m, n, seed=8)
+    Y = b.blockperm(to_dev(A), d, M, kappa, seed, s=s, wiring="affine")
+    sync()
+    ref = oracle.blockperm_dense_S(m, d, M, kappa, s, seed, "affine") @ A.astype(np.float64)
+    assert oracle.rel_frob(Y.cpu().numpy(), ref) <= 1e-5
+
+
+def test_register_kernel_deterministic_and_accumulate():
+    """Fixed summation order: two runs agree bit for bit; integer inputs
+    with kappa*s = 4 (scale 1/2) are exact, and SK_ACCUMULATE adds."""
+    m, n, d, M, kappa = 16 * 2048, 264, 512, 16, 4
+    A = inputs.integer_matrix(m, n, -8, 8, seed=5)
+    Ad = to_dev(A)
+    assert _plan(m, n, d, M, kappa, 1, "shift", 9)["kernel"] == b.SK_BLOCKPERM_KERNEL_REGISTER
+    Y1 = b.blockperm(Ad, d, M, kappa, 9)
+    Y2 = b.blockperm(Ad, d, M, kappa, 9)
+    sync()
+    assert torch.equal(Y1, Y2)
+    ref = oracle.blockperm_f64(A, d, M, kappa, 1, 9)
+    assert np.array_equal(Y1.cpu().numpy().astype(np.float64), ref)
+    b.blockperm(Ad, d, M, kappa, 9, out=Y1, flags=b.SK_ACCUMULATE)
+    sync()
+    assert np.array_equal(Y1.cpu().numpy().astype(np.float64), 2 * ref)
+
+
+@pytest.mark.parametrize("how", ["lda", "base"])
+def test_register_shape_with_unaligned_A_uses_slice_kernel(how):
+    """A shape the register kernel takes, but A's row stride (lda % 4 != 0)
+    or base address (4 bytes past a 16-byte boundary) rules out its float4
+    loads: the call falls back to the slice kernel, same result."""
+    m, n, d, M, kappa, seed = 4096, 64, 256, 16, 4, 6
+    assert _plan(m, n, d, M, kappa, 1, "affine", seed)["kernel"] == b.SK_BLOCKPERM_KERNEL_REGISTER
+    A = inputs.gaussian(m, n, seed=7)
+    if how == "lda":
+        buf = torch.zeros((m, n + 2), dtype=torch.float32, device=dev())
+        buf[:, :n] = to_dev(A)
+        Ad = buf[:, :n]
+    else:
+        flat = torch.zeros(m * n + 1, dtype=torch.float32, device=dev())
+        flat[1:] = to_dev(A).reshape(-1)
+        Ad = flat[1:].view(m, n)
+        assert Ad.data_ptr() % 16 == 4
+    Y = b.blockperm(Ad, d, M, kappa, seed, wiring="affine")
+    sync()
+    ref = oracle.blockperm_f64(A, d, M, kappa, 1, seed, "affine")
+    assert oracle.rel_frob(Y.cpu().numpy(), ref) <= 1e-5
