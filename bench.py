@@ -43,7 +43,7 @@ SEED = 1
 # dispatch; FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a 1 GiB device
 # copy reads on the same counters).  Valid for the kernels named here only.
 TRAFFIC = {"kernels": ("k_stack_fused<AccF16,32,1>", "k_stack_reduce<AccF16>"),
-           "fetch_kib": (524_567, 32_801), "write_kib": (65_536, 256),
+           "fetch_kib": (524_481, 32_798), "write_kib": (65_536, 256),
            "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-blockperm", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
-                    help="few fixed launches of the dominant kernel and a 1 GiB copy, no JSON")
+                    help="few fixed launches of the dominant kernels and a 1 GiB copy, no JSON")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -174,9 +174,18 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)                          # 1 GiB read + 1 GiB write
+        del src, dst
+        Abp = inputs.gaussian_torch(BP_M, BP_N, seed=0)
+        Y = torch.empty((BP_D, BP_N), dtype=torch.float32, device=dev)
+        wsbp = torch.empty(b.sk_blockperm_workspace_size(BP_M, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, 1,
+                                                         b.SK_WIRING_SHIFT),
+                           dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            b.sk_apply_blockperm_ex(Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, 1,
+                                    b.SK_WIRING_SHIFT, SEED, Y, BP_N, 0, wsbp, wsbp.numel(), sp)
         torch.cuda.synchronize()
         print("profile pass done: 3 x fused f16 sketch, 3 x f16 LDS apply + reduce, "
-              "3 x 1 GiB copy", flush=True)
+              "3 x 1 GiB copy, 3 x BlockPerm (register kernel + reduce)", flush=True)
         return
 
     K, W = args.steps, args.warmup

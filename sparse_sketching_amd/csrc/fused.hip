@@ -27,7 +27,8 @@
 //    wavefront per stage draws the Philox words of the stage's 128 rows
 //    (one row per lane) into LDS.  After one barrier every wavefront scans
 //    the stage's entries of its block with a ballot per owned row and adds
-//    each hit's contribution (sign applied by XOR) to that row's registers.
+//    each hit's contribution to that row's registers as a (packed) FMA by a
+//    scalar +-1 word: exactly the add or subtract.
 //    The next stage's rows are in flight from HBM while a stage is applied.
 //  * The partial is written once to the workspace, and the reduce kernel of
 //    the LDS apply (sk_stack_apply.hpp) sums the chunks in a fixed order
@@ -145,8 +146,12 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
             sg[h] = e & 0x80000000u;
         }
     };
-    // every hit of the scanned stage on this wave's rows [k0, k1)
+    // every hit of the scanned stage on this wave's rows [k0, k1); the sign
+    // is a scalar +-1 word from a ballot of the lanes' signs
     auto process = [&](const uint2 *hs, int k0, int k1) {
+        uint64_t neg[NL];
+#pragma unroll
+        for (int h = 0; h < NL; ++h) neg[h] = __ballot(sg[h] != 0u);
 #pragma unroll
         for (int k = k0; k < k1; ++k) {
 #pragma unroll
@@ -155,10 +160,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
                 while (mk) {
                     const int i = __builtin_ctzll(mk);
                     mk &= mk - 1;
-                    const uint32_t m = T::signmask((uint32_t)__builtin_amdgcn_readlane((int)sg[h], i));
                     const uint2 x = hs[(h * 64 + i) * 64 + lane];
-                    acc[k][0] = T::sum(acc[k][0], x.x ^ m);
-                    acc[k][1] = T::sum(acc[k][1], x.y ^ m);
+                    const uint32_t u = T::unit((uint32_t)(neg[h] >> i) & 1u);
+                    acc[k][0] = T::fma_unit(x.x, u, acc[k][0]);
+                    acc[k][1] = T::fma_unit(x.y, u, acc[k][1]);
                 }
             }
         }

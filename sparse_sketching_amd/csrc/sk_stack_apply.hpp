@@ -64,6 +64,12 @@ struct AccF32 {
     }
     __device__ static uint32_t get(const out_t *B, int64_t off) { return __float_as_uint(B[off]); }
     __device__ static void put(out_t *B, int64_t off, uint32_t w) { B[off] = __uint_as_float(w); }
+    // the word +1 or -1 (b = 1): acc + x*unit is exactly acc + x or acc - x
+    __device__ static uint32_t unit(uint32_t b) { return 0x3F800000u | (b << 31); }
+    __device__ static uint32_t fma_unit(uint32_t x, uint32_t u, uint32_t acc) {
+        return __float_as_uint(__builtin_fmaf(__uint_as_float(x), __uint_as_float(u),
+                                              __uint_as_float(acc)));
+    }
 };
 
 struct AccF16 {
@@ -88,6 +94,14 @@ struct AccF16 {
         return __builtin_bit_cast(uint32_t, B[off]);
     }
     __device__ static void put(out_t *B, int64_t off, uint32_t w) { B[off] = __builtin_bit_cast(h2_t, w); }
+    // the pair (+1, +1) or (-1, -1) (b = 1): a packed FMA by it is exactly the
+    // packed nearest-even add or subtract (the product is exact)
+    __device__ static uint32_t unit(uint32_t b) { return 0x3C003C00u | (b << 31) | (b << 15); }
+    __device__ static uint32_t fma_unit(uint32_t x, uint32_t u, uint32_t acc) {
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(h2_t, x),
+                                                                      __builtin_bit_cast(h2_t, u),
+                                                                      __builtin_bit_cast(h2_t, acc)));
+    }
 };
 
 // K consecutive floats of A, loaded as one vector.
