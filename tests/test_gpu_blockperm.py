@@ -235,3 +235,37 @@ def test_register_shape_with_unaligned_A_uses_slice_kernel(how):
     sync()
     ref = oracle.blockperm_f64(A, d, M, kappa, 1, seed, "affine")
     assert oracle.rel_frob(Y.cpu().numpy(), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("kind,m,n,d,M,kappa,s,R,G", [
+    ("shift", 1024 * 32, 20, 1024, 1024, 32, 1, 1, 2),        # M = 1024 (largest), kappa = 32, B_r = 1
+    ("affine", 16 * 256, 24, 16 * 32, 16, 2, 32, 4, 1),       # s = 32 of B_r = 32
+])
+def test_register_kernel_limits(kind, m, n, d, M, kappa, s, R, G):
+    seed = 13
+    p = _plan(m, n, d, M, kappa, s, kind, seed)
+    say(f"blockperm register limits {kind} M={M} kappa={kappa} s={s} plan={p}")
+    assert p["kernel"] == b.SK_BLOCKPERM_KERNEL_REGISTER
+    assert (p["rows_per_wave"], p["groups"]) == (R, G)
+    A = inputs.gaussian(m, n, seed=6)
+    Y = b.blockperm(to_dev(A), d, M, kappa, seed, s=s, wiring=kind)
+    sync()
+    # the oracle's sparse S over all blocks at once (its per-block apply
+    # rebuilds the wiring for every block: slow at M = 1024)
+    ref = oracle.blockperm_matrix(m, d, M, kappa, s, seed, kind=kind) @ A.astype(np.float64)
+    assert oracle.rel_frob(Y.cpu().numpy(), ref) <= 1e-5
+
+
+def test_register_kernel_padded_strides_accumulate():
+    """lda = 68 and ldy = 72 around n = 64 (lda % 4 == 0 keeps the register
+    kernel): Y's padding is untouched and SK_ACCUMULATE adds onto it."""
+    m, n, d, M, kappa, seed = 16 * 640, 64, 256, 16, 4, 17
+    A = inputs.gaussian(m, 68, seed=9)
+    Ad = to_dev(A)[:, :n]
+    out = torch.full((d, 72), 3.0, device=dev())
+    b.blockperm(Ad, d, M, kappa, seed, out=out[:, :n], flags=b.SK_ACCUMULATE)
+    sync()
+    Y = out.cpu().numpy()
+    assert np.all(Y[:, n:] == 3.0)
+    ref = oracle.blockperm_f64(np.ascontiguousarray(A[:, :n]), d, M, kappa, 1, seed) + 3.0
+    assert oracle.rel_frob(Y[:, :n], ref) <= 1e-5
