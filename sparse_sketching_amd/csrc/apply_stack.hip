@@ -44,11 +44,7 @@ hipError_t launch_stack(const LdsPlan &p, StackApplyArgs &a, int accumulate, hip
     e = hipLaunchKernel(kern, dim3((unsigned)p.grid), dim3(p.threads), params, p.lds_bytes, s);
     if (e != hipSuccess) return e;
     if (a.ws == nullptr) return hipSuccess;
-    const int64_t total = (int64_t)a.d * a.units;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65535) blocks = 65535;
-    k_stack_reduce<T><<<dim3((unsigned)blocks), 256, 0, s>>>(a, a.sp * p.words, accumulate);
-    return hipGetLastError();
+    return launch_stack_reduce<T>(a, a.sp * p.words, accumulate, s);
 }
 
 StackApplyArgs make_args(const LdsPlan &p, const float *A, int64_t m, int32_t units, int64_t lda,

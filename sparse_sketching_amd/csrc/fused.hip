@@ -242,11 +242,7 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
     r.d = fa.d;
     r.chunks = fa.chunks;
     r.slices = fa.slices;
-    const int64_t total = (int64_t)fa.d * units;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65535) blocks = 65535;
-    k_stack_reduce<T><<<dim3((unsigned)blocks), 256, 0, s>>>(r, 128, accumulate);
-    return hipGetLastError();
+    return launch_stack_reduce<T>(r, 128, accumulate, s);
 }
 
 }  // namespace

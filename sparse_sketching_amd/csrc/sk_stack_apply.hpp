@@ -410,35 +410,68 @@ __global__ __launch_bounds__(kStackThreads) void k_stack_apply(const StackApplyA
     }
 }
 
-// B[r, u] (=|+=) sum over chunks p = 0..P-1, in that order, of the workspace
-// partials: one thread per output word, partials read coalesced.
+// B[r, u] (=|+=) the sum over chunks p = 0..P-1 of the workspace partials.
+// A 256-thread block takes 64 output words (one per lane).  Its 4
+// wavefronts each sum a contiguous quarter of the chunks in chunk order,
+// and the non-empty quarter sums are then added in quarter order onto the
+// existing B word (accumulate) or onto zero: a fixed order, so the result
+// is deterministic, with four times the loads in flight of one thread per
+// word.
 template <class T>
 __global__ __launch_bounds__(256) void k_stack_reduce(const StackApplyArgs args, int32_t spw,
                                                        int32_t accumulate) {
+    __shared__ uint32_t part[4][64];
     typename T::out_t *B = reinterpret_cast<typename T::out_t *>(args.B);
     const int64_t total = (int64_t)args.d * args.units;
     const int64_t plane = (int64_t)args.d * spw;
     const int P = args.chunks;
-    for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < total;
-         k += (int64_t)gridDim.x * 256) {
-        const int r = (int)(k / args.units);
-        const int32_t u = (int32_t)(k - (int64_t)r * args.units);
-        const int32_t s = u / spw;
-        const int cl = u - s * spw;
-        const uint32_t *src = args.ws + (int64_t)s * P * plane + (int64_t)r * spw + cl;
-        const int64_t off = (int64_t)r * args.ldb + u;
-        uint32_t acc = accumulate ? T::get(B, off) : 0u;
-        int p = 0;
-        for (; p + 8 <= P; p += 8) {
-            uint32_t w[8];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int p0 = wave * P / 4, p1 = (wave + 1) * P / 4;
+    for (int64_t k0 = (int64_t)blockIdx.x * 64; k0 < total; k0 += (int64_t)gridDim.x * 64) {
+        const int64_t k = k0 + lane;
+        const bool act = k < total;
+        const int r = act ? (int)(k / args.units) : 0;
+        const int32_t u = act ? (int32_t)(k - (int64_t)r * args.units) : 0;
+        uint32_t acc = 0u;
+        if (act) {
+            const int32_t s = u / spw;
+            const int cl = u - s * spw;
+            const uint32_t *src = args.ws + (int64_t)s * P * plane + (int64_t)r * spw + cl;
+            int p = p0;
+            for (; p + 8 <= p1; p += 8) {
+                uint32_t w[8];
 #pragma unroll
-            for (int qq = 0; qq < 8; ++qq) w[qq] = src[(int64_t)(p + qq) * plane];
+                for (int qq = 0; qq < 8; ++qq) w[qq] = src[(int64_t)(p + qq) * plane];
 #pragma unroll
-            for (int qq = 0; qq < 8; ++qq) acc = T::sum(acc, w[qq]);
+                for (int qq = 0; qq < 8; ++qq) acc = T::sum(acc, w[qq]);
+            }
+            for (; p < p1; ++p) acc = T::sum(acc, src[(int64_t)p * plane]);
         }
-        for (; p < P; ++p) acc = T::sum(acc, src[(int64_t)p * plane]);
-        T::put(B, off, acc);
+        part[wave][lane] = acc;
+        __syncthreads();
+        if (wave == 0 && act) {
+            const int64_t off = (int64_t)r * args.ldb + u;
+            uint32_t sum = accumulate ? T::get(B, off) : 0u;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                if ((w + 1) * P / 4 > w * P / 4) sum = T::sum(sum, part[w][lane]);
+            T::put(B, off, sum);
+        }
+        __syncthreads();
     }
+}
+
+// Launch of k_stack_reduce over d x units output words.
+template <class T>
+hipError_t launch_stack_reduce(const StackApplyArgs &a, int32_t spw, int accumulate,
+                               hipStream_t s) {
+    const int64_t total = (int64_t)a.d * a.units;
+    int64_t blocks = (total + 63) / 64;
+    if (blocks > 65535) blocks = 65535;
+    if (blocks < 1) return hipSuccess;
+    k_stack_reduce<T><<<dim3((unsigned)blocks), 256, 0, s>>>(a, spw, accumulate);
+    return hipGetLastError();
 }
 
 }  // namespace sk
