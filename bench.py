@@ -17,8 +17,13 @@ dominant call's time, measured with HIP events on its stream.  The same run
 times the comparison legs: the stored-metadata FP16 sketch (sk_meta_generate
 + the LDS apply), the flat FP32 scatter (one global atomic per
 contribution), the LDS and fused FP32 sketches, the page's flat FP16
-design, and BlockPerm-SJLT on its own workload (A 2^21 x 512, d = 1024,
-M = 64, kappa = 4, s = 1).  cpu_baseline times the CPU oracle on the same
+design, the headline again under the FP16 page's protocol (medians over 11
+repetitions and sketch seeds 1..10), the complete sketch-and-solve, the
+coherence sweep (U = orth of the coherent 2^20 x 128 workload, zeta in
+{1, 2, 4, 8} x d in {256, 512, 1024}: times and E_OSE), and BlockPerm-SJLT
+on its own workload (A 2^21 x 512, d = 1024, M = 64, kappa = 4, s = 1)
+through sk_apply_blockperm_ex (register kernel) and sk_apply_blockperm
+(component kernel).  cpu_baseline times the CPU oracle on the same
 workload's rows, one thread.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]

@@ -269,3 +269,23 @@ def test_register_kernel_padded_strides_accumulate():
     assert np.all(Y[:, n:] == 3.0)
     ref = oracle.blockperm_f64(np.ascontiguousarray(A[:, :n]), d, M, kappa, 1, seed) + 3.0
     assert oracle.rel_frob(Y[:, :n], ref) <= 1e-5
+
+
+def test_ex_workspace_errors():
+    """sk_apply_blockperm_ex rejects a workspace that is too small
+    (SK_ERR_ARG) or not 16-byte aligned (SK_ERR_ALIGN), before any launch,
+    and a NULL workspace where the component kernel does not apply
+    (affine wiring) with SK_ERR_NULL."""
+    m, n, d, M, kappa = 4096, 64, 256, 16, 4
+    Ad = to_dev(inputs.gaussian(m, n, seed=1))
+    Y = torch.full((d, n), 7.0, device=dev())
+    nb = b.sk_blockperm_workspace_size(m, n, d, M, kappa, 1, b.SK_WIRING_AFFINE)
+    ws = torch.empty(nb + 64, dtype=torch.uint8, device=dev())
+    cases = [(ws, nb - 4, b.SK_ERR_ARG), (ws[4:], nb, b.SK_ERR_ALIGN), (None, 0, b.SK_ERR_NULL)]
+    for w, nbytes, expect in cases:
+        with pytest.raises(b.SketchError) as e:
+            b.sk_apply_blockperm_ex(Ad, m, n, n, d, M, kappa, 1, b.SK_WIRING_AFFINE, 3, Y, n, 0,
+                                    w, nbytes)
+        assert e.value.status == expect
+    sync()
+    assert torch.all(Y == 7.0)
