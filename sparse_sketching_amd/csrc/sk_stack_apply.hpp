@@ -64,6 +64,11 @@ struct AccF32 {
     }
     __device__ static uint32_t get(const out_t *B, int64_t off) { return __float_as_uint(B[off]); }
     __device__ static void put(out_t *B, int64_t off, uint32_t w) { B[off] = __uint_as_float(w); }
+    // the reduce's accumulator: the word itself (FP32 partials add in FP32)
+    typedef float wide_t;
+    __device__ static wide_t widen(uint32_t w) { return __uint_as_float(w); }
+    __device__ static wide_t wide_add(wide_t a, wide_t b) { return __fadd_rn(a, b); }
+    __device__ static uint32_t narrow(wide_t a) { return __float_as_uint(a); }
     // the word +1 or -1 (b = 1): acc + x*unit is exactly acc + x or acc - x
     __device__ static uint32_t unit(uint32_t b) { return 0x3F800000u | (b << 31); }
     __device__ static uint32_t fma_unit(uint32_t x, uint32_t u, uint32_t acc) {
@@ -94,6 +99,19 @@ struct AccF16 {
         return __builtin_bit_cast(uint32_t, B[off]);
     }
     __device__ static void put(out_t *B, int64_t off, uint32_t w) { B[off] = __builtin_bit_cast(h2_t, w); }
+    // the reduce's accumulator: the FP16 pair widened exactly to FP32; the
+    // sum of the partials is rounded to FP16 (nearest-even) once
+    typedef float2 wide_t;
+    __device__ static wide_t widen(uint32_t w) {
+        const h2_t h = __builtin_bit_cast(h2_t, w);
+        return make_float2((float)h.x, (float)h.y);
+    }
+    __device__ static wide_t wide_add(wide_t a, wide_t b) {
+        return make_float2(__fadd_rn(a.x, b.x), __fadd_rn(a.y, b.y));
+    }
+    __device__ static uint32_t narrow(wide_t a) {
+        return __builtin_bit_cast(uint32_t, cvt_rn_h2(a.x, a.y));
+    }
     // the pair (+1, +1) or (-1, -1) (b = 1): a packed FMA by it is exactly the
     // packed nearest-even add or subtract (the product is exact)
     __device__ static uint32_t unit(uint32_t b) { return 0x3C003C00u | (b << 31) | (b << 15); }
@@ -416,11 +434,14 @@ __global__ __launch_bounds__(kStackThreads) void k_stack_apply(const StackApplyA
 // and the non-empty quarter sums are then added in quarter order onto the
 // existing B word (accumulate) or onto zero: a fixed order, so the result
 // is deterministic, with four times the loads in flight of one thread per
-// word.
+// word.  The sums run in T::wide_t: FP32, also for FP16 partials, whose
+// total is rounded to FP16 once (the partials themselves hold FP16
+// nearest-even sums).
 template <class T>
 __global__ __launch_bounds__(256) void k_stack_reduce(const StackApplyArgs args, int32_t spw,
                                                        int32_t accumulate) {
-    __shared__ uint32_t part[4][64];
+    typedef typename T::wide_t wide_t;
+    __shared__ wide_t part[4][64];
     typename T::out_t *B = reinterpret_cast<typename T::out_t *>(args.B);
     const int64_t total = (int64_t)args.d * args.units;
     const int64_t plane = (int64_t)args.d * spw;
@@ -433,7 +454,7 @@ __global__ __launch_bounds__(256) void k_stack_reduce(const StackApplyArgs args,
         const bool act = k < total;
         const int r = act ? (int)(k / args.units) : 0;
         const int32_t u = act ? (int32_t)(k - (int64_t)r * args.units) : 0;
-        uint32_t acc = 0u;
+        wide_t acc = T::widen(0u);
         if (act) {
             const int32_t s = u / spw;
             const int cl = u - s * spw;
@@ -444,19 +465,19 @@ __global__ __launch_bounds__(256) void k_stack_reduce(const StackApplyArgs args,
 #pragma unroll
                 for (int qq = 0; qq < 8; ++qq) w[qq] = src[(int64_t)(p + qq) * plane];
 #pragma unroll
-                for (int qq = 0; qq < 8; ++qq) acc = T::sum(acc, w[qq]);
+                for (int qq = 0; qq < 8; ++qq) acc = T::wide_add(acc, T::widen(w[qq]));
             }
-            for (; p < p1; ++p) acc = T::sum(acc, src[(int64_t)p * plane]);
+            for (; p < p1; ++p) acc = T::wide_add(acc, T::widen(src[(int64_t)p * plane]));
         }
         part[wave][lane] = acc;
         __syncthreads();
         if (wave == 0 && act) {
             const int64_t off = (int64_t)r * args.ldb + u;
-            uint32_t sum = accumulate ? T::get(B, off) : 0u;
+            wide_t sum = T::widen(accumulate ? T::get(B, off) : 0u);
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                if ((w + 1) * P / 4 > w * P / 4) sum = T::sum(sum, part[w][lane]);
-            T::put(B, off, sum);
+                if ((w + 1) * P / 4 > w * P / 4) sum = T::wide_add(sum, part[w][lane]);
+            T::put(B, off, T::narrow(sum));
         }
         __syncthreads();
     }
