@@ -15,7 +15,7 @@ effective rate of the complete sketch.  The roofline block is stricter: it
 counts only the bytes the fused path must move (A + sketch) against the
 dominant call's time, measured with HIP events on its stream.  The same run
 times the comparison legs: the stored-metadata FP16 sketch (sk_meta_generate
-+ the LDS apply), the flat FP32 scatter (one global atomic per
++ the register or the LDS apply), the flat FP32 scatter (one global atomic per
 contribution), the LDS and fused FP32 sketches, the page's flat FP16
 design, the headline again under the FP16 page's protocol (medians over 11
 repetitions and sketch seeds 1..10), the complete sketch-and-solve, the
@@ -173,6 +173,8 @@ def main():
 
     ws16 = b.workspace(A, d, zeta, "f16acc")
     ws32 = b.workspace(A, d, zeta, "f32")
+    wsr16 = b.workspace(A, d, zeta, "f16acc", b.SK_VARIANT_REG)
+    wsr32 = b.workspace(A, d, zeta, "f32", b.SK_VARIANT_REG)
     wsf16 = b.sketch_workspace(A, d, zeta, "f16acc")
     wsf32 = b.sketch_workspace(A, d, zeta, "f32")
 
@@ -196,7 +198,9 @@ def main():
             fused16()
         meta()
         for _ in range(3):
-            f16()
+            f16(b.SK_VARIANT_LDS)
+        for _ in range(3):
+            f16(b.SK_VARIANT_REG, wsr16)
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -212,7 +216,8 @@ def main():
                                     b.SK_WIRING_SHIFT, SEED, Y, BP_N, 0, wsbp, wsbp.numel(), sp)
         torch.cuda.synchronize()
         print("profile pass done: 3 x fused f16 sketch, 3 x f16 LDS apply + reduce, "
-              "3 x 1 GiB copy, 3 x BlockPerm (register kernel + reduce)", flush=True)
+              "3 x f16 register apply + reduce, 3 x 1 GiB copy, 3 x BlockPerm (register "
+              "kernel + reduce)", flush=True)
         return
 
     K, W = args.steps, args.warmup
@@ -223,7 +228,8 @@ def main():
     for _ in range(max(20, W)):
         fused16()
         meta()
-        f16()
+        f16(b.SK_VARIANT_REG, wsr16)
+        f16(b.SK_VARIANT_LDS)
         f32(b.SK_VARIANT_FLAT, None)
     torch.cuda.synchronize()
 
@@ -231,20 +237,26 @@ def main():
     ms16 = timed(fused16, K, W, stream)
     print(f"[bench] f16acc complete sketch (fused) {ms16:.4f} ms", file=sys.stderr, flush=True)
     ms32_fused = timed(fused32, K, W, stream)
-    # the stored-metadata sketch: metadata kernel, then the LDS apply whose
-    # store-and-reduce flush also initializes B
-    ms16_meta = timed(lambda: (meta(), f16()), K, W, stream)
-    print(f"[bench] f32 fused {ms32_fused:.4f} ms, f16acc meta+LDS apply {ms16_meta:.4f} ms",
+    # the stored-metadata sketch through sk_meta_generate + sk_apply_*: the
+    # LDS apply (the default) and the reproducible register apply, both with
+    # the store-and-reduce flush that also initializes B
+    ms16_meta_reg = timed(lambda: (meta(), f16(b.SK_VARIANT_REG, wsr16)), K, W, stream)
+    ms16_meta = timed(lambda: (meta(), f16(b.SK_VARIANT_LDS)), K, W, stream)
+    print(f"[bench] f32 fused {ms32_fused:.4f} ms, f16acc meta+register apply "
+          f"{ms16_meta_reg:.4f} ms, meta+LDS apply {ms16_meta:.4f} ms",
           file=sys.stderr, flush=True)
-    ms16_atomic = timed(lambda: (meta(), f16(0, None)), K, W, stream)
+    ms16_atomic = timed(lambda: (meta(), f16(b.SK_VARIANT_LDS, None)), K, W, stream)
     ms32_flat = timed(lambda: (meta(), f32(b.SK_VARIANT_FLAT, None)), K, W, stream)
-    ms32_lds = timed(lambda: (meta(), f32()), K, W, stream)
+    ms32_lds = timed(lambda: (meta(), f32(b.SK_VARIANT_LDS)), K, W, stream)
+    ms32_reg = timed(lambda: (meta(), f32(b.SK_VARIANT_REG, wsr32)), K, W, stream)
     ms16_flat = timed(lambda: (meta(), f16(b.SK_VARIANT_FLAT, None)), max(1, K // 4), 1, stream)
     print(f"[bench] f16 lds+atomic flush {ms16_atomic:.4f} ms, f32 flat {ms32_flat:.4f} ms, "
-          f"f32 lds {ms32_lds:.4f} ms, f16 flat {ms16_flat:.4f} ms", file=sys.stderr, flush=True)
+          f"f32 lds {ms32_lds:.4f} ms, f32 register {ms32_reg:.4f} ms, f16 flat "
+          f"{ms16_flat:.4f} ms", file=sys.stderr, flush=True)
     # the apply alone (apply kernel + its reduce), and the metadata kernel alone
-    ms_kernel = timed(lambda: f16(b.SK_ACCUMULATE), K, W, stream)
-    ms_kernel_atomic = timed(lambda: f16(b.SK_ACCUMULATE, None), K, W, stream)
+    ms_kernel_reg = timed(lambda: f16(b.SK_ACCUMULATE | b.SK_VARIANT_REG, wsr16), K, W, stream)
+    ms_kernel = timed(lambda: f16(b.SK_ACCUMULATE | b.SK_VARIANT_LDS), K, W, stream)
+    ms_kernel_atomic = timed(lambda: f16(b.SK_ACCUMULATE | b.SK_VARIANT_LDS, None), K, W, stream)
     ms_meta = timed(meta, K, W, stream)
     # device copy bandwidth for context
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -252,7 +264,8 @@ def main():
     ms_copy = timed(lambda: dst.copy_(src), K, 2, stream)
     copy_gbs = 2 * src.numel() * 4 / ms_copy / 1e6
     del src, dst
-    print(f"[bench] apply+reduce {ms_kernel:.4f} ms, apply(atomic flush) {ms_kernel_atomic:.4f} ms, "
+    print(f"[bench] register apply+reduce {ms_kernel_reg:.4f} ms, LDS apply+reduce "
+          f"{ms_kernel:.4f} ms, LDS apply(atomic flush) {ms_kernel_atomic:.4f} ms, "
           f"meta {ms_meta:.4f} ms, copy {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
     # the FP16 sketching page's protocol (§V-A): per sketch seed 1..10, 3
@@ -321,7 +334,7 @@ def main():
     A_host = None if args.no_cpu_baseline else A.cpu().numpy()
     bp = None
     if not args.no_blockperm:
-        del A, ri, val, ws16, ws32, wsf16, wsf32
+        del A, ri, val, ws16, ws32, wsr16, wsr32, wsf16, wsf32
         torch.cuda.empty_cache()
         Abp = inputs.gaussian_torch(BP_M, BP_N, seed=0)
         Y = torch.empty((BP_D, BP_N), dtype=torch.float32, device=dev)
@@ -370,13 +383,18 @@ def main():
         "fp32_flat_GBps": round(bytes32 / ms32_flat / 1e6, 2),
         "fp32_lds_ms": round(ms32_lds, 5),
         "fp32_fused_ms": round(ms32_fused, 5),
+        "fp16_meta_reg_ms": round(ms16_meta_reg, 5),
+        "fp16_meta_reg_GBps": round(bytes16 / ms16_meta_reg / 1e6, 2),
+        "fp16_meta_reg_hbm_frac": round(bytes16 / ms16_meta_reg / 1e6 / HBM_PEAK_GBS, 4),
         "fp16_meta_lds_ms": round(ms16_meta, 5),
         "fp16_meta_lds_GBps": round(bytes16 / ms16_meta / 1e6, 2),
+        "fp32_meta_reg_ms": round(ms32_reg, 5),
         "fp16_flat_ms": round(ms16_flat, 5),
         "fp16_lds_atomic_flush_ms": round(ms16_atomic, 5),
         "speedup_vs_fp32_flat": round(ms32_flat / ms16, 3),
         "speedup_vs_fp32_lds": round(ms32_lds / ms16, 3),
         "speedup_vs_fp32_fused": round(ms32_fused / ms16, 3),
+        "fp16_reg_apply_ms": round(ms_kernel_reg, 5),
         "fp16_lds_apply_ms": round(ms_kernel, 5),
         "meta_ms": round(ms_meta, 5),
         "copy_GBps": round(copy_gbs, 1),

@@ -59,8 +59,9 @@ typedef enum sk_status {
 /* flags for the apply calls */
 #define SK_ACCUMULATE   1u  /* B += S A instead of B = S A */
 #define SK_VARIANT_FLAT 2u  /* one global atomic per contribution */
-#define SK_VARIANT_LDS  4u  /* LDS-privatized partial sketches (default when
-                               the d x slice partial fits in LDS) */
+#define SK_VARIANT_LDS  4u  /* LDS-privatized partial sketches */
+#define SK_VARIANT_REG  8u  /* partial sketches in registers, fixed order of
+                               additions (reproducible) */
 
 /* wiring argument of sk_apply_blockperm_ex */
 #define SK_WIRING_SHIFT  0
@@ -125,25 +126,39 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
  *              SK_VARIANT_LDS: each workgroup keeps a private FP32 partial
  *                of a column slice (and a group of stack blocks) in LDS,
  *                updated by read, add and integer compare-and-swap, and
- *                flushes it once.
+ *                flushes it once;
+ *              SK_VARIANT_REG: each workgroup streams a chunk of rows (and
+ *                their metadata) through LDS and each wavefront keeps its
+ *                own output rows' partial in registers; the partials go to
+ *                the workspace and a second kernel writes B as their sum.
+ *                Needs a workspace, zeta <= 16, d % 16 == 0, n >= 64
+ *                (FP32) / 128 (FP16), n and lda multiples of 2 (FP32) / 4
+ *                (FP16) and A 8 (FP32) / 16 (FP16) byte aligned: shapes
+ *                sk_fused_plan_describe reports as covered.
  *            0 picks LDS when the partial fits in LDS and zeta <= 64, else
- *            FLAT.
+ *            FLAT.  REG is only taken when asked for: it is the
+ *            reproducible variant, and at 2^20 x 256, d = 512 it is ~20%
+ *            slower than LDS.
  *   workspace, workspace_bytes
- *            optional device scratch for the LDS variant (4-byte aligned,
- *            disjoint from every other buffer; size from
- *            sk_apply_workspace_size).  With a workspace the partials are
- *            stored there and a second kernel writes B as their sum, in a
- *            fixed order (no global atomics, no separate zeroing of B).
- *            NULL: partials are added to B with global atomics.  Ignored by
- *            the FLAT variant.  The caller owns it; its contents on return
- *            are unspecified.  Calls that share a workspace must be ordered
- *            (same stream).
- * FP32 additions happen in an unspecified order (atomics, LDS locks).
- * Errors: SK_ERR_NULL, SK_ERR_SHAPE (n, d < 1, zeta range, d % zeta,
- * lda/ldb < n), SK_ERR_ARG (both variants, aliasing, workspace smaller than
- * required), SK_ERR_ALIGN (workspace not 4-byte aligned),
- * SK_ERR_UNSUPPORTED (SK_VARIANT_LDS forced where the partial cannot fit in
- * LDS or zeta > 64).
+ *            optional device scratch for the REG and LDS variants (4-byte
+ *            aligned, 16 for REG; disjoint from every other buffer; size
+ *            from sk_apply_workspace_size).  With a workspace the partials
+ *            are stored there and a second kernel writes B as their sum, in
+ *            a fixed order (no global atomics, no separate zeroing of B).
+ *            NULL: the LDS partials are added to B with global atomics.
+ *            Ignored by the FLAT variant.  The caller owns it; its contents
+ *            on return are unspecified.  Calls that share a workspace must
+ *            be ordered (same stream).
+ * Order of additions: REG is fixed (reproducible bit for bit); LDS follows
+ * which wavefront's compare-and-swap lands first, and FLAT the atomics'
+ * arrival, so neither is reproducible.
+ * Errors: SK_ERR_NULL (also: SK_VARIANT_REG without a workspace),
+ * SK_ERR_SHAPE (n, d < 1, zeta range, d % zeta, lda/ldb < n), SK_ERR_ARG
+ * (two variants, aliasing, workspace smaller than required), SK_ERR_ALIGN
+ * (workspace not 4-byte aligned, or not 16-byte aligned with
+ * SK_VARIANT_REG), SK_ERR_UNSUPPORTED (SK_VARIANT_LDS forced where the
+ * partial cannot fit in LDS or zeta > 64; SK_VARIANT_REG forced on a shape
+ * it does not cover).
  */
 sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda,
                        const int32_t *row_idx, const float *val, int32_t zeta,
@@ -163,10 +178,12 @@ sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda,
  *            aligned.  Overflow gives +-inf, inf + -inf gives NaN.
  *   flags    as for sk_apply_f32.  SK_VARIANT_FLAT is the page's design: one
  *            no-return packed global atomic per contribution pair.
- *            SK_VARIANT_LDS (the default) accumulates FP16 partials of row
- *            chunks in LDS (packed f16x2 words, nearest-even additions) and
- *            then adds the partials to B: the same RN operations in a
- *            two-level order.
+ *            SK_VARIANT_REG and SK_VARIANT_LDS accumulate FP16 partials of
+ *            row chunks (packed f16x2 words, nearest-even additions; REG in
+ *            registers, LDS in LDS); with a workspace the partials are
+ *            then added in a fixed order in FP32 and the total rounded to
+ *            FP16 once (without one, LDS adds them to B with packed FP16
+ *            atomics).
  *   workspace, workspace_bytes  as for sk_apply_f32.
  * Errors: as sk_apply_f32, plus SK_ERR_SHAPE for odd n and SK_ERR_ALIGN for
  * odd lda/ldb or misaligned A/B.
@@ -216,8 +233,10 @@ sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
 /*
  * sk_apply_workspace_size: bytes of workspace that sk_apply_f32
  * (precision SK_PRECISION_F32) or sk_apply_f16acc (SK_PRECISION_F16ACC)
- * uses for these sizes and flags on the current device; 0 when the chosen
- * variant uses none (FLAT, m = 0, or an LDS plan that does not fit).
+ * uses for these sizes and flags on the current device, whatever lda and
+ * A's alignment: SK_VARIANT_REG the register plan (for A with lda = n and
+ * an aligned base); otherwise the LDS plans.  0 when the chosen variant
+ * uses none (FLAT, m = 0, or no plan fits).
  * Errors: SK_ERR_NULL (bytes NULL), SK_ERR_SHAPE, SK_ERR_ARG (precision or
  * flags), SK_ERR_HIP (device query failed).
  */

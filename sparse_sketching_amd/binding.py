@@ -22,6 +22,7 @@ SK_OK, SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ALIGN, SK_ERR_UNSUPPORTED, SK_ERR_HIP, 
 SK_ACCUMULATE = 1
 SK_VARIANT_FLAT = 2
 SK_VARIANT_LDS = 4
+SK_VARIANT_REG = 8
 SK_PRECISION_F32 = 0
 SK_PRECISION_F16ACC = 1
 SK_FORMAT_F16 = 0
@@ -303,9 +304,10 @@ def workspace(A, d, zeta, precision="f16acc", flags=0):
 def apply(A, row_idx, val, zeta, d, precision="f16acc", out=None, flags=0, ws=True, stream=None):
     """B = S A from metadata; precision "f32" (float32 B) or "f16acc" (float16 B).
 
-    ws=True allocates the workspace the LDS variant uses for its
-    store-and-reduce flush; ws=None makes it flush with global atomics; a
-    byte tensor is used as the workspace."""
+    ws=True allocates the workspace the chosen variant needs (the LDS
+    variant's store-and-reduce flush, or the register variant's partials);
+    ws=None makes the LDS variant flush with global atomics; a byte tensor
+    is used as the workspace."""
     import torch
     _need_device(A, torch.float32, "A")
     m, n = A.shape

@@ -120,6 +120,11 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
 
 sk_status hip_status(hipError_t e) { return e == hipSuccess ? SK_OK : SK_ERR_HIP; }
 
+int variant_count(uint32_t flags) {
+    return ((flags & SK_VARIANT_FLAT) != 0) + ((flags & SK_VARIANT_LDS) != 0) +
+           ((flags & SK_VARIANT_REG) != 0);
+}
+
 // Checks shared by the SparseStack apply calls (FP32 and FP16 output).
 sk_status check_apply(const float *A, int64_t m, int32_t n, int64_t lda, const int32_t *row_idx,
                       const float *val, int32_t zeta, const void *B, size_t belem, int32_t d,
@@ -127,8 +132,9 @@ sk_status check_apply(const float *A, int64_t m, int32_t n, int64_t lda, const i
     if (m < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0) return SK_ERR_SHAPE;
     if (lda < n || ldb < n) return SK_ERR_SHAPE;
     if (m > (INT64_MAX / 8) / (zeta > lda ? zeta : lda)) return SK_ERR_SHAPE;
-    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS)) return SK_ERR_ARG;
-    if ((flags & SK_VARIANT_FLAT) && (flags & SK_VARIANT_LDS)) return SK_ERR_ARG;
+    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS | SK_VARIANT_REG))
+        return SK_ERR_ARG;
+    if (variant_count(flags) > 1) return SK_ERR_ARG;
     if (B == nullptr) return SK_ERR_NULL;
     if (m > 0 && (A == nullptr || row_idx == nullptr || val == nullptr)) return SK_ERR_NULL;
     const size_t bspan = span_bytes(d, n, ldb, belem);
@@ -148,6 +154,21 @@ sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t
     sk::DevInfo di;
     hipError_t e = sk::dev_info(&di);
     if (e != hipSuccess) return SK_ERR_HIP;
+    const bool accumulate = (flags & SK_ACCUMULATE) != 0;
+    // the register variant (asked for: reproducible, slower than LDS at
+    // C2-like shapes)
+    if (m > 0 && (flags & SK_VARIANT_REG)) {
+        sk::FusedPlan fp{};
+        const uintptr_t align = f16 ? 16 : 8;
+        if (!sk::plan_fused(di, f16, m, n, lda, (uintptr_t)A % align == 0, d, zeta, &fp))
+            return SK_ERR_UNSUPPORTED;
+        if (workspace == nullptr) return SK_ERR_NULL;
+        if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
+        if (workspace_bytes < fp.ws_bytes) return SK_ERR_ARG;
+        return hip_status(sk::launch_regs_apply(fp, f16, A, m, n, lda, row_idx, val, zeta, d, B,
+                                                ldb, static_cast<uint32_t *>(workspace),
+                                                accumulate ? 1 : 0, s));
+    }
     sk::LdsPlan plan{};
     const int64_t units = f16 ? n / 2 : n;
     // two-word lanes load 16 (FP16) or 8 (FP32) bytes per row
@@ -158,7 +179,6 @@ sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t
                         sk::plan_lds(di, m, units, wide_ok, f16 ? 1 : 2, d, zeta, &plan);
     if ((flags & SK_VARIANT_LDS) && !lds_ok && m > 0) return SK_ERR_UNSUPPORTED;
     const bool use_lds = m > 0 && !(flags & SK_VARIANT_FLAT) && lds_ok;
-    const bool accumulate = (flags & SK_ACCUMULATE) != 0;
     uint32_t *ws = nullptr;
     if (use_lds && workspace != nullptr) {
         if (workspace_bytes < plan.ws_bytes) return SK_ERR_ARG;
@@ -481,18 +501,28 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
     if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC) return SK_ERR_ARG;
     if (m < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0) return SK_ERR_SHAPE;
     if (precision == SK_PRECISION_F16ACC && n % 2 != 0) return SK_ERR_SHAPE;
-    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS)) return SK_ERR_ARG;
-    if ((flags & SK_VARIANT_FLAT) && (flags & SK_VARIANT_LDS)) return SK_ERR_ARG;
+    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS | SK_VARIANT_REG))
+        return SK_ERR_ARG;
+    if (variant_count(flags) > 1) return SK_ERR_ARG;
     if (m == 0 || (flags & SK_VARIANT_FLAT)) return SK_OK;
     sk::DevInfo di;
     if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
-    sk::LdsPlan plan{};
-    const int64_t units = precision == SK_PRECISION_F16ACC ? n / 2 : n;
-    // sizes for the widest plan: a two-word plan needs no more workspace
-    // than the one-word plan the same call may fall back to
+    const bool f16 = precision == SK_PRECISION_F16ACC;
     size_t best = 0;
-    const int gw = precision == SK_PRECISION_F16ACC ? 1 : 2;
-    if (sk::plan_lds(di, m, units, true, gw, d, zeta, &plan)) best = plan.ws_bytes;
+    // SK_VARIANT_REG: the register plan (A aligned, lda = n)
+    if (flags & SK_VARIANT_REG) {
+        sk::FusedPlan fp{};
+        if (sk::plan_fused(di, f16, m, n, n, true, d, zeta, &fp)) best = fp.ws_bytes;
+        *bytes = best;
+        return SK_OK;
+    }
+    // the LDS plans a call may take (a two-word plan needs no more
+    // workspace than the one-word plan)
+    sk::LdsPlan plan{};
+    const int64_t units = f16 ? n / 2 : n;
+    const int gw = f16 ? 1 : 2;
+    if (sk::plan_lds(di, m, units, true, gw, d, zeta, &plan) && plan.ws_bytes > best)
+        best = plan.ws_bytes;
     if (sk::plan_lds(di, m, units, false, gw, d, zeta, &plan) && plan.ws_bytes > best)
         best = plan.ws_bytes;
     *bytes = best;

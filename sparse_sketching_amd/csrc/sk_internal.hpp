@@ -76,6 +76,8 @@ constexpr int kFusedLdsBytes = 2 * 128 * 64 * 8 + 2 * kFusedMaxZeta * 128 * 4;
 struct FusedArgs {
     const float *A;
     uint32_t *ws;               // [slices][chunks][d][128] partial words
+    const int32_t *row_idx;     // stored metadata (register apply only)
+    const float *val;
     int64_t m, lda, rows_per_chunk, row_offset;
     uint64_t seed;
     int32_t n, d, zeta;
@@ -102,6 +104,12 @@ hipError_t launch_fused(const FusedPlan &plan, bool f16, const float *A, int64_t
                         int64_t lda, uint64_t seed, int64_t row_offset, int32_t d, int32_t zeta,
                         float scale, void *B, int64_t ldb, uint32_t *ws, int accumulate,
                         hipStream_t stream);
+// The register apply (apply_regs.hip): the fused sketch's plan and
+// ownership with stored metadata (any values) instead of in-kernel draws.
+hipError_t launch_regs_apply(const FusedPlan &plan, bool f16, const float *A, int64_t m,
+                             int32_t n, int64_t lda, const int32_t *row_idx, const float *val,
+                             int32_t zeta, int32_t d, void *B, int64_t ldb, uint32_t *ws,
+                             int accumulate, hipStream_t stream);
 
 constexpr int kBlockPermMaxM = 1024;
 struct BlockPermArgs {

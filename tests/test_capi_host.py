@@ -60,7 +60,9 @@ A, RI, V, B = FAKE, FAKE + (1 << 34), FAKE + (1 << 35), FAKE + (1 << 36)
     ((A, -1, 64, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_SHAPE),
     ((A, 100, 64, 64, RI, V, 4, B, 0, 64, 0), b.SK_ERR_SHAPE),      # d < 1
     ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 6), b.SK_ERR_ARG),       # FLAT|LDS
-    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 8), b.SK_ERR_ARG),       # unknown flag
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 10), b.SK_ERR_ARG),      # FLAT|REG
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 12), b.SK_ERR_ARG),      # LDS|REG
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 16), b.SK_ERR_ARG),      # unknown flag
     ((None, 100, 64, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_NULL),
     ((A, 100, 64, 64, None, V, 4, B, 64, 64, 0), b.SK_ERR_NULL),
     ((A, 100, 64, 64, RI, None, 4, B, 64, 64, 0), b.SK_ERR_NULL),
@@ -93,6 +95,8 @@ def test_workspace_validation(lib, fn, ws, nbytes, expect):
     ((1, 100, 63, 64, 4, 0), b.SK_ERR_SHAPE),      # odd n for FP16
     ((0, 100, 64, 64, 3, 0), b.SK_ERR_SHAPE),      # d % zeta
     ((0, 100, 64, 64, 4, 6), b.SK_ERR_ARG),        # FLAT|LDS
+    ((0, 100, 64, 64, 4, 12), b.SK_ERR_ARG),       # LDS|REG
+    ((0, 100, 64, 64, 4, 16), b.SK_ERR_ARG),       # unknown flag
     ((0, 0, 64, 64, 4, 0), b.SK_OK),               # m = 0: no workspace
     ((1, 100, 64, 64, 4, 2), b.SK_OK),             # FLAT: no workspace
 ])

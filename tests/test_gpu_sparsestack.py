@@ -20,10 +20,12 @@ from tests.gpuutil import dev, say, sync, to_dev
 pytestmark = pytest.mark.gpu
 
 # (flags, workspace): the page's flat scatter; the LDS-privatized apply with
-# the store-and-reduce flush (workspace); the same with the atomic flush
+# the store-and-reduce flush (workspace); the same with the atomic flush;
+# the register apply (workspace; shapes with n >= 128 and n % 4 == 0)
 VARIANTS = {"flat": (b.SK_VARIANT_FLAT, None), "lds": (b.SK_VARIANT_LDS, True),
-            "lds_atomic": (b.SK_VARIANT_LDS, None)}
-ALL = list(VARIANTS)
+            "lds_atomic": (b.SK_VARIANT_LDS, None), "reg": (b.SK_VARIANT_REG, True)}
+ALL = ["flat", "lds", "lds_atomic"]
+WIDE = ALL + ["reg"]
 U16 = 2.0**-11          # unit roundoff of binary16
 
 
