@@ -111,10 +111,11 @@ __global__ __launch_bounds__(kW * 64) void k_bp_regs(const BlockPermGenArgs args
 
     typedef FVec<4> vec_t;
     vec_t a[kP][kD];
-    // this wavefront's kD rows of stage st (clamped into the slice; stages
-    // past the last are not loaded)
+    // this wavefront's kD rows of stage st, clamped into the slice.  Every
+    // call issues its loads, also past the last stage (the clamped rows are
+    // L2 hits): a skipped load would make the compiler wait for the other
+    // register set's loads at every staging step.
     auto load = [&](int32_t st, vec_t (&av)[kD]) {
-        if (st >= nst) return;
 #pragma unroll
         for (int u = 0; u < kD; ++u) {
             int32_t rel = st * kS + wave * kD + u;
@@ -187,9 +188,11 @@ __global__ __launch_bounds__(kW * 64) void k_bp_regs(const BlockPermGenArgs args
                 apply(st, b ? hs1 : hs0, b ? me1 : me0);
                 stage(a[(b + 1) % kP], b ? hs0 : hs1);
                 draw(st + 1, b ? me0 : me1);
-                load(st + 1 + kP, a[(b + 1) % kP]);
-                lds_barrier();
             }
+            // on every path, so each staging step finds the other set's
+            // loads issued after its own
+            load(st + 1 + kP, a[(b + 1) % kP]);
+            lds_barrier();
         }
     }
     __builtin_amdgcn_s_waitcnt(0);

@@ -185,18 +185,21 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int32_t s = s0 + b;
-            if (s < nst) {
-                scan(s, b ? me1 : me0);
+            if (s < nst) scan(s, b ? me1 : me0);
 #pragma unroll
-                for (int j = 0; j < NH; ++j) {
+            for (int j = 0; j < NH; ++j) {
+                if (s < nst) {
                     process(b ? hs1 : hs0, j * R / NH, (j + 1) * R / NH);
                     stage(a[(b + 1) % P], b ? hs0 : hs1, j * D / NH, (j + 1) * D / NH);
                     // the Philox work runs while the staged registers are free
                     if (j == NH - 1) draw(s + 1, b ? me0 : me1);
-                    load(s + 1 + P, a[(b + 1) % P], j * D / NH, (j + 1) * D / NH);
                 }
-                lds_barrier();
+                // on every path (also for the odd stage past the end), so each
+                // staging step finds the other set's loads issued after its
+                // own and the compiler's wait leaves them in flight
+                load(s + 1 + P, a[(b + 1) % P], j * D / NH, (j + 1) * D / NH);
             }
+            lds_barrier();
         }
     }
     // the loads past the last stage (clamped rows) must land before exit
