@@ -143,6 +143,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-blockperm", action="store_true")
     ap.add_argument("--no-coherence", action="store_true")
+    ap.add_argument("--no-range", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="few fixed launches of the dominant kernels and a 1 GiB copy, no JSON")
     args = ap.parse_args()
@@ -332,6 +333,45 @@ def main():
                         f"{r['fp32_ose']:.4f})" for r in c3), file=sys.stderr, flush=True)
 
     A_host = None if args.no_cpu_baseline else A.cpu().numpy()
+
+    # range configuration (C4): A 4,194,304 x 64 of N(0,1) rows times
+    # exp(2Z) row scales (drawn on the device, seeded), zeta = 4, d = 128:
+    # the complete FP32 and FP16 sketches and the conversion variants of the
+    # page's flat FP16 design (apply only, metadata stored); accuracy is in
+    # the GPU tests
+    c4 = None
+    if not args.no_range:
+        mc, nc, dc, zc = 4194304, 64, 128, 4
+        g4 = torch.Generator(device=dev).manual_seed(0)
+        Ac = torch.randn((mc, nc), device=dev, generator=g4)
+        Ac *= torch.exp(2.0 * torch.randn((mc, 1), device=dev, generator=g4))
+        ric = torch.empty(mc * zc, dtype=torch.int32, device=dev)
+        vc = torch.empty(mc * zc, dtype=torch.float32, device=dev)
+        b.sk_meta_generate(SEED, 0, mc, dc, zc, ric, vc, sp)
+        Bc16 = torch.empty((dc, nc), dtype=torch.float16, device=dev)
+        Bc32 = torch.empty((dc, nc), dtype=torch.float32, device=dev)
+        wc16, wc32 = b.sketch_workspace(Ac, dc, zc, "f16acc"), b.sketch_workspace(Ac, dc, zc, "f32")
+        t = {"fp32_fused": timed(lambda: b.sk_sketch_f32(SEED, 0, Ac, mc, nc, nc, dc, zc, Bc32, nc,
+                                                         0, wc32, 0, sp), K, W, stream),
+             "fp16_two_level": timed(lambda: b.sk_sketch_f16acc(SEED, 0, Ac, mc, nc, nc, dc, zc,
+                                                                Bc16, nc, 0, wc16, 0, sp),
+                                     K, W, stream)}
+        for name, fmt, conv in (("fp16_rn_flat", b.SK_FORMAT_F16, b.SK_CONVERT_RN),
+                                ("fp16_sr_flat", b.SK_FORMAT_F16, b.SK_CONVERT_SR),
+                                ("bf16_rn_flat", b.SK_FORMAT_BF16, b.SK_CONVERT_RN)):
+            t[name] = timed(lambda: b.sk_apply_lowp(Ac, mc, nc, nc, ric, vc, zc, Bc16, dc, nc,
+                                                    fmt, conv, 1, 0, 0, sp),
+                            max(1, K // 4), 1, stream)
+        c4 = {"workload": "A 4,194,304 x 64 N(0,1) x exp(2Z) row scales, zeta = 4, d = 128",
+              **{k + "_ms": round(v, 4) for k, v in t.items()},
+              "fp16_two_level_GBps": round(sparsestack_bytes(mc, nc, dc, zc, 2)
+                                           / t["fp16_two_level"] / 1e6, 1),
+              "note": "fp32/fp16 two-level are complete sketches (metadata drawn in the call); "
+                      "the flat variants are the apply alone"}
+        print("[bench] range config: " + ", ".join(f"{k} {v:.4f} ms" for k, v in t.items()),
+              file=sys.stderr, flush=True)
+        del Ac, ric, vc, Bc16, Bc32, wc16, wc32
+
     bp = None
     if not args.no_blockperm:
         del A, ri, val, ws16, ws32, wsr16, wsr32, wsf16, wsf32
@@ -347,14 +387,27 @@ def main():
         ms_bpc = timed(lambda: b.sk_apply_blockperm(Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS,
                                                     BP_KAPPA, 1, SEED, Y, BP_N, 0, sp), K, W,
                        stream)
+        # the general options on the same workload: affine wiring, s = 2
+        var = {}
+        for name, s_rows, wiring in (("affine", 1, b.SK_WIRING_AFFINE),
+                                     ("s2", 2, b.SK_WIRING_SHIFT)):
+            nv = b.sk_blockperm_workspace_size(BP_M, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, s_rows,
+                                               wiring)
+            wsv = torch.empty(nv, dtype=torch.uint8, device=dev)
+            var[name] = timed(lambda: b.sk_apply_blockperm_ex(
+                Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, s_rows, wiring, SEED, Y, BP_N,
+                0, wsv, nv, sp), K, W, stream)
+            del wsv
         gbs_bp = blockperm_bytes(BP_M, BP_N, BP_D) / ms_bp / 1e6
         bp = {"workload": f"BlockPerm-SJLT m=2^21 n={BP_N} d={BP_D} M={BP_BLOCKS} "
                           f"kappa={BP_KAPPA} s=1", "path": "sk_apply_blockperm_ex (register kernel)",
               "ms": round(ms_bp, 4), "GBps": round(gbs_bp, 1),
               "hbm_frac": round(gbs_bp / HBM_PEAK_GBS, 4),
-              "component_kernel_ms": round(ms_bpc, 4)}
+              "component_kernel_ms": round(ms_bpc, 4),
+              "affine_wiring_ms": round(var["affine"], 4), "s2_ms": round(var["s2"], 4)}
         print(f"[bench] blockperm {ms_bp:.4f} ms {gbs_bp:.0f} GB/s (component kernel "
-              f"{ms_bpc:.4f} ms)", file=sys.stderr, flush=True)
+              f"{ms_bpc:.4f} ms, affine {var['affine']:.4f} ms, s=2 {var['s2']:.4f} ms)",
+              file=sys.stderr, flush=True)
         del Abp, Y, wsbp
 
     gbs16 = bytes16 / ms16 / 1e6
@@ -402,6 +455,7 @@ def main():
         "blockperm": bp,
         "sketch_and_solve": ls_out,
         "coherence_sweep": {"workload": "U = orth(coherent 2^20 x 128), seed 1", "rows": c3},
+        "range_config": c4,
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_bytes(),

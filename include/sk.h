@@ -131,10 +131,10 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
  *                their metadata) through LDS and each wavefront keeps its
  *                own output rows' partial in registers; the partials go to
  *                the workspace and a second kernel writes B as their sum.
- *                Needs a workspace, zeta <= 16, d % 16 == 0, n >= 64
- *                (FP32) / 128 (FP16), n and lda multiples of 2 (FP32) / 4
- *                (FP16) and A 8 (FP32) / 16 (FP16) byte aligned: shapes
- *                sk_fused_plan_describe reports as covered.
+ *                Needs a workspace, zeta <= 16, d % 16 == 0, n >= 64, n
+ *                and lda multiples of 2 (FP32) / 4 (FP16) and A 8 (FP32) /
+ *                16 (FP16) byte aligned: shapes sk_fused_plan_describe
+ *                reports as covered.
  *            0 picks LDS when the partial fits in LDS and zeta <= 64, else
  *            FLAT.  REG is only taken when asked for: it is the
  *            reproducible variant, and at 2^20 x 256, d = 512 it is ~20%
@@ -258,7 +258,7 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
  * in registers and writes it once to the workspace; a reduce kernel then
  * writes B as the sum of the partials in a fixed order (no atomics, B needs
  * no separate zeroing).  Shapes the fused kernel does not cover (zeta > 16,
- * d not a multiple of 16, fewer than 128 (FP16) / 64 (FP32) columns, rows
+ * d not a multiple of 16, fewer than 64 columns, rows
  * of A not 16-byte (FP16) / 8-byte (FP32) aligned, row ownership that does
  * not fit the registers) run sk_meta_generate into the workspace and then
  * the LDS (or flat) apply; the result is the same sketch.

@@ -254,13 +254,15 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
 // row groups G with R <= 32 (two words x R rows of registers per lane) and
 // R dividing d/zeta (a wave's rows inside one block); R must be one of the
 // built 4, 8, 16, 32.  Chunks are sized so one workgroup per CU fills the
-// device, in whole stages.  Narrow matrices (under half a slice of columns)
-// are left to the metadata + LDS apply path, which packs them better.
+// device, in whole stages.  Matrices under 64 columns are left to the
+// metadata + LDS apply path.  (From 64 columns on the fused kernel is
+// faster even with most lanes of its slice idle: a narrow sketch is bound
+// by the per-hit instructions, which do not depend on the active lanes.)
 bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
                 bool a_aligned, int32_t d, int32_t zeta, FusedPlan *p) {
     const int K = f16 ? 4 : 2;
     if (m < 1 || zeta > kFusedMaxZeta || n % K != 0 || lda % K != 0 || !a_aligned) return false;
-    if (n < 32 * K || d % kWaves != 0) return false;
+    if (n < 64 || d % kWaves != 0) return false;
     if (di.max_lds < kFusedLdsBytes) return false;
     // the kernel indexes rows inside a chunk with 32-bit integers
     if (m > (int64_t)65535 << 30) return false;

@@ -330,7 +330,9 @@ def test_fused_plan_alignment_and_validation(lib):
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, False, 512, 4, **MI355X)["fused"] == 0
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 258, True, 512, 4, **MI355X)["fused"] == 0
     assert b.sk_fused_plan_describe(P32, 1 << 20, 256, 257, True, 512, 4, **MI355X)["fused"] == 0
-    assert b.sk_fused_plan_describe(P16, 1 << 20, 64, 64, True, 128, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 64, 64, True, 128, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 60, 60, True, 128, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 62, 62, True, 128, 4, **MI355X)["fused"] == 0
     # LDS smaller than the kernel's stages
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, True, 512, 4, num_cu=256,
                                     max_lds=64 * 1024)["fused"] == 0

@@ -45,6 +45,8 @@ FUSED_SHAPES = [
     (5000, 128, 1024, 4),       # two row groups
     (129, 256, 512, 1),         # one stage plus one row
     (1, 128, 64, 4),            # a single row
+    (4096, 64, 128, 4),         # 64 columns: a quarter (FP16) / half (FP32) of the slice's lanes
+    (3000, 68, 64, 4),          # 68 columns, lanes past the row clamped
 ]
 
 
