@@ -88,6 +88,11 @@ def timed(fn, steps, warmup, stream):
     return start.elapsed_time(stop) / steps            # ms per call
 
 
+def timed_median(fn, steps, warmup, stream, blocks=3):
+    """Median over `blocks` timed regions of `steps` calls each (ms per call)."""
+    return median([timed(fn, steps, warmup, stream) for _ in range(blocks)])
+
+
 def timed_reps(fn, reps, warmup, stream):
     """Per-repetition times (ms) of fn, each bracketed by its own events."""
     import torch
@@ -137,8 +142,8 @@ def cpu_baseline(A_host, sample_rows):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-sample-rows", type=int, default=M_ROWS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-blockperm", action="store_true")
@@ -381,10 +386,12 @@ def main():
         nbp = b.sk_blockperm_workspace_size(BP_M, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, 1,
                                             b.SK_WIRING_SHIFT)
         wsbp = torch.empty(nbp, dtype=torch.uint8, device=dev)
-        ms_bp = timed(lambda: b.sk_apply_blockperm_ex(
+        # (each leg: the median of three timed regions of K calls, steadier
+        # than one region right after the 4 GiB input is drawn)
+        ms_bp = timed_median(lambda: b.sk_apply_blockperm_ex(
             Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, 1, b.SK_WIRING_SHIFT, SEED, Y, BP_N,
             0, wsbp, nbp, sp), K, W, stream)
-        ms_bpc = timed(lambda: b.sk_apply_blockperm(Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS,
+        ms_bpc = timed_median(lambda: b.sk_apply_blockperm(Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS,
                                                     BP_KAPPA, 1, SEED, Y, BP_N, 0, sp), K, W,
                        stream)
         # the general options on the same workload: affine wiring, s = 2
@@ -394,7 +401,7 @@ def main():
             nv = b.sk_blockperm_workspace_size(BP_M, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, s_rows,
                                                wiring)
             wsv = torch.empty(nv, dtype=torch.uint8, device=dev)
-            var[name] = timed(lambda: b.sk_apply_blockperm_ex(
+            var[name] = timed_median(lambda: b.sk_apply_blockperm_ex(
                 Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, s_rows, wiring, SEED, Y, BP_N,
                 0, wsv, nv, sp), K, W, stream)
             del wsv

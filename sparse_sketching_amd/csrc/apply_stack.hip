@@ -7,25 +7,30 @@
 namespace sk {
 namespace {
 
-template <class T, int W, int ZG>
+template <class T, int W, int ZG, bool NT>
 const void *pick_kernel(bool full) {
     if constexpr (W == 2) {
         (void)full;
-        return (const void *)k_stack_apply<T, 2, ZG, true>;
+        return (const void *)k_stack_apply<T, 2, ZG, true, NT>;
     } else {
-        return full ? (const void *)k_stack_apply<T, 1, ZG, true>
-                    : (const void *)k_stack_apply<T, 1, ZG, false>;
+        return full ? (const void *)k_stack_apply<T, 1, ZG, true, NT>
+                    : (const void *)k_stack_apply<T, 1, ZG, false, NT>;
     }
 }
 
+template <class T, int W, int ZG>
+const void *pick_nt(bool full, bool nt) {
+    return nt ? pick_kernel<T, W, ZG, true>(full) : pick_kernel<T, W, ZG, false>(full);
+}
+
 template <class T, int W>
-const void *pick_zg(int zg, bool full) {
+const void *pick_zg(int zg, bool full, bool nt) {
     switch (zg) {
-        case 1: return pick_kernel<T, W, 1>(full);
-        case 2: return pick_kernel<T, W, 2>(full);
-        case 4: return pick_kernel<T, W, 4>(full);
-        case 8: return pick_kernel<T, W, 8>(full);
-        default: return pick_kernel<T, W, 0>(full);
+        case 1: return pick_nt<T, W, 1>(full, nt);
+        case 2: return pick_nt<T, W, 2>(full, nt);
+        case 4: return pick_nt<T, W, 4>(full, nt);
+        case 8: return pick_nt<T, W, 8>(full, nt);
+        default: return pick_nt<T, W, 0>(full, nt);
     }
 }
 
@@ -37,7 +42,9 @@ hipError_t launch_stack(const LdsPlan &p, StackApplyArgs &a, int accumulate, hip
     if ((p.words != 1 && p.words != 2) || (p.words == 2 && !full) || p.slice != a.sp ||
         p.slice < 8 || p.slice > 64)
         return hipErrorInvalidValue;
-    const void *kern = p.words == 2 ? pick_zg<T, 2>(p.zg, full) : pick_zg<T, 1>(p.zg, full);
+    // one block group reads each row of A once: nontemporal loads
+    const bool nt = p.groups == 1;
+    const void *kern = p.words == 2 ? pick_zg<T, 2>(p.zg, full, nt) : pick_zg<T, 1>(p.zg, full, nt);
     hipError_t e = set_lds_limit(kern, p.lds_bytes);
     if (e != hipSuccess) return e;
     void *params[] = {&a};

@@ -122,26 +122,27 @@ struct AccF16 {
     }
 };
 
-// K consecutive floats of A, loaded as one vector.
+// K consecutive floats of A, loaded as one vector; NT adds the nontemporal
+// hint, for passes that read each element of A once.  (Where several
+// workgroups read the same rows, the hint costs their shared L2 hits: on
+// gfx950 the two block groups of the FP32 LDS apply of a 2^20 x 256 matrix
+// ran 12 % slower with it.)
 template <int K> struct FVec;
 template <> struct FVec<1> { float x[1]; };
 template <> struct FVec<2> { float x[2]; };
 template <> struct FVec<4> { float x[4]; };
-template <int K>
+template <int K, bool NT>
 __device__ __forceinline__ FVec<K> load_vec(const char *p) {
+    typedef float vk_t __attribute__((ext_vector_type(K)));
     FVec<K> r;
     if constexpr (K == 1) {
-        r.x[0] = *reinterpret_cast<const float *>(p);
-    } else if constexpr (K == 2) {
-        const float2 v = *reinterpret_cast<const float2 *>(p);
-        r.x[0] = v.x;
-        r.x[1] = v.y;
+        const float *q = reinterpret_cast<const float *>(p);
+        r.x[0] = NT ? __builtin_nontemporal_load(q) : *q;
     } else {
-        const float4 v = *reinterpret_cast<const float4 *>(p);
-        r.x[0] = v.x;
-        r.x[1] = v.y;
-        r.x[2] = v.z;
-        r.x[3] = v.w;
+        const vk_t *q = reinterpret_cast<const vk_t *>(p);
+        const vk_t v = NT ? __builtin_nontemporal_load(q) : *q;
+#pragma unroll
+        for (int i = 0; i < K; ++i) r.x[i] = v[i];
     }
     return r;
 }
@@ -202,8 +203,9 @@ __device__ __forceinline__ void cas_add(typename WordT<W>::type *lw, uint32_t id
     }
 }
 
-// FULL: the slice is 64 lanes wide (sp == 64).
-template <class T, int W, int ZG, bool FULL>
+// FULL: the slice is 64 lanes wide (sp == 64).  NT: one block group, so
+// this workgroup is the only reader of its rows (nontemporal loads).
+template <class T, int W, int ZG, bool FULL, bool NT>
 __global__ __launch_bounds__(kStackThreads) void k_stack_apply(const StackApplyArgs args) {
     constexpr int K = W * T::kCols;             // floats of A per lane per row
     typedef FVec<K> vec_t;
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack_apply(const StackApplyA
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
             const uint32_t off = (uint32_t)(u < lim ? u : lim) * row_bytes + lane_bytes;
-            a[u] = load_vec<K>(base + off);
+            a[u] = load_vec<K, NT>(base + off);
         }
         const int u = lane / zg;
         const int k = lane - u * zg;
