@@ -48,7 +48,7 @@ SEED = 1
 # dispatch; FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a 1 GiB device
 # copy reads on the same counters).  Valid for the kernels named here only.
 TRAFFIC = {"kernels": ("k_stack_fused<AccF16,32,1>", "k_stack_reduce<AccF16>"),
-           "fetch_kib": (524_449, 32_803), "write_kib": (65_536, 256),
+           "fetch_kib": (524_770, 32_803), "write_kib": (65_536, 256),
            "fetch_scale": 2.0, "write_scale": 1.0}
 
 
