@@ -133,9 +133,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
         }
     };
     // this wave's entries of stage s: output row inside its range (-1:
-    // none) and sign, lane j <-> stage row h*64 + j
+    // none) and the +-1 word of its sign, lane j <-> stage row h*64 + j
     int32_t rl[NL];
-    uint32_t sg[NL];
+    uint32_t su[NL];
     auto scan = [&](int32_t s, const uint32_t *me) {
 #pragma unroll
         for (int h = 0; h < NL; ++h) {
@@ -143,15 +143,14 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
             const int32_t rel = s * S + h * 64 + lane;
             const uint32_t rk = (e & 0x7FFFFFFFu) - lob;
             rl[h] = rel < nrows && rk < (uint32_t)R ? (int32_t)rk : -1;
-            sg[h] = e & 0x80000000u;
+            su[h] = T::unit(e >> 31);
         }
     };
-    // every hit of the scanned stage on this wave's rows [k0, k1); the sign
-    // is a scalar +-1 word from a ballot of the lanes' signs
+    // every hit of the scanned stage on this wave's rows [k0, k1); the +-1
+    // word is read from the hit's lane into a scalar register (one VALU
+    // readlane instead of three scalar shifts: the scalar unit, shared by
+    // the CU's waves, is the busier one in this loop)
     auto process = [&](const uint2 *hs, int k0, int k1) {
-        uint64_t neg[NL];
-#pragma unroll
-        for (int h = 0; h < NL; ++h) neg[h] = __ballot(sg[h] != 0u);
 #pragma unroll
         for (int k = k0; k < k1; ++k) {
 #pragma unroll
@@ -161,7 +160,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
                     const int i = __builtin_ctzll(mk);
                     mk &= mk - 1;
                     const uint2 x = hs[(h * 64 + i) * 64 + lane];
-                    const uint32_t u = T::unit((uint32_t)(neg[h] >> i) & 1u);
+                    const uint32_t u = __builtin_amdgcn_readlane(su[h], i);
                     acc[k][0] = T::fma_unit(x.x, u, acc[k][0]);
                     acc[k][1] = T::fma_unit(x.y, u, acc[k][1]);
                 }
