@@ -131,14 +131,19 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
  *                their metadata) through LDS and each wavefront keeps its
  *                own output rows' partial in registers; the partials go to
  *                the workspace and a second kernel writes B as their sum.
- *                Needs a workspace, zeta <= 16, d % 16 == 0, n >= 64, n
+ *                Needs a workspace, zeta <= 8, d % 16 == 0, n >= 64, n
  *                and lda multiples of 2 (FP32) / 4 (FP16) and A 8 (FP32) /
  *                16 (FP16) byte aligned: shapes sk_fused_plan_describe
- *                reports as covered.
- *            0 picks LDS when the partial fits in LDS and zeta <= 64, else
- *            FLAT.  REG is only taken when asked for: it is the
- *            reproducible variant, and at 2^20 x 256, d = 512 it is ~20%
- *            slower than LDS.
+ *                reports as covered, with zeta <= 8.  Its fast path
+ *                assumes |val| = float32(1/sqrt(zeta)), as sk_meta_generate
+ *                writes; a workgroup whose rows hold any other value redoes
+ *                them with a per-hit product (about three times slower for
+ *                that chunk, same result rules).
+ *            0 picks REG where it covers the shape and the workspace is
+ *            large enough for it (16-byte aligned), else LDS when the
+ *            partial fits in LDS and zeta <= 64, else FLAT.  At 2^20 x
+ *            256, d = 512, zeta = 4 REG takes 0.20 ms and LDS 0.25 ms
+ *            (FP16, with the reduce).
  *   workspace, workspace_bytes
  *            optional device scratch for the REG and LDS variants (4-byte
  *            aligned, 16 for REG; disjoint from every other buffer; size
@@ -235,8 +240,8 @@ sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
  * (precision SK_PRECISION_F32) or sk_apply_f16acc (SK_PRECISION_F16ACC)
  * uses for these sizes and flags on the current device, whatever lda and
  * A's alignment: SK_VARIANT_REG the register plan (for A with lda = n and
- * an aligned base); otherwise the LDS plans.  0 when the chosen variant
- * uses none (FLAT, m = 0, or no plan fits).
+ * an aligned base), SK_VARIANT_LDS the LDS plans, 0 the larger of the two.
+ * 0 when the chosen variant uses none (FLAT, m = 0, or no plan fits).
  * Errors: SK_ERR_NULL (bytes NULL), SK_ERR_SHAPE, SK_ERR_ARG (precision or
  * flags), SK_ERR_HIP (device query failed).
  */

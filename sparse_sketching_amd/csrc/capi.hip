@@ -155,19 +155,28 @@ sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t
     hipError_t e = sk::dev_info(&di);
     if (e != hipSuccess) return SK_ERR_HIP;
     const bool accumulate = (flags & SK_ACCUMULATE) != 0;
-    // the register variant (asked for: reproducible, slower than LDS at
-    // C2-like shapes)
-    if (m > 0 && (flags & SK_VARIANT_REG)) {
+    // the register variant: asked for, or by default where it covers the
+    // shape and the workspace holds its partials (reproducible, and the
+    // faster one there)
+    if (m > 0 && !(flags & (SK_VARIANT_FLAT | SK_VARIANT_LDS))) {
+        const bool forced = (flags & SK_VARIANT_REG) != 0;
         sk::FusedPlan fp{};
         const uintptr_t align = f16 ? 16 : 8;
-        if (!sk::plan_fused(di, f16, m, n, lda, (uintptr_t)A % align == 0, d, zeta, &fp))
-            return SK_ERR_UNSUPPORTED;
-        if (workspace == nullptr) return SK_ERR_NULL;
-        if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
-        if (workspace_bytes < fp.ws_bytes) return SK_ERR_ARG;
-        return hip_status(sk::launch_regs_apply(fp, f16, A, m, n, lda, row_idx, val, zeta, d, B,
-                                                ldb, static_cast<uint32_t *>(workspace),
-                                                accumulate ? 1 : 0, s));
+        const bool covered =
+            sk::plan_fused(di, f16, m, n, lda, (uintptr_t)A % align == 0, d, zeta, &fp) &&
+            zeta <= sk::kFusedMetaMaxZeta;
+        if (forced) {
+            if (!covered) return SK_ERR_UNSUPPORTED;
+            if (workspace == nullptr) return SK_ERR_NULL;
+            if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
+            if (workspace_bytes < fp.ws_bytes) return SK_ERR_ARG;
+        }
+        if (forced || (covered && workspace != nullptr && (uintptr_t)workspace % 16 == 0 &&
+                       workspace_bytes >= fp.ws_bytes))
+            return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, 0, 0, row_idx, val, d,
+                                               zeta, scale_of(zeta), B, ldb,
+                                               static_cast<uint32_t *>(workspace),
+                                               accumulate ? 1 : 0, s));
     }
     sk::LdsPlan plan{};
     const int64_t units = f16 ? n / 2 : n;
@@ -287,8 +296,9 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
     const uintptr_t align = f16 ? 16 : 8;
     sk::FusedPlan fp{};
     if (sk::plan_fused(di, f16, m, n, lda, (uintptr_t)A % align == 0, d, zeta, &fp))
-        return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, d, zeta, scale,
-                                           B, ldb, static_cast<uint32_t *>(workspace),
+        return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, nullptr,
+                                           nullptr, d, zeta, scale, B, ldb,
+                                           static_cast<uint32_t *>(workspace),
                                            accumulate ? 1 : 0, s));
     // not covered by the fused kernel: metadata into the workspace, then
     // the LDS (or flat) apply with the rest of it
@@ -509,12 +519,16 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
     if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
     const bool f16 = precision == SK_PRECISION_F16ACC;
     size_t best = 0;
-    // SK_VARIANT_REG: the register plan (A aligned, lda = n)
-    if (flags & SK_VARIANT_REG) {
+    // the register plan (A aligned, lda = n): SK_VARIANT_REG, and the
+    // default, which takes it where it covers the shape
+    if (!(flags & SK_VARIANT_LDS)) {
         sk::FusedPlan fp{};
-        if (sk::plan_fused(di, f16, m, n, n, true, d, zeta, &fp)) best = fp.ws_bytes;
-        *bytes = best;
-        return SK_OK;
+        if (sk::plan_fused(di, f16, m, n, n, true, d, zeta, &fp) && zeta <= sk::kFusedMetaMaxZeta)
+            best = fp.ws_bytes;
+        if (flags & SK_VARIANT_REG) {
+            *bytes = best;
+            return SK_OK;
+        }
     }
     // the LDS plans a call may take (a two-word plan needs no more
     // workspace than the one-word plan)

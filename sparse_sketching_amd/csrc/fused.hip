@@ -46,15 +46,27 @@ constexpr int kWaves = 16;              // wavefronts per workgroup
 constexpr int kRowsPerWave = kStage / kWaves;
 constexpr int kLaneGroups = kStage / 64;
 
-template <class T, int R, int P>
+// META: the metadata is read from row_idx / val (the stored-metadata
+// apply, zeta <= kFusedMetaMaxZeta) instead of drawn: each wavefront loads
+// the entries of the rows it stages, with them, one per lane.  Entries
+// outside their own block are dropped.  The staged words hold a * scale,
+// so the main loop assumes every |val| = scale (sk_meta_generate's
+// values); a workgroup whose chunk holds any other value redoes the chunk
+// afterwards with a per-hit product from raw rows.
+template <class T, int R, int P, bool META>
 __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs args) {
     constexpr int K = 2 * T::kCols;     // floats of A per lane per row
     typedef FVec<K> vec_t;
     constexpr int S = kStage, D = kRowsPerWave, NL = kLaneGroups;
-    __shared__ uint2 hs0[S * 64];       // stage contributions, row j at [j*64, j*64+64)
-    __shared__ uint2 hs1[S * 64];
-    __shared__ uint32_t me0[kFusedMaxZeta * S];  // entry (t, j) at t*S + j: bucket | sign << 31
+    // both stage buffers, contiguous: stage contributions, row j of buffer b
+    // at [(b*S + j)*64, +64); the general redo holds one stage of raw rows
+    __shared__ uint2 hs[2 * S * 64];
+    uint2 *const hs0 = hs;
+    uint2 *const hs1 = hs + S * 64;
+    // entry (t, j) at t*S + j: bucket | sign << 31
+    __shared__ uint32_t me0[kFusedMaxZeta * S];
     __shared__ uint32_t me1[kFusedMaxZeta * S];
+    __shared__ uint32_t vote[kWaves];   // META: wave w saw a general value
 
     // workgroup -> (slice, chunk, row group); the groups of one (slice,
     // chunk) are 8 ids apart (same XCD under round-robin dispatch)
@@ -87,6 +99,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
     const uint32_t lane_off = (uint32_t)col_c * 4u;        // bytes into a row
     const char *__restrict__ A = reinterpret_cast<const char *>(args.A);
     const float c = args.scale;
+    const uint32_t cbits = __float_as_uint(c);
+    bool gen = false;                   // META: this lane staged a general value
 
     uint32_t acc[R][2];
 #pragma unroll
@@ -94,6 +108,20 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
 
     // rows [u0, u1) of this wave's share of stage s, clamped into the chunk
     vec_t a[P][D];
+    // META: the entries of the wave's rows of a stage, D*zeta <= 64
+    // consecutive ones, entry q on lane q (clamped into the chunk), loaded
+    // with the rows
+    int32_t mi[P];
+    uint32_t mv[P];
+    const int64_t last_e = (r0 + nrows) * zeta - 1;
+    auto load_meta = [&](int32_t s, int32_t &ri, uint32_t &vb) {
+        if constexpr (META) {
+            const int64_t e0 = (r0 + (int64_t)s * S + wave * D) * zeta + lane;
+            const int64_t e = e0 < last_e ? e0 : last_e;
+            ri = args.row_idx[e];
+            vb = __float_as_uint(args.val[e]);
+        }
+    };
     // (a row's address is wave-uniform: a scalar base plus the lane's
     // 32-bit offset, so the loads take the scalar-base form)
     auto load = [&](int32_t s, vec_t (&av)[D], int u0, int u1) {
@@ -111,9 +139,25 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
             hs[(wave * D + u) * 64 + lane] =
                 make_uint2(T::contrib(av[u].x, c), T::contrib(av[u].x + T::kCols, c));
     };
+    // META: this wave's entries of a stage into me (bucket | sign << 31;
+    // 0x7FFFFFFF, which no wave owns, for an entry outside its block), and
+    // in vb_out (if given) the values' bits at the same places
+    auto stage_meta = [&](int32_t ri, uint32_t vb, uint32_t *me, uint32_t *vb_out) {
+        if constexpr (META) {
+            if (lane < D * zeta) {
+                const int jj = lane / zeta, tt = lane - jj * zeta;
+                const uint32_t bk = (uint32_t)(ri - tt * (int32_t)db);
+                const bool ok = bk < db;
+                gen |= ok && (vb & 0x7FFFFFFFu) != cbits;
+                me[tt * S + wave * D + jj] = ok ? (bk | (vb & 0x80000000u)) : 0x7FFFFFFFu;
+                if (vb_out != nullptr) vb_out[tt * S + wave * D + jj] = vb;
+            }
+        }
+    };
     // the metadata of stage s into me: one wave per stage (rotating) draws
     // the Philox blocks of the stage's rows, one row per lane
     auto draw = [&](int32_t s, uint32_t *me) {
+        if constexpr (META) return;
         if (wave != (s & (kWaves - 1))) return;
         const uint32_t k0 = (uint32_t)args.seed, k1 = (uint32_t)(args.seed >> 32);
         // one lane group at a time keeps the Philox temporaries few
@@ -168,6 +212,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
         }
     };
 
+
     // stage 0 staged and stages 1..P loading; then per stage s: apply s,
     // stage s+1 into the other buffer from the register set it was loaded
     // into, draw the metadata of s+1, and reload the set with stage s+1+P.
@@ -175,10 +220,15 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
     // the middle), so the next loads start half a stage earlier.
     constexpr int NH = (P == 1 && R < 32) ? 2 : 1;
     load(0, a[0], 0, D);
+    load_meta(0, mi[0], mv[0]);
     stage(a[0], hs0, 0, D);
+    stage_meta(mi[0], mv[0], me0, nullptr);
     draw(0, me0);
 #pragma unroll
-    for (int p = 1; p <= P; ++p) load(p, a[p % P], 0, D);
+    for (int p = 1; p <= P; ++p) {
+        load(p, a[p % P], 0, D);
+        load_meta(p, mi[p % P], mv[p % P]);
+    }
     __syncthreads();
     for (int32_t s0 = 0; s0 < nst; s0 += 2) {
 #pragma unroll
@@ -191,18 +241,71 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
                     process(b ? hs1 : hs0, j * R / NH, (j + 1) * R / NH);
                     stage(a[(b + 1) % P], b ? hs0 : hs1, j * D / NH, (j + 1) * D / NH);
                     // the Philox work runs while the staged registers are free
-                    if (j == NH - 1) draw(s + 1, b ? me0 : me1);
+                    if (j == NH - 1) {
+                        draw(s + 1, b ? me0 : me1);
+                        stage_meta(mi[(b + 1) % P], mv[(b + 1) % P], b ? me0 : me1, nullptr);
+                    }
                 }
                 // on every path (also for the odd stage past the end), so each
                 // staging step finds the other set's loads issued after its
                 // own and the compiler's wait leaves them in flight
                 load(s + 1 + P, a[(b + 1) % P], j * D / NH, (j + 1) * D / NH);
+                if (j == NH - 1) load_meta(s + 1 + P, mi[(b + 1) % P], mv[(b + 1) % P]);
             }
             lds_barrier();
         }
     }
     // the loads past the last stage (clamped rows) must land before exit
     __builtin_amdgcn_s_waitcnt(0);
+
+    if constexpr (META) {
+        // the waves' votes: does the chunk hold a value of another magnitude
+        const bool mine = __ballot(gen) != 0;
+        __syncthreads();
+        if (lane == 0) vote[wave] = mine ? 1u : 0u;
+        __syncthreads();
+        if (__ballot(vote[lane & (kWaves - 1)] != 0u) != 0) {
+            // redo the chunk: stage by stage, raw rows in LDS and the
+            // values in me1, every hit adding the rounded product a * val
+            float *raw = reinterpret_cast<float *>(hs);   // row j, lane l at (j*64 + l)*K
+#pragma unroll
+            for (int k = 0; k < R; ++k) acc[k][0] = acc[k][1] = 0u;
+            for (int32_t s = 0; s < nst; ++s) {
+                vec_t av[D];
+                load(s, av, 0, D);
+                int32_t ri;
+                uint32_t vb;
+                load_meta(s, ri, vb);
+#pragma unroll
+                for (int u = 0; u < D; ++u)
+#pragma unroll
+                    for (int i = 0; i < K; ++i) raw[((wave * D + u) * 64 + lane) * K + i] = av[u].x[i];
+                stage_meta(ri, vb, me0, me1);
+                __syncthreads();
+                scan(s, me0);
+                uint32_t vv[NL];
+#pragma unroll
+                for (int h = 0; h < NL; ++h) vv[h] = me1[t * S + h * 64 + lane];
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+#pragma unroll
+                    for (int h = 0; h < NL; ++h) {
+                        uint64_t mk = __ballot(rl[h] == k);
+                        while (mk) {
+                            const int i = __builtin_ctzll(mk);
+                            mk &= mk - 1;
+                            const float v = __uint_as_float(__builtin_amdgcn_readlane(vv[h], i));
+                            const float *xr = raw + ((h * 64 + i) * 64 + lane) * K;
+                            acc[k][0] = T::fma_unit(T::contrib(xr, v), T::unit(0u), acc[k][0]);
+                            acc[k][1] =
+                                T::fma_unit(T::contrib(xr + T::kCols, v), T::unit(0u), acc[k][1]);
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
 
     // the wave's R partial rows of this (slice, chunk)
     uint32_t *dst = args.ws + ((int64_t)slice * args.chunks + chunk) * (int64_t)args.d * 128 +
@@ -214,23 +317,27 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
 
 // The built (R, P) pairs: two register sets where the R rows leave room
 // for them (R = 8, 16), one set (loaded in two halves when R = 4) otherwise.
-template <class T>
+template <class T, bool META>
 const void *pick_fused(int R, int P) {
-    if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 4, 1>;
-    if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 8, 2>;
-    if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 16, 2>;
-    if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 32, 1>;
+    if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 4, 1, META>;
+    if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 8, 2, META>;
+    if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 16, 2, META>;
+    if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 32, 1, META>;
     return nullptr;
 }
 
 template <class T>
 hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int64_t ldb_units,
                           int32_t units, int accumulate, hipStream_t s) {
-    const void *kern = pick_fused<T>(p.rows_per_wave, p.load_sets);
+    const bool meta = fa.row_idx != nullptr;
+    const void *kern = meta ? pick_fused<T, true>(p.rows_per_wave, p.load_sets)
+                            : pick_fused<T, false>(p.rows_per_wave, p.load_sets);
     // the kernel's row ownership must match the plan the workspace was
-    // sized for: 16 waves x R rows x groups cover d exactly
+    // sized for: 16 waves x R rows x groups cover d exactly; with stored
+    // metadata a wave's rows of a stage hold at most 64 entries
     if (kern == nullptr || (int64_t)kWaves * p.rows_per_wave * p.groups != fa.d ||
-        fa.groups != p.groups || fa.zeta > kFusedMaxZeta || fa.ws == nullptr)
+        fa.groups != p.groups || fa.zeta < 1 || fa.zeta > kFusedMaxZeta || fa.ws == nullptr ||
+        (meta && (fa.val == nullptr || fa.zeta > kFusedMetaMaxZeta)))
         return hipErrorInvalidValue;
     FusedArgs a = fa;
     void *params[] = {&a};
@@ -298,12 +405,14 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
 }
 
 hipError_t launch_fused(const FusedPlan &p, bool f16, const float *A, int64_t m, int32_t n,
-                        int64_t lda, uint64_t seed, int64_t row_offset, int32_t d, int32_t zeta,
-                        float scale, void *B, int64_t ldb, uint32_t *ws, int accumulate,
-                        hipStream_t s) {
+                        int64_t lda, uint64_t seed, int64_t row_offset, const int32_t *row_idx,
+                        const float *val, int32_t d, int32_t zeta, float scale, void *B,
+                        int64_t ldb, uint32_t *ws, int accumulate, hipStream_t s) {
     FusedArgs a{};
     a.A = A;
     a.ws = ws;
+    a.row_idx = row_idx;
+    a.val = val;
     a.m = m;
     a.lda = lda;
     a.rows_per_chunk = p.rows_per_chunk;

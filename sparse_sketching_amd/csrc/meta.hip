@@ -6,6 +6,9 @@
 // and writes up to four (row_idx, val) entries; when zeta is a multiple of
 // four and the arrays are 16-byte aligned it writes them as one 16-byte
 // store each, so a wavefront writes 1 KiB of contiguous metadata per store.
+// The stores carry the nontemporal hint: the apply that reads the arrays
+// next ran 15 % slower (0.246 against 0.209 ms for metadata + register
+// apply of a 2^20 x 256 matrix on gfx950) when they were cached writes.
 #include "sk_internal.hpp"
 #include "sk_rng.hpp"
 
@@ -36,15 +39,19 @@ __global__ __launch_bounds__(256) void k_meta(uint64_t seed, int64_t row_offset,
         v[j] = (ws[j] & 1u) ? -scale : scale;
     }
     if (VEC4) {
-        *reinterpret_cast<int4 *>(row_idx + e) = int4{r[0], r[1], r[2], r[3]};
-        *reinterpret_cast<float4 *>(val + e) = float4{v[0], v[1], v[2], v[3]};
+        typedef int i4_t __attribute__((ext_vector_type(4)));
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(i4_t{r[0], r[1], r[2], r[3]},
+                                    reinterpret_cast<i4_t *>(row_idx + e));
+        __builtin_nontemporal_store(f4_t{v[0], v[1], v[2], v[3]},
+                                    reinterpret_cast<f4_t *>(val + e));
     } else {
         const int32_t cnt = zeta - t0 < 4 ? zeta - t0 : 4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j < cnt) {
-                row_idx[e + j] = r[j];
-                val[e + j] = v[j];
+                __builtin_nontemporal_store(r[j], row_idx + e + j);
+                __builtin_nontemporal_store(v[j], val + e + j);
             }
         }
     }

@@ -70,13 +70,16 @@ hipError_t launch_f16_lds(const LdsPlan &plan, const float *A, int64_t m, int32_
 
 // Fused SparseStack sketch (metadata drawn in the apply kernel, fused.hip).
 constexpr int kFusedMaxZeta = 16;
-// static LDS of the fused kernel: two 128-row stages of 64 lanes x 8 bytes
-// and two metadata stages of kFusedMaxZeta x 128 entries
-constexpr int kFusedLdsBytes = 2 * 128 * 64 * 8 + 2 * kFusedMaxZeta * 128 * 4;
+// with stored metadata (8 rows x zeta entries per wavefront and stage, one
+// per lane)
+constexpr int kFusedMetaMaxZeta = 8;
+// static LDS of the fused kernel: two 128-row stages of 64 lanes x 8 bytes,
+// two metadata stages of kFusedMaxZeta x 128 entries and 16 per-wave votes
+constexpr int kFusedLdsBytes = 2 * 128 * 64 * 8 + 2 * kFusedMaxZeta * 128 * 4 + 16 * 4;
 struct FusedArgs {
     const float *A;
     uint32_t *ws;               // [slices][chunks][d][128] partial words
-    const int32_t *row_idx;     // stored metadata (register apply only)
+    const int32_t *row_idx;     // stored metadata (NULL: drawn in the kernel)
     const float *val;
     int64_t m, lda, rows_per_chunk, row_offset;
     uint64_t seed;
@@ -100,16 +103,13 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
                 bool a_aligned, int32_t d, int32_t zeta, FusedPlan *plan);
 // Fused kernel into ws, then the chunk-order reduce into B (=, or += when
 // accumulate).  B is float* (FP32) or FP16 bits (uint16_t*), ldb in elements.
+// row_idx / val NULL: the metadata is drawn from (seed, row_offset) in the
+// kernel; else it is read from them (the stored-metadata apply; seed and
+// row_offset unused) and scale must be float32(1/sqrt(zeta)).
 hipError_t launch_fused(const FusedPlan &plan, bool f16, const float *A, int64_t m, int32_t n,
-                        int64_t lda, uint64_t seed, int64_t row_offset, int32_t d, int32_t zeta,
-                        float scale, void *B, int64_t ldb, uint32_t *ws, int accumulate,
-                        hipStream_t stream);
-// The register apply (apply_regs.hip): the fused sketch's plan and
-// ownership with stored metadata (any values) instead of in-kernel draws.
-hipError_t launch_regs_apply(const FusedPlan &plan, bool f16, const float *A, int64_t m,
-                             int32_t n, int64_t lda, const int32_t *row_idx, const float *val,
-                             int32_t zeta, int32_t d, void *B, int64_t ldb, uint32_t *ws,
-                             int accumulate, hipStream_t stream);
+                        int64_t lda, uint64_t seed, int64_t row_offset, const int32_t *row_idx,
+                        const float *val, int32_t d, int32_t zeta, float scale, void *B,
+                        int64_t ldb, uint32_t *ws, int accumulate, hipStream_t stream);
 
 constexpr int kBlockPermMaxM = 1024;
 struct BlockPermArgs {

@@ -36,7 +36,7 @@ def run_reg(A, ri, v, zeta, d, precision, flags=b.SK_VARIANT_REG, out=None):
 @pytest.mark.parametrize("m,n,d,zeta,R,G", [
     (4096, 256, 64, 4, 4, 1),       # R = 4
     (3000, 128, 128, 4, 8, 1),      # R = 8, a short last stage
-    (5000, 260, 256, 16, 16, 1),    # R = 16, zeta = 16, ragged second slice
+    (5000, 260, 256, 8, 16, 1),     # R = 16, zeta = 8, ragged second slice
     (4096, 128, 512, 8, 32, 1),     # R = 32
     (2500, 136, 1024, 1, 32, 2),    # two row groups (A read twice)
 ])
@@ -56,7 +56,9 @@ def test_register_apply_vs_oracle(precision, m, n, d, zeta, R, G):
 def test_register_exact_inputs_and_general_values(precision):
     """Integer A (FP32) / {-1,0,1} A (FP16) with stored values scaled by
     dyadic factors: every product and partial sum is exact, so B equals
-    fp64 bit for bit; values differ from entry to entry."""
+    fp64 bit for bit; values differ from entry to entry (every chunk takes
+    the kernel's per-hit-product redo), or a single entry differs (one
+    workgroup's chunk does)."""
     m, n, d, zeta = 3000, 128, 128, 4
     lo, hi = (-8, 8) if precision == "f32" else (-1, 1)
     A = inputs.integer_matrix(m, n, lo, hi, seed=13)
@@ -64,7 +66,9 @@ def test_register_exact_inputs_and_general_values(precision):
     g = np.random.default_rng(5)
     v_gen = (v_h * g.choice(np.array([0.25, 0.5, 1.0, 2.0], dtype=np.float32), size=v_h.size)
              ).astype(np.float32)
-    for vals in (v_h, v_gen):
+    v_one = v_h.copy()
+    v_one[1234 * zeta + 2] *= 2
+    for vals in (v_h, v_gen, v_one):
         B = run_reg(A, to_dev(ri_h), to_dev(vals), zeta, d, precision)
         ref = oracle.sketch_f64(A, ri_h, vals, d, zeta)
         assert np.abs(ref).max() < 1024
@@ -104,6 +108,24 @@ def test_register_out_of_range_entries_ignored(precision):
                             np.where(keep, v_h, 0).astype(np.float32), d, zeta)
     B = run_reg(A, to_dev(bad), to_dev(v_h), zeta, d, precision)
     assert np.array_equal(B.float().cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("precision,tol", [("f32", 1e-5), ("f16acc", 4e-3)])
+def test_register_general_values_gaussian(precision, tol):
+    """N(0,1) input with values of random magnitude in a few rows spread
+    over the chunks, zeta = 8: the chunks holding them are redone with
+    per-hit products; the sketch meets the bars against fp64."""
+    m, n, d, zeta = 40000, 256, 256, 8
+    A = inputs.gaussian(m, n, seed=21)
+    ri_h, v_h = oracle.meta_ref(4, m, d, zeta)
+    vals = v_h.copy()
+    g = np.random.default_rng(8)
+    rows = g.choice(m, 40, replace=False)
+    vals.reshape(m, zeta)[rows] *= g.uniform(0.1, 3.0, size=(40, zeta)).astype(np.float32)
+    B = run_reg(A, to_dev(ri_h), to_dev(vals), zeta, d, precision)
+    err = oracle.rel_frob(B.float().cpu().numpy().astype(np.float64),
+                          oracle.sketch_f64(A, ri_h, vals, d, zeta))
+    assert err <= tol, err
 
 
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
@@ -167,6 +189,12 @@ def test_register_forced_errors():
             b.sk_apply_f32(Ax, 4096, Ax.shape[1], Ax.shape[1], ri, v, zeta, Bx, d, Bx.shape[1],
                            flags, w, nbytes)
         assert e.value.status == expect
+    # zeta = 16: a wavefront's 8 rows of a stage hold more than 64 entries
+    ri16, v16 = b.meta(1, 4096, d, 16, device=dev())
+    assert b.sk_apply_workspace_size(b.SK_PRECISION_F32, 4096, 128, d, 16, b.SK_VARIANT_REG) == 0
+    with pytest.raises(b.SketchError) as e:
+        b.sk_apply_f32(A2, 4096, 128, 128, ri16, v16, 16, B2, d, 128, b.SK_VARIANT_REG, ws2, need)
+    assert e.value.status == b.SK_ERR_UNSUPPORTED
 
 
 # ------------------------------------------------- scale configuration (C2)
