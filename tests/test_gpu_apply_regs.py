@@ -220,3 +220,22 @@ def test_register_scale(scale_case, precision, tol):
     err = oracle.rel_frob(B.float().cpu().numpy().astype(np.float64), ref)
     say(f"  register apply scale {precision} rel err {err:.3e}")
     assert err <= tol
+
+
+@pytest.mark.parametrize("precision,tol", [("f32", 1e-5), ("f16acc", 4e-3)])
+def test_register_scale_general_values(scale_case, precision, tol):
+    """The scale configuration with values of another magnitude in 64 rows
+    (so about 64 of the 256 workgroups redo their chunk with per-hit
+    products) against fp64 of the same values."""
+    Ad, d, zeta, seed, _ = scale_case
+    m = Ad.shape[0]
+    ri_h, v_h = oracle.meta_ref(seed, m, d, zeta)
+    g = np.random.default_rng(17)
+    rows = g.choice(m, 64, replace=False)
+    vals = v_h.copy()
+    vals.reshape(m, zeta)[rows] *= g.uniform(0.1, 3.0, size=(64, zeta)).astype(np.float32)
+    B = run_reg(Ad, to_dev(ri_h), to_dev(vals), zeta, d, precision)
+    ref = oracle.sketch_f64(Ad.cpu().numpy(), ri_h, vals, d, zeta)
+    err = oracle.rel_frob(B.float().cpu().numpy().astype(np.float64), ref)
+    say(f"  register apply scale, general values, {precision} rel err {err:.3e}")
+    assert err <= tol

@@ -53,6 +53,20 @@ def test_lds_apply_past_2g_elements(big, precision, tol):
     assert err <= tol
 
 
+@pytest.mark.parametrize("precision,tol", [("f32", 1e-5), ("f16acc", 4e-3)])
+def test_register_apply_past_2g_elements(big, precision, tol):
+    """The stored-metadata apply on the fused kernel (the default with a
+    workspace)."""
+    A, _, ref = big
+    say(f"large register apply {precision}")
+    ri, v = b.meta(SEED, M_ROWS, D, ZETA, device=dev())
+    B = b.apply(A, ri, v, ZETA, D, precision=precision, flags=b.SK_VARIANT_REG)
+    sync()
+    err = oracle.rel_frob(B[:, COLS].float().cpu().numpy().astype(np.float64), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= tol
+
+
 def test_blockperm_register_past_2g_elements(big):
     A, Ac, _ = big
     say("large BlockPerm (register kernel)")
