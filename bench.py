@@ -244,8 +244,9 @@ def main():
     print(f"[bench] f16acc complete sketch (fused) {ms16:.4f} ms", file=sys.stderr, flush=True)
     ms32_fused = timed(fused32, K, W, stream)
     # the stored-metadata sketch through sk_meta_generate + sk_apply_*: the
-    # LDS apply (the default) and the reproducible register apply, both with
-    # the store-and-reduce flush that also initializes B
+    # register apply (the fused kernel reading the metadata; the default
+    # with a workspace) and the LDS apply, both with the store-and-reduce
+    # flush that also initializes B
     ms16_meta_reg = timed(lambda: (meta(), f16(b.SK_VARIANT_REG, wsr16)), K, W, stream)
     ms16_meta = timed(lambda: (meta(), f16(b.SK_VARIANT_LDS)), K, W, stream)
     print(f"[bench] f32 fused {ms32_fused:.4f} ms, f16acc meta+register apply "

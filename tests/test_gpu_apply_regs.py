@@ -239,3 +239,36 @@ def test_register_scale_general_values(scale_case, precision, tol):
     err = oracle.rel_frob(B.float().cpu().numpy().astype(np.float64), ref)
     say(f"  register apply scale, general values, {precision} rel err {err:.3e}")
     assert err <= tol
+
+
+@pytest.mark.parametrize("precision", ["f32", "f16acc"])
+def test_default_variant_choice(precision):
+    """flags = 0: the register apply where it covers the shape and the
+    workspace holds its partials (bit-identical to forcing it), else the
+    LDS apply (zeta = 16; or a workspace only large enough for LDS).  Exact
+    inputs, so every path equals fp64 bit for bit."""
+    m, n, d = 6000, 128, 256
+    A = inputs.integer_matrix(m, n, -1, 1, seed=23)
+    Ad = to_dev(A)
+    prec = PREC[precision]
+    for zeta in (4, 16):
+        ri, v = b.meta(6, m, d, zeta, device=dev())
+        ri_h, v_h = oracle.meta_ref(6, m, d, zeta)
+        ref = oracle.sketch_f64(A, ri_h, v_h, d, zeta)
+        need_def = b.sk_apply_workspace_size(prec, m, n, d, zeta, 0)
+        need_reg = b.sk_apply_workspace_size(prec, m, n, d, zeta, b.SK_VARIANT_REG)
+        need_lds = b.sk_apply_workspace_size(prec, m, n, d, zeta, b.SK_VARIANT_LDS)
+        assert need_def == max(need_reg, need_lds)
+        assert (need_reg > 0) == (zeta <= 8)
+        B0 = b.apply(Ad, ri, v, zeta, d, precision=precision, flags=0, ws=True)
+        sync()
+        assert np.array_equal(B0.float().cpu().numpy().astype(np.float64), ref)
+        if zeta <= 8:
+            Br = run_reg(Ad, ri, v, zeta, d, precision)
+            assert torch.equal(B0, Br)
+            # a workspace the LDS plan fits but the register plan does not
+            assert 0 < need_lds < need_reg
+            ws = torch.empty(need_lds, dtype=torch.uint8, device=dev())
+            B1 = b.apply(Ad, ri, v, zeta, d, precision=precision, flags=0, ws=ws)
+            sync()
+            assert np.array_equal(B1.float().cpu().numpy().astype(np.float64), ref)
