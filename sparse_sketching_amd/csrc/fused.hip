@@ -1,7 +1,9 @@
 // Fused SparseStack sketch for gfx950: the metadata is drawn inside the
 // apply kernel instead of being stored (FP16 sketching page §III-C names a
 // Philox metadata kernel; the FlashSketch page §5.2 makes a sketch's
-// randomness on the fly and never stores S).
+// randomness on the fly and never stores S).  The same kernel, reading
+// stored metadata instead (META), is the register variant of
+// sk_apply_f32 / sk_apply_f16acc.
 //
 // What is computed: B (=|+=) S A for the SparseStack S whose entries are
 // exactly those sk_meta_generate writes for (seed, row_offset): for global
@@ -33,6 +35,7 @@
 //  * The partial is written once to the workspace, and the reduce kernel of
 //    the LDS apply (sk_stack_apply.hpp) sums the chunks in a fixed order
 //    into B: deterministic, and B needs no separate zeroing.
+//  * Rows of A are loaded with the nontemporal hint (read once).
 #include "sk_internal.hpp"
 #include "sk_rng.hpp"
 #include "sk_stack_apply.hpp"
@@ -132,11 +135,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
             av[u] = load_row<K>(uniform_addr((uint64_t)(A + (r0 + rel) * lda * 4)), lane_off);
         }
     };
-    // contributions of loaded rows [u0, u1) into stage buffer hs
-    auto stage = [&](const vec_t (&av)[D], uint2 *hs, int u0, int u1) {
+    // contributions of loaded rows [u0, u1) into stage buffer buf
+    auto stage = [&](const vec_t (&av)[D], uint2 *buf, int u0, int u1) {
 #pragma unroll
         for (int u = u0; u < u1; ++u)
-            hs[(wave * D + u) * 64 + lane] =
+            buf[(wave * D + u) * 64 + lane] =
                 make_uint2(T::contrib(av[u].x, c), T::contrib(av[u].x + T::kCols, c));
     };
     // META: this wave's entries of a stage into me (bucket | sign << 31;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
     // word is read from the hit's lane into a scalar register (one VALU
     // readlane instead of three scalar shifts: the scalar unit, shared by
     // the CU's waves, is the busier one in this loop)
-    auto process = [&](const uint2 *hs, int k0, int k1) {
+    auto process = [&](const uint2 *buf, int k0, int k1) {
 #pragma unroll
         for (int k = k0; k < k1; ++k) {
 #pragma unroll
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
                 while (mk) {
                     const int i = __builtin_ctzll(mk);
                     mk &= mk - 1;
-                    const uint2 x = hs[(h * 64 + i) * 64 + lane];
+                    const uint2 x = buf[(h * 64 + i) * 64 + lane];
                     const uint32_t u = __builtin_amdgcn_readlane(su[h], i);
                     acc[k][0] = T::fma_unit(x.x, u, acc[k][0]);
                     acc[k][1] = T::fma_unit(x.y, u, acc[k][1]);
@@ -212,10 +215,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
         }
     };
 
-
     // stage 0 staged and stages 1..P loading; then per stage s: apply s,
     // stage s+1 into the other buffer from the register set it was loaded
-    // into, draw the metadata of s+1, and reload the set with stage s+1+P.
+    // into, draw the metadata of s+1 (META: write the entries loaded with
+    // its rows), and reload the set with stage s+1+P.
     // With P = 1 this is done in two halves (rows and output rows split at
     // the middle), so the next loads start half a stage earlier.
     constexpr int NH = (P == 1 && R < 32) ? 2 : 1;
