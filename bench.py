@@ -340,7 +340,7 @@ def main():
 
     A_host = None if args.no_cpu_baseline else A.cpu().numpy()
 
-    # range configuration (C4): A 4,194,304 x 64 of N(0,1) rows times
+    # range configuration: A 4,194,304 x 64 of N(0,1) rows times
     # exp(2Z) row scales (drawn on the device, seeded), zeta = 4, d = 128:
     # the complete FP32 and FP16 sketches and the conversion variants of the
     # page's flat FP16 design (apply only, metadata stored); accuracy is in

@@ -197,7 +197,7 @@ def test_register_forced_errors():
     assert e.value.status == b.SK_ERR_UNSUPPORTED
 
 
-# ------------------------------------------------- scale configuration (C2)
+# --------------------------- scale configuration (A 2^20 x 256, d = 512)
 
 @pytest.fixture(scope="module")
 def scale_case():

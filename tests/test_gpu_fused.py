@@ -185,7 +185,7 @@ def test_fused_equals_meta_plus_apply_f32_exact():
     assert torch.equal(Bf, Bm)
 
 
-# ------------------------------------------------- scale configuration (C2)
+# --------------------------- scale configuration (A 2^20 x 256, d = 512)
 
 @pytest.fixture(scope="module")
 def scale_case():

@@ -140,7 +140,7 @@ def test_sr_draws_depend_on_seed_and_global_row():
     assert abs(oracle.rel_frob(B1, ref) - oracle.rel_frob(B1b, ref)) < 1e-2
 
 
-# ------------------------------------------------------- range stress (C4)
+# --------------------------------- range stress (A 4,194,304 x 64, d = 128)
 
 @pytest.fixture(scope="module")
 def range_case():
@@ -169,7 +169,7 @@ def test_range_stress(range_case, k):
     FP32 is unaffected; BF16 stays finite over the whole range; the FP16
     variants are finite while the sums fit FP16 and overflow (+-inf) when
     they do not; at ordinary scale the two-level FP16 sketch is the most
-    accurate FP16 variant.  C4 is a measurement, not a parity gate: the
+    accurate FP16 variant.  The range stress is a measurement, not a parity gate: the
     bars here are properties, and the printed table is the result."""
     Ad0, ri, v, d, zeta, seed, ref = range_case
     Ad = Ad0 * (2.0**k)

@@ -258,7 +258,7 @@ def test_large_d_falls_back_to_flat():
     assert np.array_equal(B.cpu().numpy().astype(np.float64), oracle.sketch_f64(A, rh, vh, d, zeta))
 
 
-# ------------------------------------------------- scale configuration (C2)
+# --------------------------- scale configuration (A 2^20 x 256, d = 512)
 
 @pytest.fixture(scope="module")
 def scale_case():
