@@ -262,7 +262,11 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
  * nearest-even additions.  The fused kernel keeps each workgroup's partial
  * in registers and writes it once to the workspace; a reduce kernel then
  * writes B as the sum of the partials in a fixed order (no atomics, B needs
- * no separate zeroing).  Shapes the fused kernel does not cover (zeta > 16,
+ * no separate zeroing).  FP32 matrices wider than 128 columns whose rows
+ * allow 16-byte loads (lda % 4 == 0, A 16-byte aligned) take four partial
+ * words per lane (256 columns per workgroup) instead of two; the order of
+ * each output word's additions is fixed either way.  Shapes the fused
+ * kernel does not cover (zeta > 16,
  * d not a multiple of 16, fewer than 64 columns, rows
  * of A not 16-byte (FP16) / 8-byte (FP32) aligned, row ownership that does
  * not fit the registers) run sk_meta_generate into the workspace and then
@@ -307,18 +311,21 @@ sk_status sk_sketch_workspace_size(int32_t precision, int64_t m, int32_t n, int3
 
 /*
  * sk_fused_plan_describe: the launch plan of the fused kernel behind
- * sk_sketch_*, for the given sizes, lda, whether A's base is aligned for its
- * lane loads (a_aligned), and the device's compute units and per-workgroup
- * LDS bytes.  Pure host computation (no HIP call), for tests and tools that
- * check a plan against the kernel's index bounds.
+ * sk_sketch_* (and SK_VARIANT_REG), for the given sizes, lda, the alignment
+ * of A's base address in bytes (a_align: 16 or more allows every lane load;
+ * FP32 needs 8, and 16 for four words per lane; FP16 needs 16), and the
+ * device's compute units and per-workgroup LDS bytes.  Pure host
+ * computation (no HIP call), for tests and tools that check a plan against
+ * the kernel's index bounds.
  *   out  int64[SK_FUSED_PLAN_FIELDS], written: {fused kernel used (0: the
  *        fallback runs), output rows per wavefront, output row groups,
- *        column slices, rows per chunk, chunks, workgroups, workspace bytes}.
+ *        column slices, rows per chunk, chunks, workgroups, workspace bytes,
+ *        partial words per lane (2 or 4), input rows per stage}.
  * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ARG (precision, num_cu, max_lds).
  */
-#define SK_FUSED_PLAN_FIELDS 8
+#define SK_FUSED_PLAN_FIELDS 10
 sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
-                                 int32_t a_aligned, int32_t d, int32_t zeta, int32_t num_cu,
+                                 int32_t a_align, int32_t d, int32_t zeta, int32_t num_cu,
                                  int32_t max_lds, int64_t *out);
 
 /*

@@ -257,14 +257,15 @@ def sk_sketch_workspace_size(precision, m, n, d, zeta):
 
 
 FUSED_PLAN_FIELDS = ("fused", "rows_per_wave", "groups", "slices", "rows_per_chunk", "chunks",
-                     "grid", "ws_bytes")
+                     "grid", "ws_bytes", "words", "stage_rows")
 
 
-def sk_fused_plan_describe(precision, m, n, lda, a_aligned, d, zeta, num_cu, max_lds):
-    """The fused kernel's launch plan as a dict (host computation)."""
+def sk_fused_plan_describe(precision, m, n, lda, a_align, d, zeta, num_cu, max_lds):
+    """The fused kernel's launch plan as a dict (host computation); a_align
+    is the alignment of A's base address in bytes."""
     out = (ctypes.c_int64 * len(FUSED_PLAN_FIELDS))()
     _check("sk_fused_plan_describe", load().sk_fused_plan_describe(
-        precision, m, n, lda, int(bool(a_aligned)), d, zeta, num_cu, max_lds, out))
+        precision, m, n, lda, int(a_align), d, zeta, num_cu, max_lds, out))
     return dict(zip(FUSED_PLAN_FIELDS, list(out)))
 
 

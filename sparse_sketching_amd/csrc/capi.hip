@@ -113,6 +113,27 @@ bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes) {
     return x < y + bbytes && y < x + abytes;
 }
 
+// alignment of a base address in bytes, capped at 16 (the widest lane load)
+int base_align(const void *p) {
+    const uintptr_t x = (uintptr_t)p;
+    if (x % 16 == 0) return 16;
+    return (int)(x & (~x + 1));
+}
+
+// The fused plan's workspace for rows of lda = n, the larger of the plans an
+// A of 8- or 16-byte alignment gets (the word width depends on it); 0 if
+// neither covers the shape.
+size_t fused_ws_bytes(const sk::DevInfo &di, bool f16, int64_t m, int32_t n, int32_t d,
+                      int32_t zeta) {
+    size_t need = 0;
+    for (int a = 8; a <= 16; a *= 2) {
+        sk::FusedPlan fp{};
+        if (sk::plan_fused(di, f16, m, n, n, a, d, zeta, &fp) && fp.ws_bytes > need)
+            need = fp.ws_bytes;
+    }
+    return need;
+}
+
 size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
     if (rows <= 0 || cols <= 0) return 0;
     return (size_t)((rows - 1) * ld + cols) * elem;
@@ -161,9 +182,8 @@ sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t
     if (m > 0 && !(flags & (SK_VARIANT_FLAT | SK_VARIANT_LDS))) {
         const bool forced = (flags & SK_VARIANT_REG) != 0;
         sk::FusedPlan fp{};
-        const uintptr_t align = f16 ? 16 : 8;
         const bool covered =
-            sk::plan_fused(di, f16, m, n, lda, (uintptr_t)A % align == 0, d, zeta, &fp) &&
+            sk::plan_fused(di, f16, m, n, lda, base_align(A), d, zeta, &fp) &&
             zeta <= sk::kFusedMetaMaxZeta;
         if (forced) {
             if (!covered) return SK_ERR_UNSUPPORTED;
@@ -251,10 +271,8 @@ size_t sketch_ws_bytes(const sk::DevInfo &di, bool f16, int64_t m, int32_t n, in
                        int32_t zeta) {
     if (m == 0) return 0;
     size_t need = fallback_ws_bytes(di, f16, m, n, d, zeta);
-    sk::FusedPlan fp{};
-    if (sk::plan_fused(di, f16, m, n, n, true, d, zeta, &fp) && fp.ws_bytes > need)
-        need = fp.ws_bytes;
-    return need;
+    const size_t fused = fused_ws_bytes(di, f16, m, n, d, zeta);
+    return fused > need ? fused : need;
 }
 
 sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const float *A, int64_t m,
@@ -293,9 +311,8 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
     }
     if (workspace_bytes < sketch_ws_bytes(di, f16, m, n, d, zeta)) return SK_ERR_ARG;
     const float scale = scale_of(zeta);
-    const uintptr_t align = f16 ? 16 : 8;
     sk::FusedPlan fp{};
-    if (sk::plan_fused(di, f16, m, n, lda, (uintptr_t)A % align == 0, d, zeta, &fp))
+    if (sk::plan_fused(di, f16, m, n, lda, base_align(A), d, zeta, &fp))
         return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, nullptr,
                                            nullptr, d, zeta, scale, B, ldb,
                                            static_cast<uint32_t *>(workspace),
@@ -519,12 +536,10 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
     if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
     const bool f16 = precision == SK_PRECISION_F16ACC;
     size_t best = 0;
-    // the register plan (A aligned, lda = n): SK_VARIANT_REG, and the
-    // default, which takes it where it covers the shape
+    // the register plans (lda = n, either alignment): SK_VARIANT_REG, and
+    // the default, which takes it where it covers the shape
     if (!(flags & SK_VARIANT_LDS)) {
-        sk::FusedPlan fp{};
-        if (sk::plan_fused(di, f16, m, n, n, true, d, zeta, &fp) && zeta <= sk::kFusedMetaMaxZeta)
-            best = fp.ws_bytes;
+        if (zeta <= sk::kFusedMetaMaxZeta) best = fused_ws_bytes(di, f16, m, n, d, zeta);
         if (flags & SK_VARIANT_REG) {
             *bytes = best;
             return SK_OK;
@@ -623,7 +638,7 @@ sk_status sk_sketch_workspace_size(int32_t precision, int64_t m, int32_t n, int3
 }
 
 sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
-                                 int32_t a_aligned, int32_t d, int32_t zeta, int32_t num_cu,
+                                 int32_t a_align, int32_t d, int32_t zeta, int32_t num_cu,
                                  int32_t max_lds, int64_t *out) {
     if (out == nullptr) return SK_ERR_NULL;
     for (int i = 0; i < SK_FUSED_PLAN_FIELDS; ++i) out[i] = 0;
@@ -634,12 +649,11 @@ sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_
     if (num_cu < 1 || max_lds < 1) return SK_ERR_ARG;
     sk::DevInfo di{num_cu, max_lds};
     sk::FusedPlan p{};
-    if (!sk::plan_fused(di, precision == SK_PRECISION_F16ACC, m, n, lda, a_aligned != 0, d, zeta,
-                        &p))
+    if (!sk::plan_fused(di, precision == SK_PRECISION_F16ACC, m, n, lda, a_align, d, zeta, &p))
         return SK_OK;
     const int64_t v[SK_FUSED_PLAN_FIELDS] = {1, p.rows_per_wave, p.groups, p.slices,
                                              p.rows_per_chunk, p.chunks, p.grid,
-                                             (int64_t)p.ws_bytes};
+                                             (int64_t)p.ws_bytes, p.words, p.stage_rows};
     for (int i = 0; i < SK_FUSED_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }

@@ -44,10 +44,20 @@
 namespace sk {
 namespace {
 
-constexpr int kStage = 128;             // input rows per LDS stage
 constexpr int kWaves = 16;              // wavefronts per workgroup
-constexpr int kRowsPerWave = kStage / kWaves;
-constexpr int kLaneGroups = kStage / 64;
+
+// W words of a lane's partial row in one LDS access (ds_read_b64 / _b128)
+template <int W> struct WordVec;
+template <> struct WordVec<2> { typedef uint2 type; };
+template <> struct WordVec<4> { typedef uint4 type; };
+__device__ __forceinline__ uint32_t word(const uint2 &x, int j) { return j == 0 ? x.x : x.y; }
+__device__ __forceinline__ uint32_t word(const uint4 &x, int j) {
+    return j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w;
+}
+__device__ __forceinline__ void set_words(uint2 &x, const uint32_t *w) { x = make_uint2(w[0], w[1]); }
+__device__ __forceinline__ void set_words(uint4 &x, const uint32_t *w) {
+    x = make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 // META: the metadata is read from row_idx / val (the stored-metadata
 // apply, zeta <= kFusedMetaMaxZeta) instead of drawn: each wavefront loads
@@ -56,16 +66,23 @@ constexpr int kLaneGroups = kStage / 64;
 // so the main loop assumes every |val| = scale (sk_meta_generate's
 // values); a workgroup whose chunk holds any other value redoes the chunk
 // afterwards with a per-hit product from raw rows.
-template <class T, int R, int P, bool META>
+// W: words per lane (2: 64-lane slices of 128 words, 128-row stages; 4:
+// slices of 256 words, 64-row stages, so the stage buffers keep the same
+// LDS bytes and each hit covers twice the columns).
+template <class T, int W, int R, int P, bool META>
 __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs args) {
-    constexpr int K = 2 * T::kCols;     // floats of A per lane per row
+    constexpr int K = W * T::kCols;     // floats of A per lane per row
     typedef FVec<K> vec_t;
-    constexpr int S = kStage, D = kRowsPerWave, NL = kLaneGroups;
+    typedef typename WordVec<W>::type wv_t;
+    constexpr int S = W == 2 ? 128 : 64;    // input rows per LDS stage
+    constexpr int D = S / kWaves;           // rows each wave loads per stage
+    constexpr int NL = S / 64;              // lane groups of a stage's entries
+    static_assert(sizeof(wv_t) * 2 * S * 64 == 2 * 128 * 64 * 8, "stage bytes");
     // both stage buffers, contiguous: stage contributions, row j of buffer b
     // at [(b*S + j)*64, +64); the general redo holds one stage of raw rows
-    __shared__ uint2 hs[2 * S * 64];
-    uint2 *const hs0 = hs;
-    uint2 *const hs1 = hs + S * 64;
+    __shared__ wv_t hs[2 * S * 64];
+    wv_t *const hs0 = hs;
+    wv_t *const hs1 = hs + S * 64;
     // entry (t, j) at t*S + j: bucket | sign << 31
     __shared__ uint32_t me0[kFusedMaxZeta * S];
     __shared__ uint32_t me1[kFusedMaxZeta * S];
@@ -105,9 +122,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
     const uint32_t cbits = __float_as_uint(c);
     bool gen = false;                   // META: this lane staged a general value
 
-    uint32_t acc[R][2];
+    uint32_t acc[R][W];
 #pragma unroll
-    for (int k = 0; k < R; ++k) acc[k][0] = acc[k][1] = 0u;
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+        for (int j = 0; j < W; ++j) acc[k][j] = 0u;
 
     // rows [u0, u1) of this wave's share of stage s, clamped into the chunk
     vec_t a[P][D];
@@ -136,11 +155,14 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
         }
     };
     // contributions of loaded rows [u0, u1) into stage buffer buf
-    auto stage = [&](const vec_t (&av)[D], uint2 *buf, int u0, int u1) {
+    auto stage = [&](const vec_t (&av)[D], wv_t *buf, int u0, int u1) {
 #pragma unroll
-        for (int u = u0; u < u1; ++u)
-            buf[(wave * D + u) * 64 + lane] =
-                make_uint2(T::contrib(av[u].x, c), T::contrib(av[u].x + T::kCols, c));
+        for (int u = u0; u < u1; ++u) {
+            uint32_t w[W];
+#pragma unroll
+            for (int j = 0; j < W; ++j) w[j] = T::contrib(av[u].x + j * T::kCols, c);
+            set_words(buf[(wave * D + u) * 64 + lane], w);
+        }
     };
     // META: this wave's entries of a stage into me (bucket | sign << 31;
     // 0x7FFFFFFF, which no wave owns, for an entry outside its block), and
@@ -197,7 +219,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
     // word is read from the hit's lane into a scalar register (one VALU
     // readlane instead of three scalar shifts: the scalar unit, shared by
     // the CU's waves, is the busier one in this loop)
-    auto process = [&](const uint2 *buf, int k0, int k1) {
+    auto process = [&](const wv_t *buf, int k0, int k1) {
 #pragma unroll
         for (int k = k0; k < k1; ++k) {
 #pragma unroll
@@ -206,10 +228,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
                 while (mk) {
                     const int i = __builtin_ctzll(mk);
                     mk &= mk - 1;
-                    const uint2 x = buf[(h * 64 + i) * 64 + lane];
+                    const wv_t x = buf[(h * 64 + i) * 64 + lane];
                     const uint32_t u = __builtin_amdgcn_readlane(su[h], i);
-                    acc[k][0] = T::fma_unit(x.x, u, acc[k][0]);
-                    acc[k][1] = T::fma_unit(x.y, u, acc[k][1]);
+#pragma unroll
+                    for (int j = 0; j < W; ++j) acc[k][j] = T::fma_unit(word(x, j), u, acc[k][j]);
                 }
             }
         }
@@ -272,7 +294,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
             // values in me1, every hit adding the rounded product a * val
             float *raw = reinterpret_cast<float *>(hs);   // row j, lane l at (j*64 + l)*K
 #pragma unroll
-            for (int k = 0; k < R; ++k) acc[k][0] = acc[k][1] = 0u;
+            for (int k = 0; k < R; ++k)
+#pragma unroll
+                for (int j = 0; j < W; ++j) acc[k][j] = 0u;
             for (int32_t s = 0; s < nst; ++s) {
                 vec_t av[D];
                 load(s, av, 0, D);
@@ -299,9 +323,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
                             mk &= mk - 1;
                             const float v = __uint_as_float(__builtin_amdgcn_readlane(vv[h], i));
                             const float *xr = raw + ((h * 64 + i) * 64 + lane) * K;
-                            acc[k][0] = T::fma_unit(T::contrib(xr, v), T::unit(0u), acc[k][0]);
-                            acc[k][1] =
-                                T::fma_unit(T::contrib(xr + T::kCols, v), T::unit(0u), acc[k][1]);
+#pragma unroll
+                            for (int j = 0; j < W; ++j)
+                                acc[k][j] = T::fma_unit(T::contrib(xr + j * T::kCols, v), T::unit(0u),
+                                                        acc[k][j]);
                         }
                     }
                 }
@@ -310,22 +335,33 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
         }
     }
 
-    // the wave's R partial rows of this (slice, chunk)
-    uint32_t *dst = args.ws + ((int64_t)slice * args.chunks + chunk) * (int64_t)args.d * 128 +
-                    (int64_t)lo * 128 + lane * 2;
+    // the wave's R partial rows of this (slice, chunk), in the workspace's
+    // 128-word slices: a W = 4 slice is two of them, lanes 0-31 in the first
+    const int32_t half = W == 2 ? 0 : lane >> 5;
+    uint32_t *dst = args.ws +
+                    ((int64_t)(slice * (W / 2) + half) * args.chunks + chunk) * (int64_t)args.d * 128 +
+                    (int64_t)lo * 128 + ((lane * W) & 127);
 #pragma unroll
-    for (int k = 0; k < R; ++k)
-        *reinterpret_cast<uint2 *>(dst + k * 128) = make_uint2(acc[k][0], acc[k][1]);
+    for (int k = 0; k < R; ++k) set_words(*reinterpret_cast<wv_t *>(dst + k * 128), acc[k]);
 }
 
-// The built (R, P) pairs: two register sets where the R rows leave room
-// for them (R = 8, 16), one set (loaded in two halves when R = 4) otherwise.
+// The built (W, R, P) triples.  W = 2: two register sets where the R rows
+// leave room for them (R = 8, 16), one set (loaded in two halves when
+// R = 4) otherwise.  W = 4 (FP32 only): R = 8, 16 with two sets.
 template <class T, bool META>
-const void *pick_fused(int R, int P) {
-    if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 4, 1, META>;
-    if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 8, 2, META>;
-    if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 16, 2, META>;
-    if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 32, 1, META>;
+const void *pick_fused(int W, int R, int P) {
+    if (W == 2) {
+        if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 2, 4, 1, META>;
+        if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 2, 8, 2, META>;
+        if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 2, 16, 2, META>;
+        if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 2, 32, 1, META>;
+    }
+    if constexpr (T::kCols == 1) {
+        if (W == 4) {
+            if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 4, 8, 2, META>;
+            if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 4, 16, 2, META>;
+        }
+    }
     return nullptr;
 }
 
@@ -333,13 +369,14 @@ template <class T>
 hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int64_t ldb_units,
                           int32_t units, int accumulate, hipStream_t s) {
     const bool meta = fa.row_idx != nullptr;
-    const void *kern = meta ? pick_fused<T, true>(p.rows_per_wave, p.load_sets)
-                            : pick_fused<T, false>(p.rows_per_wave, p.load_sets);
+    const void *kern = meta ? pick_fused<T, true>(p.words, p.rows_per_wave, p.load_sets)
+                            : pick_fused<T, false>(p.words, p.rows_per_wave, p.load_sets);
     // the kernel's row ownership must match the plan the workspace was
     // sized for: 16 waves x R rows x groups cover d exactly; with stored
     // metadata a wave's rows of a stage hold at most 64 entries
     if (kern == nullptr || (int64_t)kWaves * p.rows_per_wave * p.groups != fa.d ||
-        fa.groups != p.groups || fa.zeta < 1 || fa.zeta > kFusedMaxZeta || fa.ws == nullptr ||
+        fa.groups != p.groups || fa.slices != p.slices || fa.rows_per_chunk % p.stage_rows != 0 ||
+        fa.zeta < 1 || fa.zeta > kFusedMaxZeta || fa.ws == nullptr ||
         (meta && (fa.val == nullptr || fa.zeta > kFusedMetaMaxZeta)))
         return hipErrorInvalidValue;
     FusedArgs a = fa;
@@ -353,57 +390,77 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
     r.units = units;
     r.d = fa.d;
     r.chunks = fa.chunks;
-    r.slices = fa.slices;
+    r.slices = fa.slices * (p.words / 2);       // in 128-word workspace slices
     return launch_stack_reduce<T>(r, 128, accumulate, s);
 }
 
 }  // namespace
 
-// Plan of the fused kernel.  Rows per wave R = d / (16 G) for the fewest
-// row groups G with R <= 32 (two words x R rows of registers per lane) and
-// R dividing d/zeta (a wave's rows inside one block); R must be one of the
-// built 4, 8, 16, 32.  Chunks are sized so one workgroup per CU fills the
-// device, in whole stages.  Matrices under 64 columns are left to the
-// metadata + LDS apply path.  (From 64 columns on the fused kernel is
-// faster even with most lanes of its slice idle: a narrow sketch is bound
-// by the per-hit instructions, which do not depend on the active lanes.)
-bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
-                bool a_aligned, int32_t d, int32_t zeta, FusedPlan *p) {
-    const int K = f16 ? 4 : 2;
-    if (m < 1 || zeta > kFusedMaxZeta || n % K != 0 || lda % K != 0 || !a_aligned) return false;
+// Plan of the fused kernel.  Words per lane W = 4 (256 FP32 columns per
+// slice, 64-row stages) for FP32 matrices wider than 128 columns whose rows
+// allow 16-byte lane loads: a hit then covers twice the columns, which
+// halves the hit loop's instructions per byte (at the cost of more row
+// groups, whose re-reads of A hit L2).  Else W = 2 (256 FP16 / 128 FP32
+// columns, 128-row stages).  Rows per wave R = d / (16 G) for the fewest
+// row groups G with R <= 32 / (W / 2) (W x R partial words per lane) and R
+// dividing d/zeta (a wave's rows inside one block); R must be one of the
+// built sizes.  Chunks are sized so one workgroup per CU fills the device,
+// in whole stages.  Matrices under 64 columns are left to the metadata +
+// LDS apply path.  (From 64 columns on the fused kernel is faster even with
+// most lanes of its slice idle: a narrow sketch is bound by the per-hit
+// instructions, which do not depend on the active lanes.)
+namespace {
+bool plan_rows(int32_t d, int32_t zeta, int W, int *R_out, int *G_out) {
+    const int64_t db = d / zeta;
+    const int rmax = W == 2 ? 32 : 16, rmin = W == 2 ? 4 : 8;
+    for (int g = 1; (int64_t)kWaves * g <= d; g *= 2) {
+        if (d % (kWaves * g) != 0) break;
+        const int64_t r = d / (kWaves * g);
+        if (r > rmax) continue;
+        if (r < rmin || (r & (r - 1)) != 0) break;
+        if (db % r == 0) {
+            *R_out = (int)r;
+            *G_out = g;
+            return true;
+        }
+    }
+    return false;
+}
+}  // namespace
+
+bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
+                int32_t d, int32_t zeta, FusedPlan *p) {
+    const int K2 = f16 ? 4 : 2;         // floats per lane at W = 2
+    if (m < 1 || zeta > kFusedMaxZeta || n % K2 != 0 || lda % K2 != 0 || a_align < K2 * 4)
+        return false;
     if (n < 64 || d % kWaves != 0) return false;
     if (di.max_lds < kFusedLdsBytes) return false;
     // the kernel indexes rows inside a chunk with 32-bit integers
     if (m > (int64_t)65535 << 30) return false;
-    const int64_t db = d / zeta;
-    int R = 0, G = 0;
-    for (int g = 1; (int64_t)kWaves * g <= d; g *= 2) {
-        if (d % (kWaves * g) != 0) break;
-        const int64_t r = d / (kWaves * g);
-        if (r > 32) continue;
-        if (r != 4 && r != 8 && r != 16 && r != 32) break;
-        if (db % r == 0) {
-            R = (int)r;
-            G = g;
-            break;
-        }
-    }
-    if (R == 0) return false;
+    int W = 2, R = 0, G = 0;
+    if (!f16 && n > 128 && n % 4 == 0 && lda % 4 == 0 && a_align >= 16 &&
+        plan_rows(d, zeta, 4, &R, &G))
+        W = 4;
+    else if (!plan_rows(d, zeta, 2, &R, &G))
+        return false;
+    const int K = W * (f16 ? 2 : 1);
+    p->words = W;
+    p->stage_rows = W == 2 ? 128 : 64;
     p->rows_per_wave = R;
     p->groups = G;
     p->load_sets = (R == 8 || R == 16) ? 2 : 1;
     p->slices = (n + 64 * K - 1) / (64 * K);
     const int64_t per_chunk = p->slices * G;
     int64_t want = (di.num_cu + per_chunk - 1) / per_chunk;
-    const int64_t stages = (m + kStage - 1) / kStage;
+    const int64_t stages = (m + p->stage_rows - 1) / p->stage_rows;
     if (want > stages) want = stages;
     if (want > 65535) want = 65535;
     if (want < 1) want = 1;
     const int64_t st_per_chunk = (stages + want - 1) / want;
-    p->rows_per_chunk = st_per_chunk * kStage;
+    p->rows_per_chunk = st_per_chunk * p->stage_rows;
     p->chunks = (m + p->rows_per_chunk - 1) / p->rows_per_chunk;
     p->grid = (p->slices * p->chunks + 7) / 8 * 8 * G;
-    p->ws_bytes = (size_t)p->slices * (size_t)p->chunks * (size_t)d * 128 * 4;
+    p->ws_bytes = (size_t)p->slices * (W / 2) * (size_t)p->chunks * (size_t)d * 128 * 4;
     return true;
 }
 

@@ -73,12 +73,14 @@ constexpr int kFusedMaxZeta = 16;
 // with stored metadata (8 rows x zeta entries per wavefront and stage, one
 // per lane)
 constexpr int kFusedMetaMaxZeta = 8;
-// static LDS of the fused kernel: two 128-row stages of 64 lanes x 8 bytes,
-// two metadata stages of kFusedMaxZeta x 128 entries and 16 per-wave votes
+// static LDS of the fused kernel (an upper bound over its word widths): two
+// stages of 128 rows x 64 lanes x 8 bytes (or 64 rows x 64 lanes x 16
+// bytes), two metadata stages of at most kFusedMaxZeta x 128 entries and 16
+// per-wave votes
 constexpr int kFusedLdsBytes = 2 * 128 * 64 * 8 + 2 * kFusedMaxZeta * 128 * 4 + 16 * 4;
 struct FusedArgs {
     const float *A;
-    uint32_t *ws;               // [slices][chunks][d][128] partial words
+    uint32_t *ws;               // [slices * words/2][chunks][d][128] partial words
     const int32_t *row_idx;     // stored metadata (NULL: drawn in the kernel)
     const float *val;
     int64_t m, lda, rows_per_chunk, row_offset;
@@ -88,19 +90,24 @@ struct FusedArgs {
     float scale;                // float32(1/sqrt(zeta))
 };
 struct FusedPlan {
+    int words;                  // W: partial words per lane and output row (2 or 4)
+    int stage_rows;             // input rows per LDS stage (128 at W = 2, 64 at W = 4)
     int rows_per_wave;          // R: output rows kept in one wavefront's registers
     int groups;                 // G: output row groups (each reads A once)
     int load_sets;              // P: stages of rows in flight in registers (1 or 2)
-    int64_t slices;             // column slices (256 FP16 / 128 FP32 columns)
-    int64_t rows_per_chunk;     // input rows per workgroup (whole 128-row stages)
+    int64_t slices;             // column slices of 64 lanes x W words (W = 2: 256 FP16 /
+                                // 128 FP32 columns; W = 4: 256 FP32 columns)
+    int64_t rows_per_chunk;     // input rows per workgroup (whole stages)
     int64_t chunks;
     int64_t grid;               // workgroups (1-D, XCD-grouped)
     size_t ws_bytes;            // partial workspace
 };
-// a_aligned: A's base allows the kernel's lane loads (16 bytes for FP16,
-// 8 for FP32).  False: the fused kernel does not cover this call.
-bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda,
-                bool a_aligned, int32_t d, int32_t zeta, FusedPlan *plan);
+// a_align: the alignment of A's base in bytes (16 or more: any lane load;
+// the kernel needs 16 for FP16 and for W = 4, 8 for FP32 at W = 2).  A plan
+// the alignment does not allow returns false: the fused kernel does not
+// cover the call.
+bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
+                int32_t d, int32_t zeta, FusedPlan *plan);
 // Fused kernel into ws, then the chunk-order reduce into B (=, or += when
 // accumulate).  B is float* (FP32) or FP16 bits (uint16_t*), ldb in elements.
 // row_idx / val NULL: the metadata is drawn from (seed, row_offset) in the

@@ -285,21 +285,26 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
     f16 = precision == b.SK_PRECISION_F16ACC
     if f16 and n % 2:
         pytest.skip("odd n")
-    K = 4 if f16 else 2
-    p = b.sk_fused_plan_describe(precision, m, n, n, True, d, zeta, **MI355X)
+    K2 = 4 if f16 else 2                # floats per lane at two words per lane
+    p = b.sk_fused_plan_describe(precision, m, n, n, 16, d, zeta, **MI355X)
     if not p["fused"]:
-        assert (zeta > 16 or n % K or n < 32 * K or d % 16
+        assert (zeta > 16 or n % K2 or n < 32 * K2 or d % 16
                 or all((d // (16 * g)) not in (4, 8, 16, 32) or (d // zeta) % (d // (16 * g))
                        for g in (1, 2, 4, 8, 16, 32) if d % (16 * g) == 0))
         return
+    W, S = p["words"], p["stage_rows"]
+    # four words per lane only for FP32 wider than 128 columns, 64-row stages
+    assert (W, S) in ((2, 128), (4, 64))
+    assert W == 2 or (not f16 and n > 128 and n % 4 == 0)
+    K = W * (2 if f16 else 1)
     R, g = p["rows_per_wave"], p["groups"]
-    assert R in (4, 8, 16, 32) and 16 * R * g == d
+    assert R in ((4, 8, 16, 32) if W == 2 else (8, 16)) and 16 * R * g == d
     db = d // zeta
     assert db % R == 0
-    assert p["rows_per_chunk"] % 128 == 0
+    assert p["rows_per_chunk"] % S == 0
     assert p["chunks"] * p["rows_per_chunk"] >= m > (p["chunks"] - 1) * p["rows_per_chunk"]
     assert p["slices"] * 64 * K >= n > (p["slices"] - 1) * 64 * K
-    for lane in (0, 63):
+    for lane in (0, 31, 32, 63):
         for sl in range(p["slices"]):
             col = sl * 64 * K + lane * K
             assert 0 <= min(col, n - K) and min(col, n - K) + K <= n
@@ -316,25 +321,49 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
             lo = (grp * 16 + wave) * R
             t = lo // db
             assert t < zeta and t * db <= lo and lo + R <= (t + 1) * db
-            last = ((sl * p["chunks"] + ch) * d + lo + R - 1) * 128 + 63 * 2 + 1
-            assert (last + 1) * 4 <= p["ws_bytes"]
+            for lane in (0, 31, 32, 63):
+                # a lane's W words in the workspace's 128-word slices
+                half = 0 if W == 2 else lane >> 5
+                first = (((sl * (W // 2) + half) * p["chunks"] + ch) * d + lo) * 128 \
+                    + ((lane * W) & 127)
+                last = first + (R - 1) * 128 + W - 1
+                assert first >= 0 and (last + 1) * 4 <= p["ws_bytes"]
+                # the reduce reads 128-word slice s's words below n (units)
+                col_word = (sl * (W // 2) + half) * 128 + ((lane * W) & 127)
+                assert col_word == sl * 64 * W + lane * W
     assert len(seen) == p["slices"] * p["chunks"] * g
     # the fused kernel's metadata stage holds at most 16 blocks
     assert zeta <= 16
 
 
+def test_fused_plan_word_width(lib):
+    """FP32 matrices wider than 128 columns with 16-byte rows take four
+    words per lane (256 columns per workgroup, two row groups at d = 512);
+    an 8-byte-aligned base, lda % 4 != 0, 128 columns or FP16 keep two."""
+    P16, P32 = b.SK_PRECISION_F16ACC, b.SK_PRECISION_F32
+    p = b.sk_fused_plan_describe(P32, 1 << 20, 256, 256, 16, 512, 4, **MI355X)
+    assert (p["fused"], p["words"], p["stage_rows"], p["rows_per_wave"], p["groups"],
+            p["slices"]) == (1, 4, 64, 16, 2, 1)
+    assert p["grid"] == 256 and p["chunks"] == 128
+    for args in ((256, 256, 8), (256, 258, 16), (128, 128, 16)):
+        q = b.sk_fused_plan_describe(P32, 1 << 20, args[0], args[1], args[2], 512, 4, **MI355X)
+        assert (q["fused"], q["words"], q["stage_rows"]) == (1, 2, 128)
+    q = b.sk_fused_plan_describe(P16, 1 << 20, 512, 512, 16, 512, 4, **MI355X)
+    assert (q["fused"], q["words"]) == (1, 2)
+
+
 def test_fused_plan_alignment_and_validation(lib):
     P16, P32 = b.SK_PRECISION_F16ACC, b.SK_PRECISION_F32
-    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, True, 512, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 16, 512, 4, **MI355X)["fused"] == 1
     # misaligned base, odd-multiple lda, narrow rows: left to the fallback
-    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, False, 512, 4, **MI355X)["fused"] == 0
-    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 258, True, 512, 4, **MI355X)["fused"] == 0
-    assert b.sk_fused_plan_describe(P32, 1 << 20, 256, 257, True, 512, 4, **MI355X)["fused"] == 0
-    assert b.sk_fused_plan_describe(P16, 1 << 20, 64, 64, True, 128, 4, **MI355X)["fused"] == 1
-    assert b.sk_fused_plan_describe(P16, 1 << 20, 60, 60, True, 128, 4, **MI355X)["fused"] == 0
-    assert b.sk_fused_plan_describe(P32, 1 << 20, 62, 62, True, 128, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 8, 512, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 258, 16, 512, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 256, 257, 16, 512, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 64, 64, 16, 128, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 60, 60, 16, 128, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 62, 62, 16, 128, 4, **MI355X)["fused"] == 0
     # LDS smaller than the kernel's stages
-    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, True, 512, 4, num_cu=256,
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 16, 512, 4, num_cu=256,
                                     max_lds=64 * 1024)["fused"] == 0
     out = (ctypes.c_int64 * len(b.FUSED_PLAN_FIELDS))()
     assert lib.sk_fused_plan_describe(0, 10, 0, 8, 1, 8, 1, 256, 163840, out) == b.SK_ERR_SHAPE

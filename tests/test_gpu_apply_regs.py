@@ -22,7 +22,7 @@ PREC = {"f32": b.SK_PRECISION_F32, "f16acc": b.SK_PRECISION_F16ACC}
 
 
 def reg_plan(precision, m, n, d, zeta, lda=None):
-    return b.sk_fused_plan_describe(PREC[precision], m, n, lda or n, True, d, zeta, **MI355X)
+    return b.sk_fused_plan_describe(PREC[precision], m, n, lda or n, 16, d, zeta, **MI355X)
 
 
 def run_reg(A, ri, v, zeta, d, precision, flags=b.SK_VARIANT_REG, out=None):
@@ -32,18 +32,24 @@ def run_reg(A, ri, v, zeta, d, precision, flags=b.SK_VARIANT_REG, out=None):
     return B
 
 
+# (m, n, d, zeta, plan): plan = (words per lane, R, G) for FP16 and, where
+# FP32 takes four words per lane (wider than 128 columns), for FP32
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
-@pytest.mark.parametrize("m,n,d,zeta,R,G", [
-    (4096, 256, 64, 4, 4, 1),       # R = 4
-    (3000, 128, 128, 4, 8, 1),      # R = 8, a short last stage
-    (5000, 260, 256, 8, 16, 1),     # R = 16, zeta = 8, ragged second slice
-    (4096, 128, 512, 8, 32, 1),     # R = 32
-    (2500, 136, 1024, 1, 32, 2),    # two row groups (A read twice)
+@pytest.mark.parametrize("m,n,d,zeta,plan16,plan32", [
+    (4096, 256, 64, 4, (2, 4, 1), (2, 4, 1)),         # R = 4 (too few rows for four words)
+    (3000, 128, 128, 4, (2, 8, 1), (2, 8, 1)),        # R = 8, a short last stage
+    (5000, 260, 256, 8, (2, 16, 1), (4, 16, 1)),      # R = 16, zeta = 8, ragged second slice
+    (4096, 128, 512, 8, (2, 32, 1), (2, 32, 1)),      # R = 32
+    (2500, 136, 1024, 1, (2, 32, 2), (4, 16, 4)),     # row groups (A read 2 / 4 times)
+    (3001, 256, 512, 4, (2, 32, 1), (4, 16, 2)),      # FP32 four words, ragged 64-row stage
+    (777, 512, 128, 2, (2, 8, 1), (4, 8, 1)),         # FP32 four words, R = 8, two slices
 ])
-def test_register_apply_vs_oracle(precision, m, n, d, zeta, R, G):
+def test_register_apply_vs_oracle(precision, m, n, d, zeta, plan16, plan32):
     say(f"register apply {precision} m={m} n={n} d={d} zeta={zeta}")
     p = reg_plan(precision, m, n, d, zeta)
-    assert p["fused"] == 1 and (p["rows_per_wave"], p["groups"]) == (R, G)
+    assert p["fused"] == 1
+    assert (p["words"], p["rows_per_wave"], p["groups"]) == (plan32 if precision == "f32"
+                                                             else plan16)
     A = inputs.gaussian(m, n, seed=3)
     ri, v = b.meta(5, m, d, zeta, device=dev())
     B = run_reg(A, ri, v, zeta, d, precision).float().cpu().numpy().astype(np.float64)
@@ -53,13 +59,16 @@ def test_register_apply_vs_oracle(precision, m, n, d, zeta, R, G):
 
 
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
-def test_register_exact_inputs_and_general_values(precision):
+@pytest.mark.parametrize("n", [128, 256])
+def test_register_exact_inputs_and_general_values(precision, n):
     """Integer A (FP32) / {-1,0,1} A (FP16) with stored values scaled by
     dyadic factors: every product and partial sum is exact, so B equals
     fp64 bit for bit; values differ from entry to entry (every chunk takes
     the kernel's per-hit-product redo), or a single entry differs (one
-    workgroup's chunk does)."""
-    m, n, d, zeta = 3000, 128, 128, 4
+    workgroup's chunk does).  FP32 at 256 columns runs four words per
+    lane."""
+    m, d, zeta = 3000, 128, 4
+    say(f"register exact/general {precision} n={n}")
     lo, hi = (-8, 8) if precision == "f32" else (-1, 1)
     A = inputs.integer_matrix(m, n, lo, hi, seed=13)
     ri_h, v_h = oracle.meta_ref(9, m, d, zeta)

@@ -24,7 +24,7 @@ PREC = {"f32": b.SK_PRECISION_F32, "f16acc": b.SK_PRECISION_F16ACC}
 
 
 def fused_used(precision, m, n, lda, d, zeta):
-    return b.sk_fused_plan_describe(PREC[precision], m, n, lda, True, d, zeta, **MI355X)["fused"]
+    return b.sk_fused_plan_describe(PREC[precision], m, n, lda, 16, d, zeta, **MI355X)["fused"]
 
 
 def run_fused(A, d, zeta, seed, precision, row_offset=0, out=None, flags=0):
@@ -35,18 +35,25 @@ def run_fused(A, d, zeta, seed, precision, row_offset=0, out=None, flags=0):
 
 
 # (m, n, d, zeta): rows per wave 4, 8, 16, 32; row groups 1 and 2; one and
-# several column slices; ragged row counts and single partial stages
+# several column slices; ragged row counts and single partial stages.  FP32
+# wider than 128 columns takes four words per lane (64-row stages): the
+# 256-, 384-, 260- and 512-column shapes cover R = 8 and 16, one to four row
+# groups and ragged slices there.  zeta is 1, 4 or 16 (scale a power of two)
+# so that integer inputs keep every product exact.
 FUSED_SHAPES = [
     (4096, 128, 64, 4),         # R = 4
     (4096, 128, 64, 1),         # CountSketch
     (3001, 256, 128, 4),        # R = 8, ragged last stage
     (1000, 128, 256, 16),       # R = 16, zeta = 16 (four Philox blocks per row)
-    (2500, 384, 512, 4),        # R = 32, two FP16 / three FP32 slices, ragged slice
+    (2500, 384, 512, 4),        # R = 32 (FP32: 16, two groups), two slices, ragged slice
     (5000, 128, 1024, 4),       # two row groups
     (129, 256, 512, 1),         # one stage plus one row
     (1, 128, 64, 4),            # a single row
     (4096, 64, 128, 4),         # 64 columns: a quarter (FP16) / half (FP32) of the slice's lanes
     (3000, 68, 64, 4),          # 68 columns, lanes past the row clamped
+    (6000, 512, 1024, 4),       # FP32 four words: R = 16, four row groups, two slices
+    (2049, 260, 256, 16),       # FP32 four words: a 4-column second slice, zeta = 16
+    (65, 256, 256, 4),          # FP32 four words: one 64-row stage plus one row
 ]
 
 
@@ -148,6 +155,29 @@ def test_fused_fallback_shapes(precision, m, n, d, zeta, lda):
     ri, v = oracle.meta_ref(8, m, d, zeta)
     ref = oracle.sketch_f64(np.ascontiguousarray(A[:, :n]), ri, v, d, zeta)
     assert np.array_equal(B, ref)
+
+
+@pytest.mark.parametrize("offset,lda", [(0, 256), (2, 258), (2, 256), (1, 257)])
+def test_fused_f32_word_width_by_alignment(offset, lda):
+    """FP32 rows of 256 columns: a 16-byte base with lda % 4 == 0 takes four
+    words per lane, an 8-byte base or lda % 4 == 2 two words, a 4-byte base
+    the fallback; every plan gives the same exact sketch, and the workspace
+    the size query reports suffices for each."""
+    m, n, d, zeta = 3000, 256, 512, 4
+    say(f"fused f32 alignment offset={offset} lda={lda}")
+    A = inputs.integer_matrix(m + 1, lda, -8, 8, seed=12)
+    flat = to_dev(A).reshape(-1)
+    Ad = flat[offset:offset + m * lda].reshape(m, lda)[:, :n]
+    align = 16 if offset == 0 else 8 if offset == 2 else 4
+    assert Ad.data_ptr() % 16 == (0 if offset == 0 else offset * 4)
+    p = b.sk_fused_plan_describe(b.SK_PRECISION_F32, m, n, lda, align, d, zeta, **MI355X)
+    want = (1, 4) if (align == 16 and lda % 4 == 0) else (1, 2) if align >= 8 and lda % 2 == 0 \
+        else (0, 0)
+    assert (p["fused"], p["words"]) == want
+    B = run_fused(Ad, d, zeta, 21, "f32")
+    A_host = np.ascontiguousarray(A.reshape(-1)[offset:offset + m * lda].reshape(m, lda)[:, :n])
+    ri, v = oracle.meta_ref(21, m, d, zeta)
+    assert np.array_equal(B, oracle.sketch_f64(A_host, ri, v, d, zeta))
 
 
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
