@@ -47,8 +47,8 @@ SEED = 1
 # FETCH_SIZE and WRITE_SIZE passes over bench.py --profile-pass (KiB per
 # dispatch; FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a 1 GiB device
 # copy reads on the same counters).  Valid for the kernels named here only.
-TRAFFIC = {"kernels": ("k_stack_fused<AccF16,32,1,false>", "k_stack_reduce<AccF16>"),
-           "fetch_kib": (524_702, 32_803), "write_kib": (65_536, 256),
+TRAFFIC = {"kernels": ("k_stack_fused<AccF16,2,32,1,false>", "k_stack_reduce<AccF16>"),
+           "fetch_kib": (524_691, 32_803), "write_kib": (65_536, 256),
            "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -202,6 +202,8 @@ def main():
     if args.profile_pass:
         for _ in range(3):
             fused16()
+        for _ in range(3):
+            fused32()
         meta()
         for _ in range(3):
             f16(b.SK_VARIANT_LDS)
@@ -221,7 +223,8 @@ def main():
             b.sk_apply_blockperm_ex(Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, 1,
                                     b.SK_WIRING_SHIFT, SEED, Y, BP_N, 0, wsbp, wsbp.numel(), sp)
         torch.cuda.synchronize()
-        print("profile pass done: 3 x fused f16 sketch, 3 x f16 LDS apply + reduce, "
+        print("profile pass done: 3 x fused f16 sketch, 3 x fused f32 sketch, "
+              "3 x f16 LDS apply + reduce, "
               "3 x f16 register apply + reduce, 3 x 1 GiB copy, 3 x BlockPerm (register "
               "kernel + reduce)", flush=True)
         return
@@ -467,7 +470,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_bytes(),
-                     "kernel": "k_stack_fused<AccF16,32,1,false> + k_stack_reduce<AccF16>",
+                     "kernel": "k_stack_fused<AccF16,2,32,1,false> + k_stack_reduce<AccF16>",
                      "kernel_ms": round(ms16, 5), "algorithmic_bytes": fbytes16,
                      "apply_atomic_flush_ms": round(ms_kernel_atomic, 5)},
         "cpu_baseline": None,
