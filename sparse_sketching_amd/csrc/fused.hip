@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
                 uint64_t mk = __ballot(rl[h] == k);
                 while (mk) {
                     const int i = __builtin_ctzll(mk);
-                    mk &= mk - 1;
+                    mk &= ~(1ull << i);     // two scalar ops (mk - 1 takes three)
                     const wv_t x = buf[(h * 64 + i) * 64 + lane];
                     const uint32_t u = __builtin_amdgcn_readlane(su[h], i);
 #pragma unroll
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
                         uint64_t mk = __ballot(rl[h] == k);
                         while (mk) {
                             const int i = __builtin_ctzll(mk);
-                            mk &= mk - 1;
+                            mk &= ~(1ull << i);
                             const float v = __uint_as_float(__builtin_amdgcn_readlane(vv[h], i));
                             const float *xr = raw + ((h * 64 + i) * 64 + lane) * K;
 #pragma unroll
