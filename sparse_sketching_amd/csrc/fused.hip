@@ -66,18 +66,22 @@ __device__ __forceinline__ void set_words(uint4 &x, const uint32_t *w) {
 // so the main loop assumes every |val| = scale (sk_meta_generate's
 // values); a workgroup whose chunk holds any other value redoes the chunk
 // afterwards with a per-hit product from raw rows.
-// W: words per lane (2: 64-lane slices of 128 words, 128-row stages; 4:
-// slices of 256 words, 64-row stages, so the stage buffers keep the same
-// LDS bytes and each hit covers twice the columns).
-template <class T, int W, int R, int P, bool META>
-__global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs args) {
+// W: words per lane (2: 64-lane slices of 128 words; 4: slices of 256
+// words, each hit covers twice the columns).  S: input rows per stage (128
+// at W = 2, 64 at W = 4: 128 KiB of stage buffers either way, one
+// workgroup per CU).  W = 2 with S = 64 is the two-per-CU variant for few
+// rows per wave (R <= 8): 72 KiB of LDS and at most 64 VGPRs, so two
+// workgroups share a CU (8 waves per SIMD) and each hides the other's
+// per-hit LDS latency and stage barriers.
+template <class T, int W, int S, int R, int P, bool META>
+__global__ __launch_bounds__(kWaves * 64, (W == 2 && S == 64) ? 8 : 4) void k_stack_fused(
+    const FusedArgs args) {
     constexpr int K = W * T::kCols;     // floats of A per lane per row
     typedef FVec<K> vec_t;
     typedef typename WordVec<W>::type wv_t;
-    constexpr int S = W == 2 ? 128 : 64;    // input rows per LDS stage
     constexpr int D = S / kWaves;           // rows each wave loads per stage
     constexpr int NL = S / 64;              // lane groups of a stage's entries
-    static_assert(sizeof(wv_t) * 2 * S * 64 == 2 * 128 * 64 * 8, "stage bytes");
+    static_assert(S == 64 || (S == 128 && W == 2), "stage shapes");
     // both stage buffers, contiguous: stage contributions, row j of buffer b
     // at [(b*S + j)*64, +64); the general redo holds one stage of raw rows
     __shared__ wv_t hs[2 * S * 64];
@@ -345,21 +349,27 @@ __global__ __launch_bounds__(kWaves * 64) void k_stack_fused(const FusedArgs arg
     for (int k = 0; k < R; ++k) set_words(*reinterpret_cast<wv_t *>(dst + k * 128), acc[k]);
 }
 
-// The built (W, R, P) triples.  W = 2: two register sets where the R rows
-// leave room for them (R = 8, 16), one set (loaded in two halves when
-// R = 4) otherwise.  W = 4 (FP32 only): R = 8, 16 with two sets.
+// The built (W, S, R, P) shapes.  W = 2, S = 128: two register sets where
+// the R rows leave room for them (R = 16), one set (loaded in two halves)
+// otherwise; R = 4 and 8 are kept for devices where two workgroups do not
+// share a CU.  W = 2, S = 64 (two workgroups per CU): R = 4, 8, one set
+// loaded in two halves.  W = 4 (FP32 only): R = 8, 16 with two sets.
 template <class T, bool META>
-const void *pick_fused(int W, int R, int P) {
-    if (W == 2) {
-        if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 2, 4, 1, META>;
-        if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 2, 8, 2, META>;
-        if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 2, 16, 2, META>;
-        if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 2, 32, 1, META>;
+const void *pick_fused(int W, int S, int R, int P) {
+    if (W == 2 && S == 128) {
+        if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 2, 128, 4, 1, META>;
+        if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 2, 128, 8, 2, META>;
+        if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 2, 128, 16, 2, META>;
+        if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 2, 128, 32, 1, META>;
+    }
+    if (W == 2 && S == 64) {
+        if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 2, 64, 4, 1, META>;
+        if (R == 8 && P == 1) return (const void *)k_stack_fused<T, 2, 64, 8, 1, META>;
     }
     if constexpr (T::kCols == 1) {
-        if (W == 4) {
-            if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 4, 8, 2, META>;
-            if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 4, 16, 2, META>;
+        if (W == 4 && S == 64) {
+            if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 4, 64, 8, 2, META>;
+            if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 4, 64, 16, 2, META>;
         }
     }
     return nullptr;
@@ -369,8 +379,9 @@ template <class T>
 hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int64_t ldb_units,
                           int32_t units, int accumulate, hipStream_t s) {
     const bool meta = fa.row_idx != nullptr;
-    const void *kern = meta ? pick_fused<T, true>(p.words, p.rows_per_wave, p.load_sets)
-                            : pick_fused<T, false>(p.words, p.rows_per_wave, p.load_sets);
+    const void *kern =
+        meta ? pick_fused<T, true>(p.words, p.stage_rows, p.rows_per_wave, p.load_sets)
+             : pick_fused<T, false>(p.words, p.stage_rows, p.rows_per_wave, p.load_sets);
     // the kernel's row ownership must match the plan the workspace was
     // sized for: 16 waves x R rows x groups cover d exactly; with stored
     // metadata a wave's rows of a stage hold at most 64 entries
@@ -444,14 +455,17 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     else if (!plan_rows(d, zeta, 2, &R, &G))
         return false;
     const int K = W * (f16 ? 2 : 1);
+    // few rows per wave: the two-per-CU shape (64-row stages), where the
+    // device's LDS holds two of its workgroups
+    const bool dual = W == 2 && R <= 8 && di.max_lds >= 2 * kFusedDualLdsBytes;
     p->words = W;
-    p->stage_rows = W == 2 ? 128 : 64;
+    p->stage_rows = (W == 2 && !dual) ? 128 : 64;
     p->rows_per_wave = R;
     p->groups = G;
-    p->load_sets = (R == 8 || R == 16) ? 2 : 1;
+    p->load_sets = dual ? 1 : (R == 8 || R == 16) ? 2 : 1;
     p->slices = (n + 64 * K - 1) / (64 * K);
     const int64_t per_chunk = p->slices * G;
-    int64_t want = (di.num_cu + per_chunk - 1) / per_chunk;
+    int64_t want = ((int64_t)di.num_cu * (dual ? 2 : 1) + per_chunk - 1) / per_chunk;
     const int64_t stages = (m + p->stage_rows - 1) / p->stage_rows;
     if (want > stages) want = stages;
     if (want > 65535) want = 65535;

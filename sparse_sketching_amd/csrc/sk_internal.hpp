@@ -78,6 +78,8 @@ constexpr int kFusedMetaMaxZeta = 8;
 // bytes), two metadata stages of at most kFusedMaxZeta x 128 entries and 16
 // per-wave votes
 constexpr int kFusedLdsBytes = 2 * 128 * 64 * 8 + 2 * kFusedMaxZeta * 128 * 4 + 16 * 4;
+// the two-per-CU shape (two words per lane, 64-row stages)
+constexpr int kFusedDualLdsBytes = 2 * 64 * 64 * 8 + 2 * kFusedMaxZeta * 64 * 4 + 16 * 4;
 struct FusedArgs {
     const float *A;
     uint32_t *ws;               // [slices * words/2][chunks][d][128] partial words
@@ -91,7 +93,8 @@ struct FusedArgs {
 };
 struct FusedPlan {
     int words;                  // W: partial words per lane and output row (2 or 4)
-    int stage_rows;             // input rows per LDS stage (128 at W = 2, 64 at W = 4)
+    int stage_rows;             // input rows per LDS stage (128 at W = 2, 64 at W = 4
+                                // and in the two-per-CU shape: W = 2, R <= 8)
     int rows_per_wave;          // R: output rows kept in one wavefront's registers
     int groups;                 // G: output row groups (each reads A once)
     int load_sets;              // P: stages of rows in flight in registers (1 or 2)

@@ -293,8 +293,11 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
                        for g in (1, 2, 4, 8, 16, 32) if d % (16 * g) == 0))
         return
     W, S = p["words"], p["stage_rows"]
-    # four words per lane only for FP32 wider than 128 columns, 64-row stages
-    assert (W, S) in ((2, 128), (4, 64))
+    # four words per lane only for FP32 wider than 128 columns, 64-row
+    # stages; two words with 64-row stages (two workgroups per CU) for R <= 8
+    assert (W, S) in ((2, 128), (4, 64), (2, 64))
+    assert (W, S) != (2, 64) or p["rows_per_wave"] <= 8
+    assert (W, S) != (2, 128) or p["rows_per_wave"] > 8
     assert W == 2 or (not f16 and n > 128 and n % 4 == 0)
     K = W * (2 if f16 else 1)
     R, g = p["rows_per_wave"], p["groups"]
