@@ -132,9 +132,9 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
  *                own output rows' partial in registers; the partials go to
  *                the workspace and a second kernel writes B as their sum.
  *                Needs a workspace, zeta <= 8, d % 16 == 0, n >= 64, n
- *                and lda multiples of 2 (FP32) / 4 (FP16) and A 8 (FP32) /
- *                16 (FP16) byte aligned: shapes sk_fused_plan_describe
- *                reports as covered, with zeta <= 8.  Its fast path
+ *                and lda even and A 8-byte aligned (FP16 wider than 128
+ *                columns: multiples of 4, 16-byte aligned): shapes
+ *                sk_fused_plan_describe reports as covered, with zeta <= 8.  Its fast path
  *                assumes |val| = float32(1/sqrt(zeta)), as sk_meta_generate
  *                writes; a workgroup whose rows hold any other value redoes
  *                them with a per-hit product (about three times slower for
@@ -266,11 +266,12 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
  * allow 16-byte loads (lda % 4 == 0, A 16-byte aligned) take four partial
  * words per lane (256 columns per workgroup) instead of two; the order of
  * each output word's additions is fixed either way.  Shapes the fused
- * kernel does not cover (zeta > 16,
- * d not a multiple of 16, fewer than 64 columns, rows
- * of A not 16-byte (FP16) / 8-byte (FP32) aligned, row ownership that does
- * not fit the registers) run sk_meta_generate into the workspace and then
- * the LDS (or flat) apply; the result is the same sketch.
+ * kernel does not cover (zeta > 16, d not a multiple of 16, fewer than 64
+ * columns, rows of A without 8-byte lane loads (A 8-byte aligned, n and lda
+ * even; FP16 wider than 128 columns: 16-byte, multiples of 4), row
+ * ownership that does not fit the registers) run sk_meta_generate into the
+ * workspace and then the LDS (or flat) apply; the result is the same
+ * sketch.
  *
  *   seed, row_offset  as for sk_meta_generate (row_offset >= 0 is the global
  *            index of A's first row, so row chunks with SK_ACCUMULATE give
@@ -320,10 +321,11 @@ sk_status sk_sketch_workspace_size(int32_t precision, int64_t m, int32_t n, int3
  *   out  int64[SK_FUSED_PLAN_FIELDS], written: {fused kernel used (0: the
  *        fallback runs), output rows per wavefront, output row groups,
  *        column slices, rows per chunk, chunks, workgroups, workspace bytes,
- *        partial words per lane (2 or 4), input rows per stage}.
+ *        partial words per lane (1, 2 or 4), input rows per stage,
+ *        workgroups per CU the plan is sized for (1 or 2)}.
  * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ARG (precision, num_cu, max_lds).
  */
-#define SK_FUSED_PLAN_FIELDS 10
+#define SK_FUSED_PLAN_FIELDS 11
 sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
                                  int32_t a_align, int32_t d, int32_t zeta, int32_t num_cu,
                                  int32_t max_lds, int64_t *out);

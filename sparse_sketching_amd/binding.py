@@ -257,7 +257,7 @@ def sk_sketch_workspace_size(precision, m, n, d, zeta):
 
 
 FUSED_PLAN_FIELDS = ("fused", "rows_per_wave", "groups", "slices", "rows_per_chunk", "chunks",
-                     "grid", "ws_bytes", "words", "stage_rows")
+                     "grid", "ws_bytes", "words", "stage_rows", "per_cu")
 
 
 def sk_fused_plan_describe(precision, m, n, lda, a_align, d, zeta, num_cu, max_lds):

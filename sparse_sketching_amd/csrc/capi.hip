@@ -653,7 +653,8 @@ sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_
         return SK_OK;
     const int64_t v[SK_FUSED_PLAN_FIELDS] = {1, p.rows_per_wave, p.groups, p.slices,
                                              p.rows_per_chunk, p.chunks, p.grid,
-                                             (int64_t)p.ws_bytes, p.words, p.stage_rows};
+                                             (int64_t)p.ws_bytes, p.words, p.stage_rows,
+                                             p.dual ? 2 : 1};
     for (int i = 0; i < SK_FUSED_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }

@@ -48,12 +48,15 @@ constexpr int kWaves = 16;              // wavefronts per workgroup
 
 // W words of a lane's partial row in one LDS access (ds_read_b64 / _b128)
 template <int W> struct WordVec;
+template <> struct WordVec<1> { typedef uint32_t type; };
 template <> struct WordVec<2> { typedef uint2 type; };
 template <> struct WordVec<4> { typedef uint4 type; };
+__device__ __forceinline__ uint32_t word(const uint32_t &x, int) { return x; }
 __device__ __forceinline__ uint32_t word(const uint2 &x, int j) { return j == 0 ? x.x : x.y; }
 __device__ __forceinline__ uint32_t word(const uint4 &x, int j) {
     return j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w;
 }
+__device__ __forceinline__ void set_words(uint32_t &x, const uint32_t *w) { x = w[0]; }
 __device__ __forceinline__ void set_words(uint2 &x, const uint32_t *w) { x = make_uint2(w[0], w[1]); }
 __device__ __forceinline__ void set_words(uint4 &x, const uint32_t *w) {
     x = make_uint4(w[0], w[1], w[2], w[3]);
@@ -67,14 +70,17 @@ __device__ __forceinline__ void set_words(uint4 &x, const uint32_t *w) {
 // values); a workgroup whose chunk holds any other value redoes the chunk
 // afterwards with a per-hit product from raw rows.
 // W: words per lane (2: 64-lane slices of 128 words; 4: slices of 256
-// words, each hit covers twice the columns).  S: input rows per stage (128
-// at W = 2, 64 at W = 4: 128 KiB of stage buffers either way, one
-// workgroup per CU).  W = 2 with S = 64 is the two-per-CU variant for few
-// rows per wave (R <= 8): 72 KiB of LDS and at most 64 VGPRs, so two
-// workgroups share a CU (8 waves per SIMD) and each hides the other's
-// per-hit LDS latency and stage barriers.
-template <class T, int W, int S, int R, int P, bool META>
-__global__ __launch_bounds__(kWaves * 64, (W == 2 && S == 64) ? 8 : 4) void k_stack_fused(
+// words, each hit covers twice the columns; 1 (FP16 only): slices of 64
+// words, 128 columns, for narrow rows: half the accumulator registers per
+// row).  S: input rows per stage (128 at W = 2, 64 at W = 4: 128 KiB of
+// stage buffers either way, one workgroup per CU; 64 at W = 1).  DUAL:
+// the two-per-CU variant for few registers per lane (FP16 W = 2 with
+// R <= 8, W = 1 with R <= 32; FP32 W = 2 with R <= 16): 64-row stages, at
+// most 74 KiB of LDS and
+// 64 VGPRs, so two workgroups share a CU (8 waves per SIMD) and each hides
+// the other's per-hit LDS latency and stage barriers.
+template <class T, int W, int S, int R, int P, bool META, bool DUAL>
+__global__ __launch_bounds__(kWaves * 64, DUAL ? 8 : 4) void k_stack_fused(
     const FusedArgs args) {
     constexpr int K = W * T::kCols;     // floats of A per lane per row
     typedef FVec<K> vec_t;
@@ -82,6 +88,7 @@ __global__ __launch_bounds__(kWaves * 64, (W == 2 && S == 64) ? 8 : 4) void k_st
     constexpr int D = S / kWaves;           // rows each wave loads per stage
     constexpr int NL = S / 64;              // lane groups of a stage's entries
     static_assert(S == 64 || (S == 128 && W == 2), "stage shapes");
+    static_assert(!DUAL || S == 64, "two-per-CU stages");
     // both stage buffers, contiguous: stage contributions, row j of buffer b
     // at [(b*S + j)*64, +64); the general redo holds one stage of raw rows
     __shared__ wv_t hs[2 * S * 64];
@@ -340,36 +347,52 @@ __global__ __launch_bounds__(kWaves * 64, (W == 2 && S == 64) ? 8 : 4) void k_st
     }
 
     // the wave's R partial rows of this (slice, chunk), in the workspace's
-    // 128-word slices: a W = 4 slice is two of them, lanes 0-31 in the first
-    const int32_t half = W == 2 ? 0 : lane >> 5;
-    uint32_t *dst = args.ws +
-                    ((int64_t)(slice * (W / 2) + half) * args.chunks + chunk) * (int64_t)args.d * 128 +
-                    (int64_t)lo * 128 + ((lane * W) & 127);
+    // 128-word slices: the lane's first word is word slice*64*W + lane*W of
+    // the row (a W = 4 slice spans two workspace slices, two W = 1 slices
+    // share one)
+    const int32_t wcol = slice * 64 * W + lane * W;
+    uint32_t *dst = args.ws + ((int64_t)(wcol >> 7) * args.chunks + chunk) * (int64_t)args.d * 128 +
+                    (int64_t)lo * 128 + (wcol & 127);
 #pragma unroll
     for (int k = 0; k < R; ++k) set_words(*reinterpret_cast<wv_t *>(dst + k * 128), acc[k]);
 }
 
-// The built (W, S, R, P) shapes.  W = 2, S = 128: two register sets where
-// the R rows leave room for them (R = 16), one set (loaded in two halves)
-// otherwise; R = 4 and 8 are kept for devices where two workgroups do not
-// share a CU.  W = 2, S = 64 (two workgroups per CU): R = 4, 8, one set
-// loaded in two halves.  W = 4 (FP32 only): R = 8, 16 with two sets.
+// The built (W, S, R, P, DUAL) shapes.  W = 2, S = 128: two register sets
+// where the R rows leave room for them (R = 16), one set (loaded in two
+// halves) otherwise; R = 4 and 8 are kept for devices where two workgroups
+// do not share a CU.  W = 2 two per CU: R = 4, 8 (and 16 for FP32), one
+// set in two halves.
+// W = 1 (FP16 only): R = 8, 16, 32 two per CU, R = 64 one per CU.  W = 4
+// (FP32 only): R = 8, 16 with two sets.
 template <class T, bool META>
-const void *pick_fused(int W, int S, int R, int P) {
-    if (W == 2 && S == 128) {
-        if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 2, 128, 4, 1, META>;
-        if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 2, 128, 8, 2, META>;
-        if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 2, 128, 16, 2, META>;
-        if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 2, 128, 32, 1, META>;
+const void *pick_fused(int W, int S, int R, int P, bool dual) {
+    if (W == 2 && S == 128 && !dual) {
+        if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 2, 128, 4, 1, META, false>;
+        if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 2, 128, 8, 2, META, false>;
+        if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 2, 128, 16, 2, META, false>;
+        if (R == 32 && P == 1) return (const void *)k_stack_fused<T, 2, 128, 32, 1, META, false>;
     }
-    if (W == 2 && S == 64) {
-        if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 2, 64, 4, 1, META>;
-        if (R == 8 && P == 1) return (const void *)k_stack_fused<T, 2, 64, 8, 1, META>;
+    if (W == 2 && S == 64 && dual) {
+        if (R == 4 && P == 1) return (const void *)k_stack_fused<T, 2, 64, 4, 1, META, true>;
+        if (R == 8 && P == 1) return (const void *)k_stack_fused<T, 2, 64, 8, 1, META, true>;
+        if constexpr (T::kCols == 1)
+            if (R == 16 && P == 1) return (const void *)k_stack_fused<T, 2, 64, 16, 1, META, true>;
+    }
+    if constexpr (T::kCols == 2) {
+        if (W == 1 && S == 64) {
+            if (dual && R == 8 && P == 1) return (const void *)k_stack_fused<T, 1, 64, 8, 1, META, true>;
+            if (dual && R == 16 && P == 1)
+                return (const void *)k_stack_fused<T, 1, 64, 16, 1, META, true>;
+            if (dual && R == 32 && P == 1)
+                return (const void *)k_stack_fused<T, 1, 64, 32, 1, META, true>;
+            if (!dual && R == 64 && P == 2)
+                return (const void *)k_stack_fused<T, 1, 64, 64, 2, META, false>;
+        }
     }
     if constexpr (T::kCols == 1) {
-        if (W == 4 && S == 64) {
-            if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 4, 64, 8, 2, META>;
-            if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 4, 64, 16, 2, META>;
+        if (W == 4 && S == 64 && !dual) {
+            if (R == 8 && P == 2) return (const void *)k_stack_fused<T, 4, 64, 8, 2, META, false>;
+            if (R == 16 && P == 2) return (const void *)k_stack_fused<T, 4, 64, 16, 2, META, false>;
         }
     }
     return nullptr;
@@ -380,8 +403,8 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
                           int32_t units, int accumulate, hipStream_t s) {
     const bool meta = fa.row_idx != nullptr;
     const void *kern =
-        meta ? pick_fused<T, true>(p.words, p.stage_rows, p.rows_per_wave, p.load_sets)
-             : pick_fused<T, false>(p.words, p.stage_rows, p.rows_per_wave, p.load_sets);
+        meta ? pick_fused<T, true>(p.words, p.stage_rows, p.rows_per_wave, p.load_sets, p.dual)
+             : pick_fused<T, false>(p.words, p.stage_rows, p.rows_per_wave, p.load_sets, p.dual);
     // the kernel's row ownership must match the plan the workspace was
     // sized for: 16 waves x R rows x groups cover d exactly; with stored
     // metadata a wave's rows of a stage hold at most 64 entries
@@ -401,29 +424,33 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
     r.units = units;
     r.d = fa.d;
     r.chunks = fa.chunks;
-    r.slices = fa.slices * (p.words / 2);       // in 128-word workspace slices
+    r.slices = (int32_t)((fa.slices * 64 * p.words + 127) / 128);   // 128-word workspace slices
     return launch_stack_reduce<T>(r, 128, accumulate, s);
 }
 
 }  // namespace
 
-// Plan of the fused kernel.  Words per lane W = 4 (256 FP32 columns per
-// slice, 64-row stages) for FP32 matrices wider than 128 columns whose rows
-// allow 16-byte lane loads: a hit then covers twice the columns, which
-// halves the hit loop's instructions per byte (at the cost of more row
-// groups, whose re-reads of A hit L2).  Else W = 2 (256 FP16 / 128 FP32
-// columns, 128-row stages).  Rows per wave R = d / (16 G) for the fewest
-// row groups G with R <= 32 / (W / 2) (W x R partial words per lane) and R
-// dividing d/zeta (a wave's rows inside one block); R must be one of the
-// built sizes.  Chunks are sized so one workgroup per CU fills the device,
-// in whole stages.  Matrices under 64 columns are left to the metadata +
-// LDS apply path.  (From 64 columns on the fused kernel is faster even with
-// most lanes of its slice idle: a narrow sketch is bound by the per-hit
-// instructions, which do not depend on the active lanes.)
+// Plan of the fused kernel.  Words per lane W: 4 (256 FP32 columns per
+// slice) for FP32 matrices wider than 128 columns whose rows allow 16-byte
+// lane loads: a hit then covers twice the columns, which halves the hit
+// loop's instructions per byte (at the cost of more row groups, whose
+// re-reads of A hit L2).  1 (128 FP16 columns) for FP16 matrices of at
+// most 128 columns: no idle half slice, and half the accumulator registers
+// per output row, so more rows per wave (fewer row groups) or two
+// workgroups per CU.  Else 2 (256 FP16 / 128 FP32 columns).  Rows per wave
+// R = d / (16 G) for the fewest row groups G with W x R <= 64 partial words
+// per lane (R <= 32 at W = 2) and R dividing d/zeta (a wave's rows inside
+// one block); R must be one of the built sizes.  Few registers per lane
+// (FP16 W = 2, R <= 8; W = 1, R <= 32; FP32 W = 2, R <= 16) take the
+// two-per-CU shape where the LDS holds two of its workgroups.  Chunks are sized so the workgroups fill
+// the device, in whole stages.  Matrices under 64 columns are left to the
+// metadata + LDS apply path.  (From 64 columns on the fused kernel is
+// faster even with most lanes of its slice idle: a narrow sketch is bound
+// by the per-hit instructions, which do not depend on the active lanes.)
 namespace {
 bool plan_rows(int32_t d, int32_t zeta, int W, int *R_out, int *G_out) {
     const int64_t db = d / zeta;
-    const int rmax = W == 2 ? 32 : 16, rmin = W == 2 ? 4 : 8;
+    const int rmax = W == 1 ? 64 : W == 2 ? 32 : 16, rmin = W == 2 ? 4 : 8;
     for (int g = 1; (int64_t)kWaves * g <= d; g *= 2) {
         if (d % (kWaves * g) != 0) break;
         const int64_t r = d / (kWaves * g);
@@ -441,28 +468,33 @@ bool plan_rows(int32_t d, int32_t zeta, int W, int *R_out, int *G_out) {
 
 bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
                 int32_t d, int32_t zeta, FusedPlan *p) {
-    const int K2 = f16 ? 4 : 2;         // floats per lane at W = 2
-    if (m < 1 || zeta > kFusedMaxZeta || n % K2 != 0 || lda % K2 != 0 || a_align < K2 * 4)
-        return false;
-    if (n < 64 || d % kWaves != 0) return false;
+    if (m < 1 || zeta > kFusedMaxZeta || n < 64 || d % kWaves != 0) return false;
     if (di.max_lds < kFusedLdsBytes) return false;
     // the kernel indexes rows inside a chunk with 32-bit integers
     if (m > (int64_t)65535 << 30) return false;
-    int W = 2, R = 0, G = 0;
-    if (!f16 && n > 128 && n % 4 == 0 && lda % 4 == 0 && a_align >= 16 &&
-        plan_rows(d, zeta, 4, &R, &G))
+    // a lane loads K = W x (2 for FP16, 1 for FP32) floats of a row
+    auto rows_ok = [&](int K) { return n % K == 0 && lda % K == 0 && a_align >= K * 4; };
+    int W = 0, R = 0, G = 0;
+    if (!f16 && n > 128 && rows_ok(4) && plan_rows(d, zeta, 4, &R, &G))
         W = 4;
-    else if (!plan_rows(d, zeta, 2, &R, &G))
+    else if (f16 && n <= 128 && rows_ok(2) && plan_rows(d, zeta, 1, &R, &G))
+        W = 1;
+    else if (rows_ok(f16 ? 4 : 2) && plan_rows(d, zeta, 2, &R, &G))
+        W = 2;
+    else
         return false;
     const int K = W * (f16 ? 2 : 1);
-    // few rows per wave: the two-per-CU shape (64-row stages), where the
-    // device's LDS holds two of its workgroups
-    const bool dual = W == 2 && R <= 8 && di.max_lds >= 2 * kFusedDualLdsBytes;
+    // two per CU where a lane's partial words (W x R) and one set of staged
+    // rows (4 rows x K floats) take at most 40 registers: FP16 W = 2, R <= 8;
+    // FP16 W = 1, R <= 32; FP32 W = 2, R <= 16 (all fit 64 VGPRs)
+    const bool dual = W <= 2 && W * R + 4 * K <= 40 && di.max_lds >= 2 * kFusedDualLdsBytes;
+    if (W == 1 && !dual && R != 64) return false;   // W = 1, one per CU: R = 64 only
     p->words = W;
+    p->dual = dual ? 1 : 0;
     p->stage_rows = (W == 2 && !dual) ? 128 : 64;
     p->rows_per_wave = R;
     p->groups = G;
-    p->load_sets = dual ? 1 : (R == 8 || R == 16) ? 2 : 1;
+    p->load_sets = dual ? 1 : (R == 8 || R == 16 || R == 64) ? 2 : 1;
     p->slices = (n + 64 * K - 1) / (64 * K);
     const int64_t per_chunk = p->slices * G;
     int64_t want = ((int64_t)di.num_cu * (dual ? 2 : 1) + per_chunk - 1) / per_chunk;
@@ -474,7 +506,9 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     p->rows_per_chunk = st_per_chunk * p->stage_rows;
     p->chunks = (m + p->rows_per_chunk - 1) / p->rows_per_chunk;
     p->grid = (p->slices * p->chunks + 7) / 8 * 8 * G;
-    p->ws_bytes = (size_t)p->slices * (W / 2) * (size_t)p->chunks * (size_t)d * 128 * 4;
+    // partial words per row: slices x 64 x W, stored in 128-word slices
+    const size_t ws_slices = (size_t)((p->slices * 64 * W + 127) / 128);
+    p->ws_bytes = ws_slices * (size_t)p->chunks * (size_t)d * 128 * 4;
     return true;
 }
 

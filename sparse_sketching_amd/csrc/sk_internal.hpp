@@ -78,11 +78,11 @@ constexpr int kFusedMetaMaxZeta = 8;
 // bytes), two metadata stages of at most kFusedMaxZeta x 128 entries and 16
 // per-wave votes
 constexpr int kFusedLdsBytes = 2 * 128 * 64 * 8 + 2 * kFusedMaxZeta * 128 * 4 + 16 * 4;
-// the two-per-CU shape (two words per lane, 64-row stages)
+// the two-per-CU shapes (one or two words per lane, 64-row stages)
 constexpr int kFusedDualLdsBytes = 2 * 64 * 64 * 8 + 2 * kFusedMaxZeta * 64 * 4 + 16 * 4;
 struct FusedArgs {
     const float *A;
-    uint32_t *ws;               // [slices * words/2][chunks][d][128] partial words
+    uint32_t *ws;               // [ceil(slices*64*words/128)][chunks][d][128] partial words
     const int32_t *row_idx;     // stored metadata (NULL: drawn in the kernel)
     const float *val;
     int64_t m, lda, rows_per_chunk, row_offset;
@@ -92,14 +92,15 @@ struct FusedArgs {
     float scale;                // float32(1/sqrt(zeta))
 };
 struct FusedPlan {
-    int words;                  // W: partial words per lane and output row (2 or 4)
-    int stage_rows;             // input rows per LDS stage (128 at W = 2, 64 at W = 4
-                                // and in the two-per-CU shape: W = 2, R <= 8)
+    int words;                  // W: partial words per lane and output row (1, 2 or 4)
+    int dual;                   // 1: the two-workgroups-per-CU shape
+    int stage_rows;             // input rows per LDS stage (128 at W = 2 one per CU,
+                                // 64 otherwise)
     int rows_per_wave;          // R: output rows kept in one wavefront's registers
     int groups;                 // G: output row groups (each reads A once)
     int load_sets;              // P: stages of rows in flight in registers (1 or 2)
     int64_t slices;             // column slices of 64 lanes x W words (W = 2: 256 FP16 /
-                                // 128 FP32 columns; W = 4: 256 FP32 columns)
+                                // 128 FP32 columns; W = 4: 256 FP32; W = 1: 128 FP16)
     int64_t rows_per_chunk;     // input rows per workgroup (whole stages)
     int64_t chunks;
     int64_t grid;               // workgroups (1-D, XCD-grouped)

@@ -292,16 +292,20 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
                 or all((d // (16 * g)) not in (4, 8, 16, 32) or (d // zeta) % (d // (16 * g))
                        for g in (1, 2, 4, 8, 16, 32) if d % (16 * g) == 0))
         return
-    W, S = p["words"], p["stage_rows"]
-    # four words per lane only for FP32 wider than 128 columns, 64-row
-    # stages; two words with 64-row stages (two workgroups per CU) for R <= 8
-    assert (W, S) in ((2, 128), (4, 64), (2, 64))
-    assert (W, S) != (2, 64) or p["rows_per_wave"] <= 8
-    assert (W, S) != (2, 128) or p["rows_per_wave"] > 8
-    assert W == 2 or (not f16 and n > 128 and n % 4 == 0)
+    W, S, per_cu = p["words"], p["stage_rows"], p["per_cu"]
+    # four words per lane only for FP32 wider than 128 columns; one word only
+    # for FP16 of at most 128 columns; two per CU (64-row stages) for few
+    # partial words per lane; 128-row stages only at two words, one per CU
+    assert (W, S, per_cu) in ((2, 128, 1), (4, 64, 1), (2, 64, 2), (1, 64, 2), (1, 64, 1))
+    assert W != 4 or (not f16 and n > 128 and n % 4 == 0)
+    assert W != 1 or (f16 and n <= 128)
     K = W * (2 if f16 else 1)
     R, g = p["rows_per_wave"], p["groups"]
-    assert R in ((4, 8, 16, 32) if W == 2 else (8, 16)) and 16 * R * g == d
+    assert R in {1: (8, 16, 32, 64), 2: (4, 8, 16, 32), 4: (8, 16)}[W] and 16 * R * g == d
+    # the built two-per-CU instances
+    assert per_cu == 1 or (W, R) in ((2, 4), (2, 8), (1, 8), (1, 16), (1, 32)) \
+        or (not f16 and (W, R) == (2, 16))
+    assert (per_cu == 2) == (W <= 2 and W * R + 4 * K <= 40)
     db = d // zeta
     assert db % R == 0
     assert p["rows_per_chunk"] % S == 0
@@ -325,15 +329,13 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
             t = lo // db
             assert t < zeta and t * db <= lo and lo + R <= (t + 1) * db
             for lane in (0, 31, 32, 63):
-                # a lane's W words in the workspace's 128-word slices
-                half = 0 if W == 2 else lane >> 5
-                first = (((sl * (W // 2) + half) * p["chunks"] + ch) * d + lo) * 128 \
-                    + ((lane * W) & 127)
+                # a lane's W words: word sl*64*W + lane*W of the row, stored
+                # in the workspace's 128-word slices
+                wcol = sl * 64 * W + lane * W
+                first = (((wcol >> 7) * p["chunks"] + ch) * d + lo) * 128 + (wcol & 127)
                 last = first + (R - 1) * 128 + W - 1
+                assert (wcol & 127) + W <= 128
                 assert first >= 0 and (last + 1) * 4 <= p["ws_bytes"]
-                # the reduce reads 128-word slice s's words below n (units)
-                col_word = (sl * (W // 2) + half) * 128 + ((lane * W) & 127)
-                assert col_word == sl * 64 * W + lane * W
     assert len(seen) == p["slices"] * p["chunks"] * g
     # the fused kernel's metadata stage holds at most 16 blocks
     assert zeta <= 16
@@ -353,6 +355,16 @@ def test_fused_plan_word_width(lib):
         assert (q["fused"], q["words"], q["stage_rows"]) == (1, 2, 128)
     q = b.sk_fused_plan_describe(P16, 1 << 20, 512, 512, 16, 512, 4, **MI355X)
     assert (q["fused"], q["words"]) == (1, 2)
+    # FP16 rows of at most 128 columns: one word per lane (8-byte loads);
+    # R <= 32 two per CU, d = 1024 in one row group (R = 64)
+    for d, R, per_cu in ((256, 16, 2), (512, 32, 2), (1024, 64, 1)):
+        q = b.sk_fused_plan_describe(P16, 1 << 20, 128, 128, 8, d, 4, **MI355X)
+        assert (q["fused"], q["words"], q["rows_per_wave"], q["groups"], q["per_cu"],
+                q["slices"]) == (1, 1, R, 1, per_cu, 1)
+    # two words per lane and R <= 8: two per CU, 64-row stages, chunks for 512
+    q = b.sk_fused_plan_describe(P32, 1 << 22, 64, 64, 16, 128, 4, **MI355X)
+    assert (q["words"], q["rows_per_wave"], q["per_cu"], q["stage_rows"], q["grid"]) == \
+        (2, 8, 2, 64, 512)
 
 
 def test_fused_plan_alignment_and_validation(lib):

@@ -32,14 +32,16 @@ def run_reg(A, ri, v, zeta, d, precision, flags=b.SK_VARIANT_REG, out=None):
     return B
 
 
-# (m, n, d, zeta, plan): plan = (words per lane, R, G) for FP16 and, where
-# FP32 takes four words per lane (wider than 128 columns), for FP32
+# (m, n, d, zeta, plan16, plan32): plan = (words per lane, R, G) for FP16
+# (one word per lane at most 128 columns) and FP32 (four words per lane
+# wider than 128 columns)
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
 @pytest.mark.parametrize("m,n,d,zeta,plan16,plan32", [
     (4096, 256, 64, 4, (2, 4, 1), (2, 4, 1)),         # R = 4 (too few rows for four words)
-    (3000, 128, 128, 4, (2, 8, 1), (2, 8, 1)),        # R = 8, a short last stage
+    (3000, 128, 128, 4, (1, 8, 1), (2, 8, 1)),        # R = 8, a short last stage
     (5000, 260, 256, 8, (2, 16, 1), (4, 16, 1)),      # R = 16, zeta = 8, ragged second slice
-    (4096, 128, 512, 8, (2, 32, 1), (2, 32, 1)),      # R = 32
+    (4096, 128, 512, 8, (1, 32, 1), (2, 32, 1)),      # R = 32 (FP16 one word per lane)
+    (3001, 128, 1024, 4, (1, 64, 1), (2, 32, 2)),     # FP16 R = 64: d = 1024 in one group
     (2500, 136, 1024, 1, (2, 32, 2), (4, 16, 4)),     # row groups (A read 2 / 4 times)
     (3001, 256, 512, 4, (2, 32, 1), (4, 16, 2)),      # FP32 four words, ragged 64-row stage
     (777, 512, 128, 2, (2, 8, 1), (4, 8, 1)),         # FP32 four words, R = 8, two slices

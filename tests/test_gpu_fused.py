@@ -38,7 +38,9 @@ def run_fused(A, d, zeta, seed, precision, row_offset=0, out=None, flags=0):
 # several column slices; ragged row counts and single partial stages.  FP32
 # wider than 128 columns takes four words per lane (64-row stages): the
 # 256-, 384-, 260- and 512-column shapes cover R = 8 and 16, one to four row
-# groups and ragged slices there.  zeta is 1, 4 or 16 (scale a power of two)
+# groups and ragged slices there; FP16 of at most 128 columns takes one word
+# per lane (the 128-, 96-, 66- and 64-column shapes; two workgroups per CU up
+# to R = 32).  zeta is 1, 4 or 16 (scale a power of two)
 # so that integer inputs keep every product exact.
 FUSED_SHAPES = [
     (4096, 128, 64, 4),         # R = 4
@@ -46,7 +48,7 @@ FUSED_SHAPES = [
     (3001, 256, 128, 4),        # R = 8, ragged last stage
     (1000, 128, 256, 16),       # R = 16, zeta = 16 (four Philox blocks per row)
     (2500, 384, 512, 4),        # R = 32 (FP32: 16, two groups), two slices, ragged slice
-    (5000, 128, 1024, 4),       # two row groups
+    (5000, 128, 1024, 4),       # two row groups (FP16: one word per lane, R = 64, one group)
     (129, 256, 512, 1),         # one stage plus one row
     (1, 128, 64, 4),            # a single row
     (4096, 64, 128, 4),         # 64 columns: a quarter (FP16) / half (FP32) of the slice's lanes
@@ -54,6 +56,8 @@ FUSED_SHAPES = [
     (6000, 512, 1024, 4),       # FP32 four words: R = 16, four row groups, two slices
     (2049, 260, 256, 16),       # FP32 four words: a 4-column second slice, zeta = 16
     (65, 256, 256, 4),          # FP32 four words: one 64-row stage plus one row
+    (2000, 96, 512, 4),         # FP16 one word, R = 32 two per CU, lanes past 96 columns clamped
+    (777, 66, 256, 16),         # FP16 one word, R = 16 two per CU, zeta = 16, 66 columns
 ]
 
 
