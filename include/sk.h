@@ -450,6 +450,33 @@ sk_status sk_lds_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t 
                                int32_t zeta, int32_t wide_ok, int32_t num_cu, int32_t max_lds,
                                int64_t *out);
 
+/*
+ * sk_lstsq_qr_f32: x = argmin ||SA x - Sb||_2 for a small sketch, by an FP32
+ * Householder QR of SA, the projection Q^T Sb and a triangular solve: the
+ * reduced solve of sketch-and-solve least squares (FP16 sketching page
+ * §V-A, §V-D: FP32 QR, projection and solve on the d x n sketch;
+ * FlashSketch page App. F.1.4).  One workgroup does the whole solve in one
+ * launch (reflectors as in LAPACK's larfg, panels of up to 32 columns
+ * combined as I - V T V^T).
+ *   SA        device float, d x n row-major, row stride ld >= n; 1 <= n <= d
+ *             <= 2048.  Not modified.
+ *   Sb        device float[d].  Not modified.
+ *   x         device float[n], written.
+ *   workspace device scratch of at least sk_lstsq_workspace_size(d, n)
+ *             bytes, 4-byte aligned, disjoint from SA, Sb and x; contents on
+ *             return unspecified.  Calls sharing it must be ordered.
+ * A zero diagonal entry of R (SA without full column rank) gives inf or NaN
+ * entries of x, as a plain triangular solve would.
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE (n, d, ld), SK_ERR_ALIGN (workspace),
+ * SK_ERR_ARG (workspace too small, or overlapping an argument), SK_ERR_HIP.
+ */
+sk_status sk_lstsq_qr_f32(const float *SA, int32_t d, int32_t n, int64_t ld, const float *Sb,
+                          float *x, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of sk_lstsq_qr_f32 for these sizes ((n + 1) * d floats).
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE. */
+sk_status sk_lstsq_workspace_size(int32_t d, int32_t n, size_t *bytes);
+
 /* Static, NUL-terminated description of a status code. */
 const char *sk_status_string(sk_status status);
 

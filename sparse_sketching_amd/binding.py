@@ -50,6 +50,9 @@ _SIGNATURES = {
     "sk_apply_blockperm": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32,
                                       _c.c_int32, _c.c_int32, _c.c_int32, _c.c_uint64, _c.c_void_p,
                                       _c.c_int64, _c.c_uint32, _c.c_void_p]),
+    "sk_lstsq_qr_f32": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int64, _c.c_void_p,
+                                   _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "sk_lstsq_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int32, _c.POINTER(_c.c_size_t)]),
     "sk_lds_plan_describe": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32,
                                         _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
                                         _c.POINTER(_c.c_int64)]),
@@ -188,6 +191,34 @@ def sk_apply_workspace_size(precision, m, n, d, zeta, flags=0):
 def sk_apply_blockperm(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags=0, stream=None):
     _check("sk_apply_blockperm", load().sk_apply_blockperm(
         _ptr(A), m, n, lda, d, M, kappa, s, seed, _ptr(Y), ldy, flags, _stream(stream)))
+
+
+def sk_lstsq_qr_f32(SA, d, n, ld, Sb, x, workspace, workspace_bytes=0, stream=None):
+    _check("sk_lstsq_qr_f32", load().sk_lstsq_qr_f32(
+        _ptr(SA), d, n, ld, _ptr(Sb), _ptr(x), _ptr(workspace),
+        _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def sk_lstsq_workspace_size(d, n):
+    out = ctypes.c_size_t(0)
+    _check("sk_lstsq_workspace_size", load().sk_lstsq_workspace_size(d, n, ctypes.byref(out)))
+    return out.value
+
+
+def lstsq_qr(SA, Sb, stream=None):
+    """x = argmin ||SA x - Sb||_2 (FP32 Householder QR in the library's
+    kernel) for a float32 device matrix SA (d x n, n <= d <= 2048) and
+    vector Sb; returns x as a float32 device tensor."""
+    import torch
+    _need_device(SA, torch.float32, "SA")
+    _need_device(Sb, torch.float32, "Sb")
+    d, n = SA.shape
+    if Sb.shape != (d,) or not Sb.is_contiguous():
+        raise ValueError("Sb must be a contiguous vector of SA's row count")
+    x = torch.empty(n, dtype=torch.float32, device=SA.device)
+    ws = torch.empty(sk_lstsq_workspace_size(d, n), dtype=torch.uint8, device=SA.device)
+    sk_lstsq_qr_f32(SA, d, n, SA.stride(0), Sb, x, ws, 0, stream)
+    return x
 
 
 PLAN_FIELDS = ("lds", "words", "slice", "groups", "zg", "threads", "rows_per_chunk", "chunks",

@@ -637,6 +637,31 @@ sk_status sk_sketch_workspace_size(int32_t precision, int64_t m, int32_t n, int3
     return SK_OK;
 }
 
+sk_status sk_lstsq_workspace_size(int32_t d, int32_t n, size_t *bytes) {
+    if (bytes == nullptr) return SK_ERR_NULL;
+    *bytes = 0;
+    if (n < 1 || d < n || d > sk::kQrMaxRows) return SK_ERR_SHAPE;
+    *bytes = (size_t)(n + 1) * (size_t)d * sizeof(float);
+    return SK_OK;
+}
+
+sk_status sk_lstsq_qr_f32(const float *SA, int32_t d, int32_t n, int64_t ld, const float *Sb,
+                          float *x, void *workspace, size_t workspace_bytes, void *stream) {
+    if (n < 1 || d < n || d > sk::kQrMaxRows || ld < n) return SK_ERR_SHAPE;
+    if (SA == nullptr || Sb == nullptr || x == nullptr || workspace == nullptr)
+        return SK_ERR_NULL;
+    if ((uintptr_t)workspace % 4 != 0) return SK_ERR_ALIGN;
+    const size_t need = (size_t)(n + 1) * (size_t)d * sizeof(float);
+    if (workspace_bytes < need) return SK_ERR_ARG;
+    const size_t aspan = span_bytes(d, n, ld, 4);
+    if (overlaps(workspace, need, SA, aspan) || overlaps(workspace, need, Sb, (size_t)d * 4) ||
+        overlaps(workspace, need, x, (size_t)n * 4) || overlaps(x, (size_t)n * 4, SA, aspan) ||
+        overlaps(x, (size_t)n * 4, Sb, (size_t)d * 4))
+        return SK_ERR_ARG;
+    return hip_status(sk::launch_lstsq_qr(SA, d, n, ld, Sb, x, static_cast<float *>(workspace),
+                                          (hipStream_t)stream));
+}
+
 sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
                                  int32_t a_align, int32_t d, int32_t zeta, int32_t num_cu,
                                  int32_t max_lds, int64_t *out) {

@@ -13,8 +13,9 @@ metrics on top of the library's sketches.
   sketched orthonormal basis (FlashSketch page App. F.1.1, F.1.2; FP16
   sketching page §V-C).
 
-The small dense steps on the d x n sketch are torch linear algebra on the
-same device; the sketches themselves run only in the library's kernels.
+The sketches and the FP32 QR solve run in the library's kernels; torch
+supplies device memory, stacks the ridge system and evaluates the FP64
+residuals and metrics (measurement, not part of the solve).
 """
 import torch
 
@@ -34,15 +35,10 @@ def sketch_pair(A, rhs, d, zeta, seed, precision="f16acc", row_offset=0):
 
 
 def solve_sketched(SA, Sb):
-    """argmin ||SA x - Sb||_2 by an FP32 Householder QR, the projection
-    Q^T Sb and a triangular solve; float32 result.  Q is never formed: the
-    reflectors from geqrf are applied to Sb directly (ormqr), which skips
-    building the d x n factor (1.5x faster than a thin QR at 512 x 256)."""
-    SA = SA.float()
-    n = SA.shape[1]
-    a, tau = torch.geqrf(SA)
-    z = torch.ormqr(a, tau, Sb.float()[:, None], left=True, transpose=True)[:n]
-    return torch.linalg.solve_triangular(a[:n].triu(), z, upper=True)[:, 0]
+    """argmin ||SA x - Sb||_2 by the library's FP32 Householder QR, the
+    projection Q^T Sb and a triangular solve (sk_lstsq_qr_f32, one launch);
+    float32 result."""
+    return b.lstsq_qr(SA.float().contiguous(), Sb.float().contiguous())
 
 
 def ridge_sketched(SA, Sb, lam):

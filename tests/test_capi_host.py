@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(lib):
                           "sk_sketch_f32", "sk_sketch_f16acc", "sk_sketch_workspace_size",
                           "sk_fused_plan_describe", "sk_apply_lowp", "sk_apply_blockperm",
                           "sk_apply_blockperm_ex", "sk_blockperm_workspace_size",
-                          "sk_blockperm_plan_describe", "sk_status_string"}
+                          "sk_blockperm_plan_describe", "sk_lstsq_qr_f32",
+                          "sk_lstsq_workspace_size", "sk_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -496,3 +497,33 @@ def test_blockperm_register_grid_covers_every_unit_once():
 ])
 def test_blockperm_ex_validation(lib, args, expect):
     assert lib.sk_apply_blockperm_ex(*args, None) == expect
+
+
+def test_lstsq_validation(lib):
+    """sk_lstsq_qr_f32 rejects bad arguments before any HIP call (host
+    buffers stand in for device pointers; every call here fails validation,
+    so nothing is launched), and the workspace size is (n + 1) d floats."""
+    d, n = 64, 32
+    SA = (ctypes.c_float * (d * n))()
+    Sb = (ctypes.c_float * d)()
+    x = (ctypes.c_float * n)()
+    ws = (ctypes.c_float * ((n + 1) * d + 1))()
+    nb = (n + 1) * d * 4
+    f = lib.sk_lstsq_qr_f32
+    A, B, X, Wp = (ctypes.addressof(t) for t in (SA, Sb, x, ws))
+    assert f(A, d, d + 1, d + 1, B, X, Wp, nb, None) == b.SK_ERR_SHAPE      # n > d
+    assert f(A, d, 0, n, B, X, Wp, nb, None) == b.SK_ERR_SHAPE              # n < 1
+    assert f(A, 2049, n, n, B, X, Wp, nb, None) == b.SK_ERR_SHAPE           # d above 2048
+    assert f(A, d, n, n - 1, B, X, Wp, nb, None) == b.SK_ERR_SHAPE          # ld < n
+    assert f(None, d, n, n, B, X, Wp, nb, None) == b.SK_ERR_NULL
+    assert f(A, d, n, n, None, X, Wp, nb, None) == b.SK_ERR_NULL
+    assert f(A, d, n, n, B, None, Wp, nb, None) == b.SK_ERR_NULL
+    assert f(A, d, n, n, B, X, None, nb, None) == b.SK_ERR_NULL
+    assert f(A, d, n, n, B, X, Wp + 2, nb, None) == b.SK_ERR_ALIGN         # 4-byte rule
+    assert f(A, d, n, n, B, X, Wp, nb - 4, None) == b.SK_ERR_ARG           # too small
+    assert f(A, d, n, n, B, X, A, nb, None) == b.SK_ERR_ARG                # workspace = SA
+    assert f(A, d, n, n, B, A, Wp, nb, None) == b.SK_ERR_ARG               # x inside SA
+    out = ctypes.c_size_t(0)
+    assert lib.sk_lstsq_workspace_size(d, n, ctypes.byref(out)) == b.SK_OK and out.value == nb
+    assert lib.sk_lstsq_workspace_size(d, d + 1, ctypes.byref(out)) == b.SK_ERR_SHAPE
+    assert lib.sk_lstsq_workspace_size(d, n, None) == b.SK_ERR_NULL

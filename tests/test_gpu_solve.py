@@ -113,3 +113,76 @@ def test_sparsestack_beats_countsketch_on_coherent_system():
     assert res[(4, "f32")] <= res[(1, "f32")] * 1.0001
     assert res[(4, "f16acc")] <= res[(1, "f16acc")] * 1.1
     assert res[(1, "f16acc")] <= res[(4, "f16acc")] * 1.1
+
+
+# ------------------------------------------- the library's FP32 QR solver
+
+@pytest.mark.parametrize("d,n", [
+    (512, 256),         # the sketch-and-solve size (d = 2n): eight 32-column panels
+    (768, 256),         # the ridge system [SA; sqrt(lam) I]
+    (100, 37),          # a 32-column panel, then 4- and 1-column panels
+    (64, 64),           # square
+    (33, 1),            # one column
+    (1000, 777),        # 16-column panels, then 8, 1
+    (2048, 1024),       # the largest: 8-column panels
+])
+def test_lstsq_qr_vs_oracle(d, n):
+    """sk_lstsq_qr_f32 on N(0,1) systems: x within 5e-5 (relative) of the
+    oracle's fp64 QR solution (an FP32 Householder solve of a matrix with
+    condition number below ~10 on these shapes), and its residual within
+    1e-5 (relative, plus 1e-5 absolute for FP32 rounding on consistent
+    square systems) of the fp64 minimum."""
+    from sparse_sketching_amd import binding as b
+    say(f"lstsq qr d={d} n={n}")
+    g = np.random.default_rng(d * 7 + n)
+    M = g.standard_normal((d, n)).astype(np.float32)
+    y = g.standard_normal(d).astype(np.float32)
+    x = b.lstsq_qr(to_dev(M), to_dev(y))
+    sync()
+    x = x.cpu().numpy().astype(np.float64)
+    ref = oracle.lstsq_qr(M, y)
+    assert np.linalg.norm(x - ref) <= 5e-5 * np.linalg.norm(ref)
+    assert oracle.residual(M, x, y) <= oracle.residual(M, ref, y) * (1 + 1e-5) + 1e-5
+
+
+@pytest.mark.parametrize("d,n", [(512, 256), (100, 37), (40, 40)])
+def test_lstsq_qr_exact_triangular(d, n):
+    """SA = [U; 0] with U upper triangular (power-of-two diagonal, small
+    integer entries) and Sb = [U x0; 0] for integer x0: every reflector is
+    the identity (tau = 0, nothing below the diagonal), so R = U and
+    Q^T Sb = Sb exactly, and the blocked back substitution must return x0
+    bit for bit (all partial sums are integers below 2^24)."""
+    from sparse_sketching_amd import binding as b
+    say(f"lstsq exact d={d} n={n}")
+    g = np.random.default_rng(n)
+    U = np.triu(g.integers(-2, 3, size=(n, n))).astype(np.float64)
+    np.fill_diagonal(U, g.choice([-2.0, -1.0, 1.0, 2.0], size=n))
+    # z = U x0 is integer; the back substitution's running value at row i
+    # is z_i - sum_{j>i} U_ij x0_j = U_ii x0_i, an integer below 2^24 at
+    # every step, and dividing it by U_ii (a power of two) gives x0_i
+    x0 = g.integers(-3, 4, size=n).astype(np.float64)
+    z = U @ x0
+    assert np.abs(z).max() < 2 ** 20
+    SA = np.zeros((d, n), dtype=np.float32)
+    SA[:n] = U
+    Sb = np.zeros(d, dtype=np.float32)
+    Sb[:n] = z
+    x = b.lstsq_qr(to_dev(SA), to_dev(Sb))
+    sync()
+    assert np.array_equal(x.cpu().numpy().astype(np.float64), x0)
+
+
+def test_lstsq_qr_matches_sketch_solve_route():
+    """The library's solver on a real sketch (the FP32 fused sketch of a 2^16
+    x 128 system, d = 256): same residual as the oracle's FP32 QR of the same
+    sketch, within 1e-5 relative."""
+    from sparse_sketching_amd import binding as b
+    m, n, d, zeta, seed = 1 << 16, 128, 256, 4, 3
+    A, rhs = system(m, n, seed=21)
+    SA, Sb = solve.sketch_pair(to_dev(A), to_dev(rhs), d, zeta, seed, "f32")
+    x = b.lstsq_qr(SA, Sb)
+    sync()
+    x_or = oracle.sketch_solve(SA.cpu().numpy(), Sb.cpu().numpy())
+    r_gpu = oracle.residual(A, x.cpu().numpy(), rhs)
+    r_or = oracle.residual(A, x_or, rhs)
+    assert abs(r_gpu - r_or) <= 1e-5 * r_or
