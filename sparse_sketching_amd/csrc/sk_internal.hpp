@@ -197,7 +197,8 @@ hipError_t launch_bp_regs(const BpRegsPlan &p, const BlockPermGenArgs &args,
 
 // Least squares on a small sketch (lstsq.hip): x = argmin ||SA x - Sb||_2 by
 // an FP32 Householder QR, one workgroup.  SA is d x n row-major (row stride
-// ld), 1 <= n <= d <= kQrMaxRows; W is a workspace of (n + 1) * d floats.
+// ld), 1 <= n <= d <= kQrMaxRows; W is a workspace of (n + 1) * d + 1024
+// floats.
 constexpr int kQrMaxRows = 2048;
 hipError_t launch_lstsq_qr(const float *SA, int32_t d, int32_t n, int64_t ld, const float *Sb,
                            float *x, float *W, hipStream_t stream);
