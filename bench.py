@@ -47,8 +47,8 @@ SEED = 1
 # FETCH_SIZE and WRITE_SIZE passes over bench.py --profile-pass (KiB per
 # dispatch; FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a 1 GiB device
 # copy reads on the same counters).  Valid for the kernels named here only.
-TRAFFIC = {"kernels": ("k_stack_fused<AccF16,2,32,1,false>", "k_stack_reduce<AccF16>"),
-           "fetch_kib": (524_691, 32_803), "write_kib": (65_536, 256),
+TRAFFIC = {"kernels": ("k_stack_fused<AccF16,2,128,32,1,false,false>", "k_stack_reduce<AccF16>"),
+           "fetch_kib": (524_701, 32_803), "write_kib": (65_536, 256),
            "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -470,7 +470,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_bytes(),
-                     "kernel": "k_stack_fused<AccF16,2,32,1,false> + k_stack_reduce<AccF16>",
+                     "kernel": "k_stack_fused<AccF16,2,128,32,1,false,false> + k_stack_reduce<AccF16>",
                      "kernel_ms": round(ms16, 5), "algorithmic_bytes": fbytes16,
                      "apply_atomic_flush_ms": round(ms_kernel_atomic, 5)},
         "cpu_baseline": None,
