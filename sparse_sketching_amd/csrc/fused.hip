@@ -442,11 +442,12 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
 // per lane (R <= 32 at W = 2) and R dividing d/zeta (a wave's rows inside
 // one block); R must be one of the built sizes.  Few registers per lane
 // (FP16 W = 2, R <= 8; W = 1, R <= 32; FP32 W = 2, R <= 16) take the
-// two-per-CU shape where the LDS holds two of its workgroups.  Chunks are sized so the workgroups fill
-// the device, in whole stages.  Matrices under 64 columns are left to the
-// metadata + LDS apply path.  (From 64 columns on the fused kernel is
-// faster even with most lanes of its slice idle: a narrow sketch is bound
-// by the per-hit instructions, which do not depend on the active lanes.)
+// two-per-CU shape where the LDS holds two of its workgroups.  Chunks are
+// sized so the workgroups fill the device, in whole stages.  Narrow
+// matrices (down to 2 columns, a right-hand side sketched with its matrix)
+// run here too, most lanes of their slice idle: a narrow sketch is bound by
+// the per-hit instructions, which do not depend on the active lanes, and
+// the fused kernel's hits are cheaper than the LDS apply's.
 namespace {
 bool plan_rows(int32_t d, int32_t zeta, int W, int *R_out, int *G_out) {
     const int64_t db = d / zeta;
@@ -468,7 +469,7 @@ bool plan_rows(int32_t d, int32_t zeta, int W, int *R_out, int *G_out) {
 
 bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
                 int32_t d, int32_t zeta, FusedPlan *p) {
-    if (m < 1 || zeta > kFusedMaxZeta || n < 64 || d % kWaves != 0) return false;
+    if (m < 1 || zeta > kFusedMaxZeta || n < 2 || d % kWaves != 0) return false;
     if (di.max_lds < kFusedLdsBytes) return false;
     // the kernel indexes rows inside a chunk with 32-bit integers
     if (m > (int64_t)65535 << 30) return false;

@@ -289,7 +289,7 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
     K2 = 4 if f16 else 2                # floats per lane at two words per lane
     p = b.sk_fused_plan_describe(precision, m, n, n, 16, d, zeta, **MI355X)
     if not p["fused"]:
-        assert (zeta > 16 or n % K2 or n < 32 * K2 or d % 16
+        assert (zeta > 16 or n % 2 or d % 16
                 or all((d // (16 * g)) not in (4, 8, 16, 32) or (d // zeta) % (d // (16 * g))
                        for g in (1, 2, 4, 8, 16, 32) if d % (16 * g) == 0))
         return
@@ -371,13 +371,19 @@ def test_fused_plan_word_width(lib):
 def test_fused_plan_alignment_and_validation(lib):
     P16, P32 = b.SK_PRECISION_F16ACC, b.SK_PRECISION_F32
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 16, 512, 4, **MI355X)["fused"] == 1
-    # misaligned base, odd-multiple lda, narrow rows: left to the fallback
+    # wide FP16 rows with an 8-byte base or lda % 4 != 0, an odd FP32 lda: the fallback
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 8, 512, 4, **MI355X)["fused"] == 0
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 258, 16, 512, 4, **MI355X)["fused"] == 0
     assert b.sk_fused_plan_describe(P32, 1 << 20, 256, 257, 16, 512, 4, **MI355X)["fused"] == 0
     assert b.sk_fused_plan_describe(P16, 1 << 20, 64, 64, 16, 128, 4, **MI355X)["fused"] == 1
-    assert b.sk_fused_plan_describe(P16, 1 << 20, 60, 60, 16, 128, 4, **MI355X)["fused"] == 0
-    assert b.sk_fused_plan_describe(P32, 1 << 20, 62, 62, 16, 128, 4, **MI355X)["fused"] == 0
+    # narrow rows are covered (one word per lane for FP16, two for FP32);
+    # an odd FP32 width or lda is not
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 60, 60, 16, 128, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 62, 62, 16, 128, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P16, 1 << 20, 2, 2, 8, 512, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 2, 2, 8, 512, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 31, 31, 16, 128, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 1, 1, 16, 128, 4, **MI355X)["fused"] == 0
     # LDS smaller than the kernel's stages
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 16, 512, 4, num_cu=256,
                                     max_lds=64 * 1024)["fused"] == 0

@@ -179,12 +179,13 @@ def test_register_row_chunks_and_padded_strides(precision):
 
 
 def test_register_forced_errors():
-    """SK_VARIANT_REG on a shape it does not cover (n = 32), without a
-    workspace, with a misaligned one, or together with another variant."""
+    """SK_VARIANT_REG on a shape it does not cover (FP32 with an odd n = 31),
+    without a workspace, with a misaligned one, or together with another
+    variant."""
     d, zeta = 64, 4
-    A = to_dev(inputs.gaussian(4096, 32))
+    A = to_dev(inputs.gaussian(4096, 31))
     ri, v = b.meta(1, 4096, d, zeta, device=dev())
-    B = torch.empty((d, 32), dtype=torch.float32, device=dev())
+    B = torch.empty((d, 31), dtype=torch.float32, device=dev())
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev())
     A2 = to_dev(inputs.gaussian(4096, 128))
     B2 = torch.empty((d, 128), dtype=torch.float32, device=dev())

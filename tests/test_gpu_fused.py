@@ -142,7 +142,7 @@ def test_fused_large_row_offset():
 
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
 @pytest.mark.parametrize("m,n,d,zeta,lda", [
-    (4096, 32, 64, 4, 32),      # narrow rows
+    (4096, 32, 40, 4, 32),      # narrow rows and d not a multiple of 16
     (2048, 128, 128, 64, 128),  # zeta above the fused metadata stage
     (3001, 128, 40, 4, 128),    # d not a multiple of 16
     (2048, 128, 64, 4, 130),    # rows not 16-byte aligned (FP16) / fine for FP32

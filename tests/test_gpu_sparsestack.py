@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 # (flags, workspace): the page's flat scatter; the LDS-privatized apply with
 # the store-and-reduce flush (workspace); the same with the atomic flush;
-# the register apply (workspace; shapes with n >= 64 and n % 4 == 0)
+# the register apply (workspace; the shapes the fused kernel covers)
 VARIANTS = {"flat": (b.SK_VARIANT_FLAT, None), "lds": (b.SK_VARIANT_LDS, True),
             "lds_atomic": (b.SK_VARIANT_LDS, None), "reg": (b.SK_VARIANT_REG, True)}
 ALL = ["flat", "lds", "lds_atomic"]
