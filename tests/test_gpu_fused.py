@@ -58,6 +58,9 @@ FUSED_SHAPES = [
     (65, 256, 256, 4),          # FP32 four words: one 64-row stage plus one row
     (2000, 96, 512, 4),         # FP16 one word, R = 32 two per CU, lanes past 96 columns clamped
     (777, 66, 256, 16),         # FP16 one word, R = 16 two per CU, zeta = 16, 66 columns
+    (5000, 2, 512, 4),          # a right-hand side: 2 columns, all other lanes clamped
+    (3001, 8, 256, 16),         # 8 columns, zeta = 16, ragged last stage
+    (4096, 32, 64, 4),          # 32 columns, R = 4 two per CU
 ]
 
 
