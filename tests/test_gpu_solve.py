@@ -186,3 +186,21 @@ def test_lstsq_qr_matches_sketch_solve_route():
     r_gpu = oracle.residual(A, x.cpu().numpy(), rhs)
     r_or = oracle.residual(A, x_or, rhs)
     assert abs(r_gpu - r_or) <= 1e-5 * r_or
+
+
+def test_lstsq_qr_padded_stride():
+    """SA as a column slice of a wider matrix (row stride ld = n + 13): the
+    same solution as the contiguous copy, bit for bit (the solver reads SA
+    once, into its own column-major workspace)."""
+    from sparse_sketching_amd import binding as b
+    d, n, pad = 300, 97, 13
+    g = np.random.default_rng(4)
+    M = g.standard_normal((d, n + pad)).astype(np.float32)
+    y = g.standard_normal(d).astype(np.float32)
+    Md = to_dev(M)
+    x_view = b.lstsq_qr(Md[:, :n], to_dev(y))
+    x_copy = b.lstsq_qr(Md[:, :n].contiguous(), to_dev(y))
+    sync()
+    assert torch.equal(x_view, x_copy)
+    ref = oracle.lstsq_qr(M[:, :n], y)
+    assert np.linalg.norm(x_view.cpu().numpy() - ref) <= 5e-5 * np.linalg.norm(ref)
