@@ -294,8 +294,9 @@ def main():
     print(f"[bench] pages' protocol: fp16 {proto['fp16']:.4f} ms, fp32 {proto['fp32']:.4f} ms",
           file=sys.stderr, flush=True)
 
-    # downstream: complete sketch-and-solve (shared-map SA and Sb, FP32 QR,
-    # projection, triangular solve) with FP16 and FP32 sketches, d = 2n
+    # downstream: complete sketch-and-solve (shared-map SA and Sb, then the
+    # library's FP32 QR, projection and triangular solve, sk_lstsq_qr_f32)
+    # with FP16 and FP32 sketches, d = 2n
     from sparse_sketching_amd import solve
     g = torch.Generator(device=dev).manual_seed(5)
     x0 = torch.randn(n, device=dev, generator=g)
