@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kQrThreads) void k_qr_panel(const QrArgs args, int 
     __shared__ float G[kQrMaxNb * kQrMaxNb];        // V^T V
     __shared__ float taus[kQrMaxNb];
     __shared__ float scales[kQrMaxNb];
+    __shared__ float betas[kQrMaxNb];               // R's diagonal, written back with the panel
     // column c's ||x||^2 and alpha in slot c & 1 (read in step c; the next
     // column's are written into the other slot during step c)
     __shared__ float nrm[2][2];
@@ -124,10 +125,12 @@ __global__ __launch_bounds__(kQrThreads) void k_qr_panel(const QrArgs args, int 
             tau = (beta - alpha) / beta;
             scale = 1.f / (alpha - beta);
         }
+        // (no global store inside the column loop: each barrier would wait
+        // for it to land)
         if (tid == 0) {
             taus[c] = tau;
             scales[c] = scale;
-            W[(int64_t)(p0 + c) * d + p0 + c] = beta;   // R's diagonal entry
+            betas[c] = beta;
         }
         // H_c on the panel's later columns, one wave per column
         for (int c2 = c + 1 + wave; c2 < PB; c2 += kQrWaves) {
@@ -158,11 +161,10 @@ __global__ __launch_bounds__(kQrThreads) void k_qr_panel(const QrArgs args, int 
         else if (r == c) V[r * LS + c] = 1.f;
     }
     __syncthreads();
-    // R above the diagonal and the reflectors below it to W (the diagonal
-    // already holds beta)
+    // R above the diagonal, beta on it and the reflectors below it to W
     for (int idx = tid; idx < PB * dp; idx += kQrThreads) {
         const int c = idx / dp, r = idx - c * dp;
-        if (r != c) W[(int64_t)(p0 + c) * d + p0 + r] = V[r * LS + c];
+        W[(int64_t)(p0 + c) * d + p0 + r] = r == c ? betas[c] : V[r * LS + c];
     }
     // G[m][i] = v_m . v_i for m < i (v_i: zero above row i, one at row i)
     for (int pr = wave; pr < PB * PB; pr += kQrWaves) {
