@@ -131,9 +131,10 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
  *                their metadata) through LDS and each wavefront keeps its
  *                own output rows' partial in registers; the partials go to
  *                the workspace and a second kernel writes B as their sum.
- *                Needs a workspace, zeta <= 8, d % 16 == 0, n >= 2, n
- *                and lda even and A 8-byte aligned (FP16 wider than 128
- *                columns: multiples of 4, 16-byte aligned): shapes
+ *                Needs a workspace, zeta <= 8, d % 16 == 0; FP32 up to 64
+ *                columns any rows, wider: n and lda even and A 8-byte
+ *                aligned; FP16: A 8-byte aligned, wider than 128 columns
+ *                n and lda multiples of 4 and A 16-byte aligned: shapes
  *                sk_fused_plan_describe reports as covered, with zeta <= 8.  Its fast path
  *                assumes |val| = float32(1/sqrt(zeta)), as sk_meta_generate
  *                writes; a workgroup whose rows hold any other value redoes
@@ -266,10 +267,10 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
  * allow 16-byte loads (lda % 4 == 0, A 16-byte aligned) take four partial
  * words per lane (256 columns per workgroup) instead of two; the order of
  * each output word's additions is fixed either way.  Shapes the fused
- * kernel does not cover (zeta > 16, d not a multiple of 16, one column,
- * rows of A without 8-byte lane loads (A 8-byte aligned, n and lda
- * even; FP16 wider than 128 columns: 16-byte, multiples of 4), row
- * ownership that does not fit the registers) run sk_meta_generate into the
+ * kernel does not cover (zeta > 16, d not a multiple of 16, FP32 rows
+ * wider than 64 columns without 8-byte lane loads (A 8-byte aligned, n and
+ * lda even), FP16 rows wider than 128 columns without 16-byte lane loads,
+ * row ownership that does not fit the registers) run sk_meta_generate into the
  * workspace and then the LDS (or flat) apply; the result is the same
  * sketch.
  *

@@ -70,12 +70,13 @@ __device__ __forceinline__ void set_words(uint4 &x, const uint32_t *w) {
 // values); a workgroup whose chunk holds any other value redoes the chunk
 // afterwards with a per-hit product from raw rows.
 // W: words per lane (2: 64-lane slices of 128 words; 4: slices of 256
-// words, each hit covers twice the columns; 1 (FP16 only): slices of 64
-// words, 128 columns, for narrow rows: half the accumulator registers per
-// row).  S: input rows per stage (128 at W = 2, 64 at W = 4: 128 KiB of
+// words, each hit covers twice the columns; 1: slices of 64 words (128
+// FP16 / 64 FP32 columns) for narrow rows: half the accumulator registers
+// per row, and 4-byte FP32 loads for any width or stride).  S: input rows per stage (128 at W = 2, 64 at W = 4: 128 KiB of
 // stage buffers either way, one workgroup per CU; 64 at W = 1).  DUAL:
 // the two-per-CU variant for few registers per lane (FP16 W = 2 with
-// R <= 8, W = 1 with R <= 32; FP32 W = 2 with R <= 16): 64-row stages, at
+// R <= 8, W = 1 with R <= 32; FP32 W = 2 with R <= 16, W = 1 with
+// R <= 32): 64-row stages, at
 // most 74 KiB of LDS and
 // 64 VGPRs, so two workgroups share a CU (8 waves per SIMD) and each hides
 // the other's per-hit LDS latency and stage barriers.
@@ -362,8 +363,8 @@ __global__ __launch_bounds__(kWaves * 64, DUAL ? 8 : 4) void k_stack_fused(
 // halves) otherwise; R = 4 and 8 are kept for devices where two workgroups
 // do not share a CU.  W = 2 two per CU: R = 4, 8 (and 16 for FP32), one
 // set in two halves.
-// W = 1 (FP16 only): R = 8, 16, 32 two per CU, R = 64 one per CU.  W = 4
-// (FP32 only): R = 8, 16 with two sets.
+// W = 1: R = 8, 16, 32 two per CU, R = 64 one per CU.  W = 4 (FP32 only):
+// R = 8, 16 with two sets.
 template <class T, bool META>
 const void *pick_fused(int W, int S, int R, int P, bool dual) {
     if (W == 2 && S == 128 && !dual) {
@@ -378,7 +379,7 @@ const void *pick_fused(int W, int S, int R, int P, bool dual) {
         if constexpr (T::kCols == 1)
             if (R == 16 && P == 1) return (const void *)k_stack_fused<T, 2, 64, 16, 1, META, true>;
     }
-    if constexpr (T::kCols == 2) {
+    {
         if (W == 1 && S == 64) {
             if (dual && R == 8 && P == 1) return (const void *)k_stack_fused<T, 1, 64, 8, 1, META, true>;
             if (dual && R == 16 && P == 1)
@@ -434,17 +435,18 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
 // slice) for FP32 matrices wider than 128 columns whose rows allow 16-byte
 // lane loads: a hit then covers twice the columns, which halves the hit
 // loop's instructions per byte (at the cost of more row groups, whose
-// re-reads of A hit L2).  1 (128 FP16 columns) for FP16 matrices of at
-// most 128 columns: no idle half slice, and half the accumulator registers
-// per output row, so more rows per wave (fewer row groups) or two
-// workgroups per CU.  Else 2 (256 FP16 / 128 FP32 columns).  Rows per wave
+// re-reads of A hit L2).  1 (128 FP16 / 64 FP32 columns) for FP16 matrices
+// of at most 128 columns and FP32 matrices of at most 64: no idle half
+// slice, half the accumulator registers per output row, so more rows per
+// wave (fewer row groups) or two workgroups per CU, and for FP32 4-byte
+// loads (any width, stride or base).  Else 2 (256 FP16 / 128 FP32 columns).  Rows per wave
 // R = d / (16 G) for the fewest row groups G with W x R <= 64 partial words
 // per lane (R <= 32 at W = 2) and R dividing d/zeta (a wave's rows inside
 // one block); R must be one of the built sizes.  Few registers per lane
 // (FP16 W = 2, R <= 8; W = 1, R <= 32; FP32 W = 2, R <= 16) take the
 // two-per-CU shape where the LDS holds two of its workgroups.  Chunks are
 // sized so the workgroups fill the device, in whole stages.  Narrow
-// matrices (down to 2 columns, a right-hand side sketched with its matrix)
+// matrices (down to 2 FP16 / 1 FP32 columns: a right-hand side)
 // run here too, most lanes of their slice idle: a narrow sketch is bound by
 // the per-hit instructions, which do not depend on the active lanes, and
 // the fused kernel's hits are cheaper than the LDS apply's.
@@ -469,7 +471,8 @@ bool plan_rows(int32_t d, int32_t zeta, int W, int *R_out, int *G_out) {
 
 bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
                 int32_t d, int32_t zeta, FusedPlan *p) {
-    if (m < 1 || zeta > kFusedMaxZeta || n < 2 || d % kWaves != 0) return false;
+    if (m < 1 || zeta > kFusedMaxZeta || d % kWaves != 0) return false;
+    if (n < (f16 ? 2 : 1)) return false;
     if (di.max_lds < kFusedLdsBytes) return false;
     // the kernel indexes rows inside a chunk with 32-bit integers
     if (m > (int64_t)65535 << 30) return false;
@@ -479,6 +482,8 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     if (!f16 && n > 128 && rows_ok(4) && plan_rows(d, zeta, 4, &R, &G))
         W = 4;
     else if (f16 && n <= 128 && rows_ok(2) && plan_rows(d, zeta, 1, &R, &G))
+        W = 1;
+    else if (!f16 && n <= 64 && rows_ok(1) && plan_rows(d, zeta, 1, &R, &G))
         W = 1;
     else if (rows_ok(f16 ? 4 : 2) && plan_rows(d, zeta, 2, &R, &G))
         W = 2;

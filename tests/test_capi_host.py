@@ -289,7 +289,7 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
     K2 = 4 if f16 else 2                # floats per lane at two words per lane
     p = b.sk_fused_plan_describe(precision, m, n, n, 16, d, zeta, **MI355X)
     if not p["fused"]:
-        assert (zeta > 16 or n % 2 or d % 16
+        assert (zeta > 16 or (n % 2 and (f16 or n > 64)) or d % 16
                 or all((d // (16 * g)) not in (4, 8, 16, 32) or (d // zeta) % (d // (16 * g))
                        for g in (1, 2, 4, 8, 16, 32) if d % (16 * g) == 0))
         return
@@ -299,7 +299,7 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
     # partial words per lane; 128-row stages only at two words, one per CU
     assert (W, S, per_cu) in ((2, 128, 1), (4, 64, 1), (2, 64, 2), (1, 64, 2), (1, 64, 1))
     assert W != 4 or (not f16 and n > 128 and n % 4 == 0)
-    assert W != 1 or (f16 and n <= 128)
+    assert W != 1 or (f16 and n <= 128) or (not f16 and n <= 64)
     K = W * (2 if f16 else 1)
     R, g = p["rows_per_wave"], p["groups"]
     assert R in {1: (8, 16, 32, 64), 2: (4, 8, 16, 32), 4: (8, 16)}[W] and 16 * R * g == d
@@ -362,28 +362,37 @@ def test_fused_plan_word_width(lib):
         q = b.sk_fused_plan_describe(P16, 1 << 20, 128, 128, 8, d, 4, **MI355X)
         assert (q["fused"], q["words"], q["rows_per_wave"], q["groups"], q["per_cu"],
                 q["slices"]) == (1, 1, R, 1, per_cu, 1)
-    # two words per lane and R <= 8: two per CU, 64-row stages, chunks for 512
+    # FP32 of at most 64 columns: one word per lane, any width or stride;
+    # R = 8 two per CU, 64-row stages, chunks for 512 workgroups
     q = b.sk_fused_plan_describe(P32, 1 << 22, 64, 64, 16, 128, 4, **MI355X)
     assert (q["words"], q["rows_per_wave"], q["per_cu"], q["stage_rows"], q["grid"]) == \
-        (2, 8, 2, 64, 512)
+        (1, 8, 2, 64, 512)
+    for n, lda, align in ((1, 1, 4), (31, 33, 4), (64, 65, 4)):
+        q = b.sk_fused_plan_describe(P32, 1 << 20, n, lda, align, 512, 4, **MI355X)
+        assert (q["fused"], q["words"], q["rows_per_wave"], q["per_cu"]) == (1, 1, 32, 2)
+    # two words per lane and R <= 8 (FP32 between 65 and 128 columns)
+    q = b.sk_fused_plan_describe(P32, 1 << 22, 128, 128, 16, 128, 4, **MI355X)
+    assert (q["words"], q["rows_per_wave"], q["per_cu"], q["stage_rows"]) == (2, 8, 2, 64)
 
 
 def test_fused_plan_alignment_and_validation(lib):
     P16, P32 = b.SK_PRECISION_F16ACC, b.SK_PRECISION_F32
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 16, 512, 4, **MI355X)["fused"] == 1
-    # wide FP16 rows with an 8-byte base or lda % 4 != 0, an odd FP32 lda: the fallback
+    # wide FP16 rows with an 8-byte base or lda % 4 != 0, an odd FP32 lda
+    # above 64 columns: the fallback
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 8, 512, 4, **MI355X)["fused"] == 0
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 258, 16, 512, 4, **MI355X)["fused"] == 0
     assert b.sk_fused_plan_describe(P32, 1 << 20, 256, 257, 16, 512, 4, **MI355X)["fused"] == 0
     assert b.sk_fused_plan_describe(P16, 1 << 20, 64, 64, 16, 128, 4, **MI355X)["fused"] == 1
-    # narrow rows are covered (one word per lane for FP16, two for FP32);
-    # an odd FP32 width or lda is not
+    # narrow rows are covered (one word per lane, any FP32 width up to 64);
+    # an odd FP32 width or lda above 64 columns is not
     assert b.sk_fused_plan_describe(P16, 1 << 20, 60, 60, 16, 128, 4, **MI355X)["fused"] == 1
     assert b.sk_fused_plan_describe(P32, 1 << 20, 62, 62, 16, 128, 4, **MI355X)["fused"] == 1
     assert b.sk_fused_plan_describe(P16, 1 << 20, 2, 2, 8, 512, 4, **MI355X)["fused"] == 1
     assert b.sk_fused_plan_describe(P32, 1 << 20, 2, 2, 8, 512, 4, **MI355X)["fused"] == 1
-    assert b.sk_fused_plan_describe(P32, 1 << 20, 31, 31, 16, 128, 4, **MI355X)["fused"] == 0
-    assert b.sk_fused_plan_describe(P32, 1 << 20, 1, 1, 16, 128, 4, **MI355X)["fused"] == 0
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 31, 31, 16, 128, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 1, 1, 16, 128, 4, **MI355X)["fused"] == 1
+    assert b.sk_fused_plan_describe(P32, 1 << 20, 65, 65, 16, 128, 4, **MI355X)["fused"] == 0
     # LDS smaller than the kernel's stages
     assert b.sk_fused_plan_describe(P16, 1 << 20, 256, 256, 16, 512, 4, num_cu=256,
                                     max_lds=64 * 1024)["fused"] == 0

@@ -179,20 +179,23 @@ def test_register_row_chunks_and_padded_strides(precision):
 
 
 def test_register_forced_errors():
-    """SK_VARIANT_REG on a shape it does not cover (FP32 with an odd n = 31),
-    without a workspace, with a misaligned one, or together with another
-    variant."""
+    """SK_VARIANT_REG on a shape it does not cover (d = 40, not a multiple
+    of 16), without a workspace, with a misaligned one, or together with
+    another variant."""
     d, zeta = 64, 4
-    A = to_dev(inputs.gaussian(4096, 31))
+    A = to_dev(inputs.gaussian(4096, 128))
     ri, v = b.meta(1, 4096, d, zeta, device=dev())
-    B = torch.empty((d, 31), dtype=torch.float32, device=dev())
+    ri40, v40 = b.meta(1, 4096, 40, zeta, device=dev())
+    B = torch.empty((40, 128), dtype=torch.float32, device=dev())
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev())
     A2 = to_dev(inputs.gaussian(4096, 128))
     B2 = torch.empty((d, 128), dtype=torch.float32, device=dev())
     need = b.sk_apply_workspace_size(b.SK_PRECISION_F32, 4096, 128, d, zeta, b.SK_VARIANT_REG)
     ws2 = torch.empty(need + 64, dtype=torch.uint8, device=dev())
+    with pytest.raises(b.SketchError) as e:
+        b.sk_apply_f32(A, 4096, 128, 128, ri40, v40, zeta, B, 40, 128, b.SK_VARIANT_REG, ws, 0)
+    assert e.value.status == b.SK_ERR_UNSUPPORTED
     for Ax, Bx, w, nbytes, flags, expect in [
-            (A, B, ws, 0, b.SK_VARIANT_REG, b.SK_ERR_UNSUPPORTED),
             (A2, B2, None, 0, b.SK_VARIANT_REG, b.SK_ERR_NULL),
             (A2, B2, ws2[4:], need, b.SK_VARIANT_REG, b.SK_ERR_ALIGN),
             (A2, B2, ws2, need - 4, b.SK_VARIANT_REG, b.SK_ERR_ARG),

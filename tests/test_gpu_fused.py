@@ -187,6 +187,29 @@ def test_fused_f32_word_width_by_alignment(offset, lda):
     assert np.array_equal(B, oracle.sketch_f64(A_host, ri, v, d, zeta))
 
 
+@pytest.mark.parametrize("m,n,lda,offset,d,zeta", [
+    (5000, 1, 1, 0, 512, 4),        # a vector
+    (3001, 31, 33, 1, 256, 16),     # odd width and stride, 4-byte aligned base
+    (4096, 63, 64, 3, 128, 1),      # 63 columns, CountSketch
+    (2000, 64, 67, 0, 1024, 4),     # 64 columns, R = 64 (one per CU)
+])
+def test_fused_f32_one_word_lanes(m, n, lda, offset, d, zeta):
+    """FP32 of at most 64 columns runs one word per lane with 4-byte loads:
+    any width, stride and base.  Integer inputs keep every sum exact, so the
+    sketch equals the fp64 oracle bit for bit."""
+    say(f"fused f32 one word m={m} n={n} lda={lda} offset={offset} d={d} zeta={zeta}")
+    A = inputs.integer_matrix(m + 1, lda, -8, 8, seed=31)
+    flat = to_dev(A).reshape(-1)
+    Ad = flat[offset:offset + m * lda].reshape(m, lda)[:, :n]
+    p = b.sk_fused_plan_describe(b.SK_PRECISION_F32, m, n, lda, 16 if offset == 0 else 4, d,
+                                 zeta, **MI355X)
+    assert (p["fused"], p["words"]) == (1, 1)
+    B = run_fused(Ad, d, zeta, 5, "f32")
+    A_host = np.ascontiguousarray(A.reshape(-1)[offset:offset + m * lda].reshape(m, lda)[:, :n])
+    ri, v = oracle.meta_ref(5, m, d, zeta)
+    assert np.array_equal(B, oracle.sketch_f64(A_host, ri, v, d, zeta))
+
+
 @pytest.mark.parametrize("precision", ["f32", "f16acc"])
 def test_fused_empty_input(precision):
     d, n = 64, 128
