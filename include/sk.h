@@ -62,6 +62,10 @@ typedef enum sk_status {
 #define SK_VARIANT_LDS  4u  /* LDS-privatized partial sketches */
 #define SK_VARIANT_REG  8u  /* partial sketches in registers, fixed order of
                                additions (reproducible) */
+#define SK_COMBINE_F32 16u  /* FP16 output with a workspace: add the FP16
+                               row-chunk partials in FP32 and round the total
+                               to FP16 once (default: FP16 nearest-even
+                               additions, as for every other contribution) */
 
 /* wiring argument of sk_apply_blockperm_ex */
 #define SK_WIRING_SHIFT  0
@@ -126,50 +130,22 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
  *              SK_VARIANT_LDS: each workgroup keeps a private FP32 partial
  *                of a column slice (and a group of stack blocks) in LDS,
  *                updated by read, add and integer compare-and-swap, and
- *                flushes it once;
- *              SK_VARIANT_REG: each workgroup streams a chunk of rows (and
- *                their metadata) through LDS and each wavefront keeps its
- *                own output rows' partial in registers; the partials go to
- *                the workspace and a second kernel writes B as their sum.
- *                Needs a workspace, zeta <= 8, d % 16 == 0; FP32 up to 64
- *                columns any rows, wider: n and lda even and A 8-byte
- *                aligned; FP16: A 8-byte aligned, wider than 128 columns
- *                n and lda multiples of 4 and A 16-byte aligned: shapes
- *                sk_fused_plan_describe reports as covered, with zeta <= 8.  Its fast path
- *                assumes |val| = float32(1/sqrt(zeta)), as sk_meta_generate
- *                writes; a workgroup whose rows hold any other value redoes
- *                them with a per-hit product (about three times slower for
- *                that chunk, same result rules).
- *            0 picks REG where it covers the shape and the workspace is
- *            large enough for it (16-byte aligned), else LDS when the
- *            partial fits in LDS and zeta <= 64, else FLAT.  At 2^20 x
- *            256, d = 512, zeta = 4 REG takes 0.20 ms and LDS 0.25 ms
- *            (FP16, with the reduce).
- *   workspace, workspace_bytes
- *            optional device scratch for the REG and LDS variants (4-byte
- *            aligned, 16 for REG; disjoint from every other buffer; size
- *            from sk_apply_workspace_size).  With a workspace the partials
- *            are stored there and a second kernel writes B as their sum, in
- *            a fixed order (no global atomics, no separate zeroing of B).
- *            NULL: the LDS partials are added to B with global atomics.
- *            Ignored by the FLAT variant.  The caller owns it; its contents
- *            on return are unspecified.  Calls that share a workspace must
- *            be ordered (same stream).
- * Order of additions: REG is fixed (reproducible bit for bit); LDS follows
- * which wavefront's compare-and-swap lands first, and FLAT the atomics'
- * arrival, so neither is reproducible.
- * Errors: SK_ERR_NULL (also: SK_VARIANT_REG without a workspace),
- * SK_ERR_SHAPE (n, d < 1, zeta range, d % zeta, lda/ldb < n), SK_ERR_ARG
- * (two variants, aliasing, workspace smaller than required), SK_ERR_ALIGN
- * (workspace not 4-byte aligned, or not 16-byte aligned with
- * SK_VARIANT_REG), SK_ERR_UNSUPPORTED (SK_VARIANT_LDS forced where the
- * partial cannot fit in LDS or zeta > 64; SK_VARIANT_REG forced on a shape
- * it does not cover).
+ *                adds it once to B with global atomics (B is zeroed first
+ *                unless SK_ACCUMULATE).
+ *            0 picks LDS when the partial fits in LDS and zeta <= 64, else
+ *            FLAT.  The call allocates nothing and takes no workspace;
+ *            sk_apply_f32_ws adds the workspace-based variants.
+ * Order of additions: LDS follows which wavefront's compare-and-swap lands
+ * first, FLAT the atomics' arrival, so neither is reproducible bit for bit.
+ * Errors: SK_ERR_NULL (also SK_VARIANT_REG, which needs the workspace of
+ * sk_apply_f32_ws), SK_ERR_SHAPE (n, d < 1, zeta range, d % zeta,
+ * lda/ldb < n), SK_ERR_ARG (unknown flags, two variants, aliasing),
+ * SK_ERR_UNSUPPORTED (SK_VARIANT_LDS forced where the partial cannot fit in
+ * LDS or zeta > 64; SK_VARIANT_REG on a shape it does not cover), SK_ERR_HIP.
  */
 sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda,
                        const int32_t *row_idx, const float *val, int32_t zeta,
-                       float *B, int32_t d, int64_t ldb, uint32_t flags,
-                       void *workspace, size_t workspace_bytes, void *stream);
+                       float *B, int32_t d, int64_t ldb, uint32_t flags, void *stream);
 
 /*
  * sk_apply_f16acc: FP16-accumulated sketch.
@@ -184,20 +160,77 @@ sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda,
  *            aligned.  Overflow gives +-inf, inf + -inf gives NaN.
  *   flags    as for sk_apply_f32.  SK_VARIANT_FLAT is the page's design: one
  *            no-return packed global atomic per contribution pair.
- *            SK_VARIANT_REG and SK_VARIANT_LDS accumulate FP16 partials of
- *            row chunks (packed f16x2 words, nearest-even additions; REG in
- *            registers, LDS in LDS); with a workspace the partials are
- *            then added in a fixed order in FP32 and the total rounded to
- *            FP16 once (without one, LDS adds them to B with packed FP16
- *            atomics).
- *   workspace, workspace_bytes  as for sk_apply_f32.
- * Errors: as sk_apply_f32, plus SK_ERR_SHAPE for odd n and SK_ERR_ALIGN for
- * odd lda/ldb or misaligned A/B.
+ *            SK_VARIANT_LDS accumulates FP16 partials of row chunks in LDS
+ *            (packed f16x2 words, nearest-even additions) and adds them to
+ *            B with packed FP16 nearest-even atomics.  Every addition is an
+ *            FP16 nearest-even addition.
+ * Errors: as sk_apply_f32, plus SK_ERR_SHAPE for odd n, SK_ERR_ALIGN for
+ * odd lda/ldb or misaligned A/B, and SK_ERR_ARG for SK_COMBINE_F32 (there
+ * is no reduce without a workspace).
  */
 sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *row_idx, const float *val, int32_t zeta,
-                          uint16_t *B, int32_t d, int64_t ldb, uint32_t flags,
+                          uint16_t *B, int32_t d, int64_t ldb, uint32_t flags, void *stream);
+
+/*
+ * sk_apply_f32_ws / sk_apply_f16acc_ws: sk_apply_f32 / sk_apply_f16acc with
+ * a caller workspace, which adds the store-and-reduce flush and the register
+ * variant (same sketch definition and argument rules as above).
+ *
+ *   flags    as above, plus
+ *              SK_VARIANT_REG: each workgroup streams a chunk of rows (and
+ *                their metadata) through LDS and each wavefront keeps its
+ *                own output rows' partial in registers; the partials go to
+ *                the workspace and a second kernel writes B as their sum.
+ *                Needs a workspace, zeta <= 8, d % 16 == 0; FP32 up to 64
+ *                columns any rows, wider: n and lda even and A 8-byte
+ *                aligned; FP16: A 8-byte aligned, wider than 128 columns
+ *                n and lda multiples of 4 and A 16-byte aligned: shapes
+ *                sk_fused_plan_describe reports as covered, with zeta <= 8.  Its fast path
+ *                assumes |val| = float32(1/sqrt(zeta)), as sk_meta_generate
+ *                writes; a workgroup whose rows hold any other value redoes
+ *                them with a per-hit product (about three times slower for
+ *                that chunk, same result rules).
+ *              SK_COMBINE_F32 (FP16 only): the reduce adds the FP16
+ *                partials in FP32 and rounds the total to FP16 once (this
+ *                library's option, more accurate than the FP16 additions of
+ *                the default; ignored where no reduce runs: FLAT, or LDS
+ *                without a workspace).  Without it every addition, the
+ *                reduce's included, is an FP16 nearest-even addition.
+ *            0 picks REG where it covers the shape and the workspace is
+ *            large enough for it (16-byte aligned), else LDS when the
+ *            partial fits in LDS and zeta <= 64, else FLAT.  At 2^20 x
+ *            256, d = 512, zeta = 4 REG takes 0.20 ms and LDS 0.25 ms
+ *            (FP16, with the reduce).
+ *   workspace, workspace_bytes
+ *            optional device scratch for the REG and LDS variants (4-byte
+ *            aligned, 16 for REG; disjoint from every other buffer; size
+ *            from sk_apply_workspace_size).  With a workspace the partials
+ *            are stored there and a second kernel writes B as their sum, in
+ *            a fixed order: four contiguous quarters of the row chunks,
+ *            each summed in chunk order from +0, then the quarter sums added
+ *            in order onto B (SK_ACCUMULATE) or +0 (no global atomics, no
+ *            separate zeroing of B).  NULL: as sk_apply_f32 /
+ *            sk_apply_f16acc.  Ignored by the FLAT variant.  The caller owns
+ *            it; its contents on return are unspecified.  Calls that share a
+ *            workspace must be ordered (same stream).
+ * Order of additions: REG is fixed (reproducible bit for bit): each output
+ * entry adds its contributions of a row chunk in ascending row order, from
+ * +0, and the chunk partials in the reduce's order above.
+ * Errors: as sk_apply_f32 / sk_apply_f16acc, plus SK_ERR_NULL
+ * (SK_VARIANT_REG without a workspace), SK_ERR_ARG (SK_COMBINE_F32 on the
+ * FP32 call, workspace smaller than required), SK_ERR_ALIGN (workspace not
+ * 4-byte aligned, or not 16-byte aligned with SK_VARIANT_REG),
+ * SK_ERR_UNSUPPORTED (SK_VARIANT_REG forced on a shape it does not cover).
+ */
+sk_status sk_apply_f32_ws(const float *A, int64_t m, int32_t n, int64_t lda,
+                          const int32_t *row_idx, const float *val, int32_t zeta,
+                          float *B, int32_t d, int64_t ldb, uint32_t flags,
                           void *workspace, size_t workspace_bytes, void *stream);
+sk_status sk_apply_f16acc_ws(const float *A, int64_t m, int32_t n, int64_t lda,
+                             const int32_t *row_idx, const float *val, int32_t zeta,
+                             uint16_t *B, int32_t d, int64_t ldb, uint32_t flags,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sk_apply_lowp: the reduced-precision sketch with a choice of contribution
@@ -237,8 +270,8 @@ sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
                         uint64_t sr_seed, int64_t row_offset, uint32_t flags, void *stream);
 
 /*
- * sk_apply_workspace_size: bytes of workspace that sk_apply_f32
- * (precision SK_PRECISION_F32) or sk_apply_f16acc (SK_PRECISION_F16ACC)
+ * sk_apply_workspace_size: bytes of workspace that sk_apply_f32_ws
+ * (precision SK_PRECISION_F32) or sk_apply_f16acc_ws (SK_PRECISION_F16ACC)
  * uses for these sizes and flags on the current device, whatever lda and
  * A's alignment: SK_VARIANT_REG the register plan (for A with lda = n and
  * an aligned base), SK_VARIANT_LDS the LDS plans, 0 the larger of the two.
@@ -257,13 +290,13 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
  * randomness can be made inside the apply kernel, so S is never stored.)
  *
  * Computes exactly what sk_meta_generate(seed, row_offset, m, d, zeta)
- * followed by sk_apply_f32 / sk_apply_f16acc (same flags) computes: the
+ * followed by sk_apply_f32_ws / sk_apply_f16acc_ws (same flags) computes: the
  * same S, every contribution the FP32 product a*val, and for FP16 each
  * contribution rounded to FP16 nearest-even and accumulated with FP16
  * nearest-even additions.  The fused kernel keeps each workgroup's partial
  * in registers and writes it once to the workspace; a reduce kernel then
- * writes B as the sum of the partials in a fixed order (no atomics, B needs
- * no separate zeroing).  FP32 matrices wider than 128 columns whose rows
+ * writes B as the sum of the partials in a fixed order (sk_apply_f16acc_ws's
+ * register variant's order; no atomics, B needs no separate zeroing).  FP32 matrices wider than 128 columns whose rows
  * allow 16-byte loads (lda % 4 == 0, A 16-byte aligned) take four partial
  * words per lane (256 columns per workgroup) instead of two; the order of
  * each output word's additions is fixed either way.  Shapes the fused
@@ -281,7 +314,9 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
  *            aligned).
  *   B        device float (FP32) or IEEE binary16 bits (FP16: ldb even, B
  *            4-byte aligned), d x n, ldb >= n.
- *   flags    SK_ACCUMULATE or 0.
+ *   flags    SK_ACCUMULATE, and for FP16 SK_COMBINE_F32 (the reduce adds
+ *            the FP16 partials in FP32 and rounds once; by default every
+ *            addition is an FP16 nearest-even addition).
  *   workspace, workspace_bytes
  *            device scratch, required when m > 0: 16-byte aligned, disjoint
  *            from A and B, at least sk_sketch_workspace_size bytes.  The

@@ -25,7 +25,8 @@ itself; the one function without such a pin says so in its docstring
 """
 from .philox import philox4x32_10, philox_scalar, PHILOX4x32, PHILOX4x64
 from .sparsestack import (scale_f32, meta_ref, sketch_matrix, dense_S, sketch_f64,
-                          countsketch_f64, sketch_f16_rn_emul, rn_f16_add)
+                          countsketch_f64, sketch_f16_rn_emul, rn_f16_add, in_block,
+                          f16_erasures, f16_zero_subnormal_counts)
 from .blockperm import (fmix32, perm_sigma, shift_wiring, blockperm_params,
                         blockperm_hash, blockperm_hash_s, blockperm_matrix, blockperm_dense_S,
                         blockperm_f64, affine_params, affine_wiring, wiring, prime_factors)
@@ -37,7 +38,8 @@ from .lowp import (sr_words, f16_neighbours, sr_f16, rn_bf16, rn_bf16_add,
 __all__ = [
     "philox4x32_10", "philox_scalar", "PHILOX4x32", "PHILOX4x64",
     "scale_f32", "meta_ref", "sketch_matrix", "dense_S", "sketch_f64",
-    "countsketch_f64", "sketch_f16_rn_emul", "rn_f16_add",
+    "countsketch_f64", "sketch_f16_rn_emul", "rn_f16_add", "in_block", "f16_erasures",
+    "f16_zero_subnormal_counts",
     "fmix32", "perm_sigma", "shift_wiring", "blockperm_params",
     "blockperm_hash", "blockperm_matrix", "blockperm_dense_S", "blockperm_f64",
     "blockperm_hash_s", "affine_params", "affine_wiring", "wiring", "prime_factors",

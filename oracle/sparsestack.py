@@ -24,7 +24,11 @@ Readings where the page is silent (each listed in the design notes):
   is the multiply-high floor(w * (d/zeta) / 2^32) and the sign is negative
   when bit 0 of w is set ("coupled": one word routes and signs);
 * the stored value is sign * float32(1/sqrt(zeta)), the scale rounded once
-  from fp64 on the host.
+  from fp64 on the host;
+* entry i*zeta + t belongs to stack block t, a CountSketch of the block's
+  d/zeta rows: an entry whose row lies outside [t*d/zeta, (t+1)*d/zeta)
+  is not an entry of a SparseStack S and contributes nothing, in every
+  function here (the metadata this oracle generates never holds one).
 """
 import numpy as np
 import scipy.sparse as sp
@@ -68,20 +72,33 @@ def meta_ref(seed, m, d, zeta, row_offset=0):
     return row_idx.reshape(-1), val.reshape(-1)
 
 
+def in_block(row_idx, d, zeta):
+    """Mask of metadata entries whose row lies in their own stack block
+    (entry i*zeta + t in rows [t*d/zeta, (t+1)*d/zeta))."""
+    db = d // zeta
+    r = np.asarray(row_idx, dtype=np.int64)
+    t = np.arange(r.size, dtype=np.int64) % zeta
+    return (r >= t * db) & (r < (t + 1) * db)
+
+
 def sketch_matrix(row_idx, val, m, d, zeta):
-    """S as a d x m sparse matrix (fp64 entries equal to the stored fp32)."""
+    """S as a d x m sparse matrix (fp64 entries equal to the stored fp32);
+    entries outside their block are left out."""
     cols = np.repeat(np.arange(m, dtype=np.int64), zeta)
-    return sp.csr_matrix((val.astype(np.float64), (row_idx.astype(np.int64), cols)),
-                         shape=(d, m))
+    keep = in_block(row_idx, d, zeta)
+    return sp.csr_matrix((val.astype(np.float64)[keep],
+                          (row_idx.astype(np.int64)[keep], cols[keep])), shape=(d, m))
 
 
 def dense_S(row_idx, val, m, d, zeta):
     """Dense S built entry by entry (tiny inputs only)."""
+    db = d // zeta
     S = np.zeros((d, m), dtype=np.float64)
     for i in range(m):
         for t in range(zeta):
             e = i * zeta + t
-            S[row_idx[e], i] += float(val[e])
+            if t * db <= row_idx[e] < (t + 1) * db:
+                S[row_idx[e], i] += float(val[e])
     return S
 
 
@@ -133,7 +150,11 @@ def _accumulate_flat(A, row_idx, val, d, zeta, e0, e1):
     if e1 <= e0:
         return B
     e = np.arange(e0, e1, dtype=np.int64)
-    r = row_idx[e0:e1].astype(np.int64)
+    keep = in_block(row_idx, d, zeta)[e0:e1]
+    e = e[keep]
+    if e.size == 0:
+        return B
+    r = row_idx[e].astype(np.int64)
     order = np.argsort(r, kind="stable")          # by bucket, then entry
     counts = np.bincount(r, minlength=d)
     starts = np.concatenate(([0], np.cumsum(counts)[:-1]))
@@ -145,7 +166,7 @@ def _accumulate_flat(A, row_idx, val, d, zeta, e0, e1):
     return B
 
 
-def sketch_f16_rn_emul(A, row_idx, val, d, zeta, chunk_rows=None):
+def sketch_f16_rn_emul(A, row_idx, val, d, zeta, chunk_rows=None, combine="f16", B0=None):
     """FP16-accumulated sketch with per-contribution RN conversion.
 
     chunk_rows=None: every output entry adds its contributions one at a
@@ -153,15 +174,87 @@ def sketch_f16_rn_emul(A, row_idx, val, d, zeta, chunk_rows=None):
     contribution applied row by row.
     chunk_rows=R: each run of R input rows is accumulated that way into its
     own FP16 partial starting from +0, and the partials are then added in
-    FP16 in chunk order.  Both orders are valid instances of "accumulate
-    the RN contributions with FP16 RN additions"; atomics fix no order.
+    chunk order.  combine="f16" adds them with FP16 RN additions: both
+    orders are then valid instances of "accumulate the RN contributions with
+    FP16 RN additions" (atomics fix no order).  combine="f32" instead sums
+    the FP16 partials in FP32 in chunk order and rounds the total to FP16
+    once: not the page's arithmetic, but a combine step a two-level
+    implementation may take (it is more accurate than FP16 additions).
+    B0 (float16 d x n): the sum starts from B0 instead of +0 (a sketch
+    accumulated onto an existing one); with combine="f32" B0 is the first
+    term of the FP32 sum.
     """
     m = A.shape[0]
-    if chunk_rows is None or chunk_rows >= m:
-        return _accumulate_flat(A, row_idx, val, d, zeta, 0, m * zeta)
-    B = np.zeros((d, A.shape[1]), dtype=np.float16)
-    for r0 in range(0, m, chunk_rows):
-        r1 = min(m, r0 + chunk_rows)
-        P = _accumulate_flat(A, row_idx, val, d, zeta, r0 * zeta, r1 * zeta)
-        B = rn_f16_add(B, P)
-    return B
+    if combine not in ("f16", "f32"):
+        raise ValueError("combine is 'f16' or 'f32'")
+    if chunk_rows is None:
+        B = _accumulate_flat(A, row_idx, val, d, zeta, 0, m * zeta)
+        return B if B0 is None else rn_f16_add(np.asarray(B0, np.float16), B)
+    parts = [_accumulate_flat(A, row_idx, val, d, zeta, r0 * zeta, min(m, r0 + chunk_rows) * zeta)
+             for r0 in range(0, m, chunk_rows)]
+    start = np.zeros((d, A.shape[1]), dtype=np.float16) if B0 is None else \
+        np.asarray(B0, dtype=np.float16)
+    if combine == "f16":
+        B = start
+        for P in parts:
+            B = rn_f16_add(B, P)
+        return B
+    acc = start.astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for P in parts:
+            acc = acc + P.astype(np.float32)
+        return acc.astype(np.float16)
+
+
+def f16_zero_subnormal_counts(q):
+    """For FP32 magnitudes q >= 0: (how many nonzero q convert to 0, how
+    many to a nonzero subnormal, how many are nonzero) under nearest-even
+    conversion to binary16.  With h = 2^-24 the subnormal spacing: (0, h/2]
+    goes to 0 (the tie h/2 to the even 0), (h/2, 2^-14 - h/2) to the
+    subnormals, and from 2^-14 - h/2 up (the tie there to the even 2^-14)
+    the result is normal."""
+    q = np.asarray(q, dtype=np.float32)
+    half_h = np.float32(2.0**-25)
+    top = np.float32(2.0**-14 - 2.0**-25)
+    nz = int(np.count_nonzero(q))
+    zero = int(np.count_nonzero((q > 0) & (q <= half_h)))
+    sub = int(np.count_nonzero((q > half_h) & (q < top)))
+    return zero, sub, nz
+
+
+def f16_erasures(A, row_idx, val, d, zeta):
+    """Counts of the FP16 conversion's losses at the bottom of the range
+    (FP16 page §IV-E, §V-E: nearest-even conversion sends every contribution
+    of magnitude at most h/2 = 2^-25 to zero, and keeps subnormals above it).
+
+    Returns (erased, subnormal, total): contributions q = fl32(a*val) with
+    q != 0 whose RN-to-FP16 conversion is zero, those that convert to a
+    nonzero subnormal (0 < |RN(q)| < 2^-14), and the nonzero contributions,
+    over the in-block metadata entries."""
+    mask = in_block(row_idx, d, zeta)
+    mag = np.abs(np.asarray(val, dtype=np.float32))
+    if mask.all() and mag.size and (mag == mag[0]).all():
+        # every entry of a row scales the row by the same magnitude c, and
+        # the sign does not change whether a product converts to zero or to
+        # a subnormal: count the row's products once and take zeta of them
+        c = mag[0]
+        m = A.shape[0]
+        erased = sub = total = 0
+        for r0 in range(0, m, 1 << 18):
+            q = np.abs(A[r0:r0 + (1 << 18)].astype(np.float32, copy=False)) * c
+            z, s_, t = f16_zero_subnormal_counts(q)
+            erased, sub, total = erased + z, sub + s_, total + t
+        return zeta * erased, zeta * sub, zeta * total
+    keep = np.nonzero(mask)[0]
+    erased = sub = total = 0
+    for e0 in range(0, keep.size, 1 << 16):
+        e = keep[e0:e0 + (1 << 16)]
+        q = A[e // zeta].astype(np.float32, copy=False) * val[e].astype(np.float32)[:, None]
+        with np.errstate(over="ignore"):
+            c = q.astype(np.float16)
+        nz = q != 0
+        total += int(nz.sum())
+        erased += int((nz & (c == 0)).sum())
+        ac = np.abs(c.astype(np.float64))
+        sub += int(((ac > 0) & (ac < 2.0**-14)).sum())
+    return erased, sub, total

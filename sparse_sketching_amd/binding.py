@@ -23,6 +23,7 @@ SK_ACCUMULATE = 1
 SK_VARIANT_FLAT = 2
 SK_VARIANT_LDS = 4
 SK_VARIANT_REG = 8
+SK_COMBINE_F32 = 16
 SK_PRECISION_F32 = 0
 SK_PRECISION_F16ACC = 1
 SK_FORMAT_F16 = 0
@@ -41,10 +42,17 @@ _SIGNATURES = {
                                      _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "sk_apply_f32": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
                                 _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
-                                _c.c_uint32, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+                                _c.c_uint32, _c.c_void_p]),
     "sk_apply_f16acc": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
                                    _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
+                                   _c.c_uint32, _c.c_void_p]),
+    "sk_apply_f32_ws": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
+                                   _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
                                    _c.c_uint32, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "sk_apply_f16acc_ws": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64,
+                                      _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_void_p,
+                                      _c.c_int32, _c.c_int64, _c.c_uint32, _c.c_void_p,
+                                      _c.c_size_t, _c.c_void_p]),
     "sk_apply_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32,
                                            _c.c_int32, _c.c_uint32, _c.POINTER(_c.c_size_t)]),
     "sk_apply_blockperm": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_int32,
@@ -159,6 +167,26 @@ def _check(fn, status):
         raise SketchError(fn, status)
 
 
+def _launch_stream(stream):
+    """The torch stream object of a launch (None: the current stream)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
+def _keep(stream, *tensors):
+    """Mark tensors the helpers allocated as in use on the launch stream, so
+    the caching allocator does not hand their memory to another stream while
+    the enqueued kernels may still read or write it."""
+    s = _launch_stream(stream)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 # ---- the C entry points, same names and argument order -------------------
 
 def sk_meta_generate(seed, row_offset, m, d, zeta, row_idx, val, stream=None):
@@ -166,16 +194,28 @@ def sk_meta_generate(seed, row_offset, m, d, zeta, row_idx, val, stream=None):
         seed, row_offset, m, d, zeta, _ptr(row_idx), _ptr(val), _stream(stream)))
 
 
-def sk_apply_f32(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, workspace=None,
-                 workspace_bytes=0, stream=None):
+def sk_apply_f32(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, stream=None):
     _check("sk_apply_f32", load().sk_apply_f32(
+        _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, flags,
+        _stream(stream)))
+
+
+def sk_apply_f16acc(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, stream=None):
+    _check("sk_apply_f16acc", load().sk_apply_f16acc(
+        _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, flags,
+        _stream(stream)))
+
+
+def sk_apply_f32_ws(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, workspace=None,
+                    workspace_bytes=0, stream=None):
+    _check("sk_apply_f32_ws", load().sk_apply_f32_ws(
         _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, flags,
         _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)))
 
 
-def sk_apply_f16acc(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, workspace=None,
-                    workspace_bytes=0, stream=None):
-    _check("sk_apply_f16acc", load().sk_apply_f16acc(
+def sk_apply_f16acc_ws(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags=0, workspace=None,
+                       workspace_bytes=0, stream=None):
+    _check("sk_apply_f16acc_ws", load().sk_apply_f16acc_ws(
         _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, flags,
         _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)))
 
@@ -218,6 +258,7 @@ def lstsq_qr(SA, Sb, stream=None):
     x = torch.empty(n, dtype=torch.float32, device=SA.device)
     ws = torch.empty(sk_lstsq_workspace_size(d, n), dtype=torch.uint8, device=SA.device)
     sk_lstsq_qr_f32(SA, d, n, SA.stride(0), Sb, x, ws, 0, stream)
+    _keep(stream, x, ws)
     return x
 
 
@@ -319,6 +360,7 @@ def meta(seed, m, d, zeta, row_offset=0, device=None, stream=None):
     row_idx = torch.empty(m * zeta, dtype=torch.int32, device=device)
     val = torch.empty(m * zeta, dtype=torch.float32, device=device)
     sk_meta_generate(seed, row_offset, m, d, zeta, row_idx, val, stream)
+    _keep(stream, row_idx, val)
     return row_idx, val
 
 
@@ -337,9 +379,10 @@ def apply(A, row_idx, val, zeta, d, precision="f16acc", out=None, flags=0, ws=Tr
     """B = S A from metadata; precision "f32" (float32 B) or "f16acc" (float16 B).
 
     ws=True allocates the workspace the chosen variant needs (the LDS
-    variant's store-and-reduce flush, or the register variant's partials);
-    ws=None makes the LDS variant flush with global atomics; a byte tensor
-    is used as the workspace."""
+    variant's store-and-reduce flush, or the register variant's partials)
+    and calls sk_apply_*_ws; ws=None calls sk_apply_f32 / sk_apply_f16acc,
+    which take no workspace (the LDS variant flushes with global atomics);
+    a byte tensor is used as the workspace."""
     import torch
     _need_device(A, torch.float32, "A")
     m, n = A.shape
@@ -352,11 +395,18 @@ def apply(A, row_idx, val, zeta, d, precision="f16acc", out=None, flags=0, ws=Tr
         _need_device(val, torch.float32, "val")
         if row_idx.numel() < m * zeta or val.numel() < m * zeta:
             raise ValueError("metadata shorter than m*zeta")
+    fresh = None
     if ws is True:
-        ws = workspace(A, d, zeta, precision, flags)
-    fn = sk_apply_f16acc if precision == "f16acc" else sk_apply_f32
-    fn(A, m, n, A.stride(0) if m else n, row_idx if m else None, val if m else None, zeta,
-       out, d, out.stride(0), flags, ws, 0, stream)
+        ws = fresh = workspace(A, d, zeta, precision, flags)
+    lda = A.stride(0) if m else n
+    ri, v = (row_idx, val) if m else (None, None)
+    if ws is None:
+        fn = sk_apply_f16acc if precision == "f16acc" else sk_apply_f32
+        fn(A, m, n, lda, ri, v, zeta, out, d, out.stride(0), flags, stream)
+    else:
+        fn = sk_apply_f16acc_ws if precision == "f16acc" else sk_apply_f32_ws
+        fn(A, m, n, lda, ri, v, zeta, out, d, out.stride(0), flags, ws, 0, stream)
+    _keep(stream, out, fresh)
     return out
 
 
@@ -386,6 +436,7 @@ def apply_lowp(A, row_idx, val, zeta, d, fmt="f16", conv="rn", sr_seed=0, row_of
     c = SK_CONVERT_RN if conv == "rn" else SK_CONVERT_SR
     sk_apply_lowp(A, m, n, A.stride(0) if m else n, row_idx if m else None, val if m else None,
                   zeta, out, d, out.stride(0), f, c, sr_seed, row_offset, flags, stream)
+    _keep(stream, out)
     return out
 
 
@@ -411,11 +462,13 @@ def sketch_fused(A, d, zeta, seed, precision="f16acc", row_offset=0, out=None, f
     if out is None:
         out = torch.empty((d, n), dtype=dt, device=A.device)
     _need_device(out, dt, "out")
+    fresh = None
     if ws is None and m:
-        ws = sketch_workspace(A, d, zeta, precision)
+        ws = fresh = sketch_workspace(A, d, zeta, precision)
     fn = sk_sketch_f16acc if precision == "f16acc" else sk_sketch_f32
     fn(seed, row_offset, A, m, n, A.stride(0) if m else n, d, zeta, out, out.stride(0), flags,
        ws, 0, stream)
+    _keep(stream, out, fresh)
     return out
 
 
@@ -431,10 +484,12 @@ def blockperm(A, d, M, kappa, seed, s=1, out=None, flags=0, wiring="shift", ws=N
         out = torch.empty((d, n), dtype=torch.float32, device=A.device)
     _need_device(out, torch.float32, "out")
     w = SK_WIRING_SHIFT if wiring == "shift" else SK_WIRING_AFFINE
+    fresh = None
     if ws is None:
         nbytes = sk_blockperm_workspace_size(m, n, d, M, kappa, s, w)
         if nbytes:
-            ws = torch.empty(nbytes, dtype=torch.uint8, device=A.device)
+            ws = fresh = torch.empty(nbytes, dtype=torch.uint8, device=A.device)
     sk_apply_blockperm_ex(A, m, n, A.stride(0), d, M, kappa, s, w, seed, out, out.stride(0),
                           flags, ws, 0, stream)
+    _keep(stream, out, fresh)
     return out

@@ -35,7 +35,7 @@ const void *pick_zg(int zg, bool full, bool nt) {
 }
 
 template <class T>
-hipError_t launch_stack(const LdsPlan &p, StackApplyArgs &a, int accumulate, hipStream_t s) {
+hipError_t launch_stack(const LdsPlan &p, StackApplyArgs &a, int mode, hipStream_t s) {
     const bool full = p.slice == 64;
     // the kernel's slice width must match the plan the LDS and workspace
     // were sized for: two-word kernels exist for 64-lane slices only
@@ -51,7 +51,7 @@ hipError_t launch_stack(const LdsPlan &p, StackApplyArgs &a, int accumulate, hip
     e = hipLaunchKernel(kern, dim3((unsigned)p.grid), dim3(p.threads), params, p.lds_bytes, s);
     if (e != hipSuccess) return e;
     if (a.ws == nullptr) return hipSuccess;
-    return launch_stack_reduce<T>(a, a.sp * p.words, accumulate, s);
+    return launch_stack_reduce<T>(a, a.sp * p.words, mode, s);
 }
 
 StackApplyArgs make_args(const LdsPlan &p, const float *A, int64_t m, int32_t units, int64_t lda,
@@ -82,16 +82,16 @@ StackApplyArgs make_args(const LdsPlan &p, const float *A, int64_t m, int32_t un
 
 hipError_t launch_f32_lds(const LdsPlan &p, const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *ri, const float *v, int32_t zeta, float *B, int32_t d,
-                          int64_t ldb, uint32_t *ws, int accumulate, hipStream_t s) {
+                          int64_t ldb, uint32_t *ws, int mode, hipStream_t s) {
     StackApplyArgs a = make_args(p, A, m, n, lda, ri, v, zeta, B, d, ldb, ws);
-    return launch_stack<AccF32>(p, a, accumulate, s);
+    return launch_stack<AccF32>(p, a, mode, s);
 }
 
 hipError_t launch_f16_lds(const LdsPlan &p, const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *ri, const float *v, int32_t zeta, uint16_t *B, int32_t d,
-                          int64_t ldb, uint32_t *ws, int accumulate, hipStream_t s) {
+                          int64_t ldb, uint32_t *ws, int mode, hipStream_t s) {
     StackApplyArgs a = make_args(p, A, m, n / 2, lda, ri, v, zeta, B, d, ldb / 2, ws);
-    return launch_stack<AccF16>(p, a, accumulate, s);
+    return launch_stack<AccF16>(p, a, mode, s);
 }
 
 }  // namespace sk

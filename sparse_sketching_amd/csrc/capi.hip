@@ -4,31 +4,41 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "sk.h"
 #include "sk_internal.hpp"
 #include "sk_rng.hpp"
 
 namespace sk {
 
+// The per-device attributes are read once and kept in atomics (0 = not yet
+// read), so concurrent first calls from several host threads are safe: each
+// stores the same values.
 hipError_t dev_info(DevInfo *out) {
     constexpr int kMaxDev = 64;
-    static DevInfo cache[kMaxDev];
-    static bool have[kMaxDev];
+    static std::atomic<int> cache_cu[kMaxDev];
+    static std::atomic<int> cache_lds[kMaxDev];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDev && have[dev]) {
-        *out = cache[dev];
-        return hipSuccess;
+    const bool cached = dev >= 0 && dev < kMaxDev;
+    if (cached) {
+        const int cu = cache_cu[dev].load(std::memory_order_relaxed);
+        const int lds = cache_lds[dev].load(std::memory_order_relaxed);
+        if (cu > 0 && lds > 0) {
+            *out = DevInfo{cu, lds};
+            return hipSuccess;
+        }
     }
     DevInfo di{};
     e = hipDeviceGetAttribute(&di.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&di.max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDev) {
-        cache[dev] = di;
-        have[dev] = true;
+    if (cached && di.num_cu > 0 && di.max_lds > 0) {
+        cache_cu[dev].store(di.num_cu, std::memory_order_relaxed);
+        cache_lds[dev].store(di.max_lds, std::memory_order_relaxed);
     }
     *out = di;
     return hipSuccess;
@@ -147,13 +157,15 @@ int variant_count(uint32_t flags) {
 }
 
 // Checks shared by the SparseStack apply calls (FP32 and FP16 output).
+// extra_flags: the flags a precision adds to SK_ACCUMULATE and the variants
+// (SK_COMBINE_F32 for FP16 output).
 sk_status check_apply(const float *A, int64_t m, int32_t n, int64_t lda, const int32_t *row_idx,
                       const float *val, int32_t zeta, const void *B, size_t belem, int32_t d,
-                      int64_t ldb, uint32_t flags) {
+                      int64_t ldb, uint32_t flags, uint32_t extra_flags) {
     if (m < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0) return SK_ERR_SHAPE;
     if (lda < n || ldb < n) return SK_ERR_SHAPE;
     if (m > (INT64_MAX / 8) / (zeta > lda ? zeta : lda)) return SK_ERR_SHAPE;
-    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS | SK_VARIANT_REG))
+    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS | SK_VARIANT_REG | extra_flags))
         return SK_ERR_ARG;
     if (variant_count(flags) > 1) return SK_ERR_ARG;
     if (B == nullptr) return SK_ERR_NULL;
@@ -176,6 +188,9 @@ sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t
     hipError_t e = sk::dev_info(&di);
     if (e != hipSuccess) return SK_ERR_HIP;
     const bool accumulate = (flags & SK_ACCUMULATE) != 0;
+    // the reduce's mode: accumulate, and the FP32 combine of FP16 partials
+    const int mode = (accumulate ? sk::kReduceModeAccumulate : 0) |
+                     ((f16 && (flags & SK_COMBINE_F32)) ? sk::kReduceModeCombineF32 : 0);
     // the register variant: asked for, or by default where it covers the
     // shape and the workspace holds its partials (reproducible, and the
     // faster one there)
@@ -195,8 +210,7 @@ sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t
                        workspace_bytes >= fp.ws_bytes))
             return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, 0, 0, row_idx, val, d,
                                                zeta, scale_of(zeta), B, ldb,
-                                               static_cast<uint32_t *>(workspace),
-                                               accumulate ? 1 : 0, s));
+                                               static_cast<uint32_t *>(workspace), mode, s));
     }
     sk::LdsPlan plan{};
     const int64_t units = f16 ? n / 2 : n;
@@ -224,13 +238,13 @@ sk_status apply_dispatch(bool f16, const float *A, int64_t m, int32_t n, int64_t
         uint16_t *B16 = static_cast<uint16_t *>(B);
         if (use_lds)
             return hip_status(sk::launch_f16_lds(plan, A, m, n, lda, row_idx, val, zeta, B16, d, ldb,
-                                                 ws, accumulate ? 1 : 0, s));
+                                                 ws, mode, s));
         return hip_status(sk::launch_f16_flat(A, m, n, lda, row_idx, val, zeta, B16, d, ldb, s));
     }
     float *B32 = static_cast<float *>(B);
     if (use_lds)
         return hip_status(sk::launch_f32_lds(plan, A, m, n, lda, row_idx, val, zeta, B32, d, ldb, ws,
-                                             accumulate ? 1 : 0, s));
+                                             mode, s));
     return hip_status(sk::launch_f32_flat(A, m, n, lda, row_idx, val, zeta, B32, d, ldb, s));
 }
 
@@ -285,11 +299,13 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
     if (lda < n || ldb < n) return SK_ERR_SHAPE;
     if (m > (INT64_MAX / 8) / (zeta > lda ? zeta : lda)) return SK_ERR_SHAPE;
     if (f16 && n % 2 != 0) return SK_ERR_SHAPE;
-    if (flags & ~SK_ACCUMULATE) return SK_ERR_ARG;
+    if (flags & ~(SK_ACCUMULATE | (f16 ? SK_COMBINE_F32 : 0u))) return SK_ERR_ARG;
     if (B == nullptr) return SK_ERR_NULL;
     if (f16 && (ldb % 2 != 0 || (uintptr_t)B % 4 != 0)) return SK_ERR_ALIGN;
     const size_t bspan = span_bytes(d, n, ldb, belem);
     const bool accumulate = (flags & SK_ACCUMULATE) != 0;
+    const int mode = (accumulate ? sk::kReduceModeAccumulate : 0) |
+                     ((flags & SK_COMBINE_F32) ? sk::kReduceModeCombineF32 : 0);
     if (m > 0) {
         if (A == nullptr || workspace == nullptr) return SK_ERR_NULL;
         if (f16 && (lda % 2 != 0 || (uintptr_t)A % 8 != 0)) return SK_ERR_ALIGN;
@@ -315,8 +331,7 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
     if (sk::plan_fused(di, f16, m, n, lda, base_align(A), d, zeta, &fp))
         return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, nullptr,
                                            nullptr, d, zeta, scale, B, ldb,
-                                           static_cast<uint32_t *>(workspace),
-                                           accumulate ? 1 : 0, s));
+                                           static_cast<uint32_t *>(workspace), mode, s));
     // not covered by the fused kernel: metadata into the workspace, then
     // the LDS (or flat) apply with the rest of it
     char *w = static_cast<char *>(workspace);
@@ -325,8 +340,9 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
     float *v = reinterpret_cast<float *>(w + meta);
     hipError_t e = sk::launch_meta(seed, row_offset, m, d, zeta, scale, ri, v, s);
     if (e != hipSuccess) return SK_ERR_HIP;
-    return apply_dispatch(f16, A, m, n, lda, ri, v, zeta, B, d, ldb, flags & SK_ACCUMULATE,
-                          w + 2 * meta, workspace_bytes - 2 * meta, s);
+    return apply_dispatch(f16, A, m, n, lda, ri, v, zeta, B, d, ldb,
+                          flags & (SK_ACCUMULATE | SK_COMBINE_F32), w + 2 * meta,
+                          workspace_bytes - 2 * meta, s);
 }
 
 // BlockPerm launch plan: the register kernel where its shape rules hold;
@@ -493,10 +509,11 @@ sk_status sk_meta_generate(uint64_t seed, int64_t row_offset, int64_t m, int32_t
                                       (hipStream_t)stream));
 }
 
-sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda, const int32_t *row_idx,
-                       const float *val, int32_t zeta, float *B, int32_t d, int64_t ldb,
-                       uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
-    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 4, d, ldb, flags);
+sk_status sk_apply_f32_ws(const float *A, int64_t m, int32_t n, int64_t lda,
+                          const int32_t *row_idx, const float *val, int32_t zeta, float *B,
+                          int32_t d, int64_t ldb, uint32_t flags, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 4, d, ldb, flags, 0u);
     if (st != SK_OK) return st;
     st = check_workspace(workspace, workspace_bytes, A, m, n, lda, row_idx, val, zeta, B,
                          span_bytes(d, n, ldb, 4));
@@ -505,11 +522,18 @@ sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda, const 
                           workspace_bytes, (hipStream_t)stream);
 }
 
-sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
-                          const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
-                          int32_t d, int64_t ldb, uint32_t flags, void *workspace,
-                          size_t workspace_bytes, void *stream) {
-    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 2, d, ldb, flags);
+sk_status sk_apply_f32(const float *A, int64_t m, int32_t n, int64_t lda, const int32_t *row_idx,
+                       const float *val, int32_t zeta, float *B, int32_t d, int64_t ldb,
+                       uint32_t flags, void *stream) {
+    return sk_apply_f32_ws(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags, nullptr, 0, stream);
+}
+
+sk_status sk_apply_f16acc_ws(const float *A, int64_t m, int32_t n, int64_t lda,
+                             const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
+                             int32_t d, int64_t ldb, uint32_t flags, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 2, d, ldb, flags,
+                               SK_COMBINE_F32);
     if (st != SK_OK) return st;
     if (n % 2 != 0) return SK_ERR_SHAPE;
     if (ldb % 2 != 0 || (uintptr_t)B % 4 != 0) return SK_ERR_ALIGN;
@@ -521,6 +545,14 @@ sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
                           workspace_bytes, (hipStream_t)stream);
 }
 
+sk_status sk_apply_f16acc(const float *A, int64_t m, int32_t n, int64_t lda,
+                          const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
+                          int32_t d, int64_t ldb, uint32_t flags, void *stream) {
+    if (flags & SK_COMBINE_F32) return SK_ERR_ARG;
+    return sk_apply_f16acc_ws(A, m, n, lda, row_idx, val, zeta, B, d, ldb, flags, nullptr, 0,
+                              stream);
+}
+
 sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32_t d,
                                   int32_t zeta, uint32_t flags, size_t *bytes) {
     if (bytes == nullptr) return SK_ERR_NULL;
@@ -528,7 +560,8 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
     if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC) return SK_ERR_ARG;
     if (m < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0) return SK_ERR_SHAPE;
     if (precision == SK_PRECISION_F16ACC && n % 2 != 0) return SK_ERR_SHAPE;
-    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS | SK_VARIANT_REG))
+    const uint32_t extra = precision == SK_PRECISION_F16ACC ? SK_COMBINE_F32 : 0u;
+    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS | SK_VARIANT_REG | extra))
         return SK_ERR_ARG;
     if (variant_count(flags) > 1) return SK_ERR_ARG;
     if (m == 0 || (flags & SK_VARIANT_FLAT)) return SK_OK;
@@ -591,7 +624,7 @@ sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
     if (convert != SK_CONVERT_RN && convert != SK_CONVERT_SR) return SK_ERR_ARG;
     if (flags & ~SK_ACCUMULATE) return SK_ERR_ARG;
     if (row_offset < 0) return SK_ERR_SHAPE;
-    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 2, d, ldb, flags);
+    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 2, d, ldb, flags, 0u);
     if (st != SK_OK) return st;
     if (n % 2 != 0) return SK_ERR_SHAPE;
     if (ldb % 2 != 0 || (uintptr_t)B % 4 != 0) return SK_ERR_ALIGN;

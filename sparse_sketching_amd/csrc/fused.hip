@@ -401,7 +401,7 @@ const void *pick_fused(int W, int S, int R, int P, bool dual) {
 
 template <class T>
 hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int64_t ldb_units,
-                          int32_t units, int accumulate, hipStream_t s) {
+                          int32_t units, int mode, hipStream_t s) {
     const bool meta = fa.row_idx != nullptr;
     const void *kern =
         meta ? pick_fused<T, true>(p.words, p.stage_rows, p.rows_per_wave, p.load_sets, p.dual)
@@ -426,7 +426,7 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
     r.d = fa.d;
     r.chunks = fa.chunks;
     r.slices = (int32_t)((fa.slices * 64 * p.words + 127) / 128);   // 128-word workspace slices
-    return launch_stack_reduce<T>(r, 128, accumulate, s);
+    return launch_stack_reduce<T>(r, 128, mode, s);
 }
 
 }  // namespace
@@ -521,7 +521,7 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
 hipError_t launch_fused(const FusedPlan &p, bool f16, const float *A, int64_t m, int32_t n,
                         int64_t lda, uint64_t seed, int64_t row_offset, const int32_t *row_idx,
                         const float *val, int32_t d, int32_t zeta, float scale, void *B,
-                        int64_t ldb, uint32_t *ws, int accumulate, hipStream_t s) {
+                        int64_t ldb, uint32_t *ws, int mode, hipStream_t s) {
     FusedArgs a{};
     a.A = A;
     a.ws = ws;
@@ -539,8 +539,8 @@ hipError_t launch_fused(const FusedPlan &p, bool f16, const float *A, int64_t m,
     a.slices = (int32_t)p.slices;
     a.groups = p.groups;
     a.scale = scale;
-    if (f16) return launch_fused_t<AccF16>(p, a, B, ldb / 2, n / 2, accumulate, s);
-    return launch_fused_t<AccF32>(p, a, B, ldb, n, accumulate, s);
+    if (f16) return launch_fused_t<AccF16>(p, a, B, ldb / 2, n / 2, mode, s);
+    return launch_fused_t<AccF32>(p, a, B, ldb, n, mode, s);
 }
 
 }  // namespace sk

@@ -55,17 +55,24 @@ hipError_t launch_lowp_flat(const float *A, int64_t m, int32_t n, int64_t lda,
                             const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
                             int32_t d, int64_t ldb, bool bf16, bool sr, uint64_t sr_seed,
                             int64_t row_offset, hipStream_t stream);
+// The reduce's mode (bits): kReduceModeAccumulate adds onto B's current
+// words (B += ...); kReduceModeCombineF32 (FP16 only) sums the FP16 chunk
+// partials in FP32 and rounds the total once, instead of FP16 nearest-even
+// additions.
+constexpr int kReduceModeAccumulate = 1;
+constexpr int kReduceModeCombineF32 = 2;
+
 // LDS-privatized apply.  ws == NULL: the partials are added to B with global
-// atomics (B must hold its start value).  ws != NULL: the partials are
-// stored to ws (plan.ws_bytes) and a reduce kernel writes B (accumulate=0)
-// or adds to it (accumulate=1) in chunk order.
+// atomics (B must hold its start value; mode is ignored).  ws != NULL: the
+// partials are stored to ws (plan.ws_bytes) and a reduce kernel writes B
+// (or adds to it, mode & kReduceModeAccumulate) in chunk order.
 hipError_t launch_f32_lds(const LdsPlan &plan, const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *row_idx, const float *val, int32_t zeta, float *B,
-                          int32_t d, int64_t ldb, uint32_t *ws, int accumulate,
+                          int32_t d, int64_t ldb, uint32_t *ws, int mode,
                           hipStream_t stream);
 hipError_t launch_f16_lds(const LdsPlan &plan, const float *A, int64_t m, int32_t n, int64_t lda,
                           const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
-                          int32_t d, int64_t ldb, uint32_t *ws, int accumulate,
+                          int32_t d, int64_t ldb, uint32_t *ws, int mode,
                           hipStream_t stream);
 
 // Fused SparseStack sketch (metadata drawn in the apply kernel, fused.hip).
@@ -112,15 +119,15 @@ struct FusedPlan {
 // cover the call.
 bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
                 int32_t d, int32_t zeta, FusedPlan *plan);
-// Fused kernel into ws, then the chunk-order reduce into B (=, or += when
-// accumulate).  B is float* (FP32) or FP16 bits (uint16_t*), ldb in elements.
+// Fused kernel into ws, then the chunk-order reduce into B (mode: the
+// reduce's kReduceMode* bits).  B is float* (FP32) or FP16 bits (uint16_t*), ldb in elements.
 // row_idx / val NULL: the metadata is drawn from (seed, row_offset) in the
 // kernel; else it is read from them (the stored-metadata apply; seed and
 // row_offset unused) and scale must be float32(1/sqrt(zeta)).
 hipError_t launch_fused(const FusedPlan &plan, bool f16, const float *A, int64_t m, int32_t n,
                         int64_t lda, uint64_t seed, int64_t row_offset, const int32_t *row_idx,
                         const float *val, int32_t d, int32_t zeta, float scale, void *B,
-                        int64_t ldb, uint32_t *ws, int accumulate, hipStream_t stream);
+                        int64_t ldb, uint32_t *ws, int mode, hipStream_t stream);
 
 constexpr int kBlockPermMaxM = 1024;
 struct BlockPermArgs {

@@ -42,7 +42,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sk_apply_common.hpp"
+#include "sk_internal.hpp"
 
 namespace sk {
 
@@ -430,19 +433,35 @@ __global__ __launch_bounds__(kStackThreads) void k_stack_apply(const StackApplyA
     }
 }
 
+// How the reduce combines the chunk partials (the mode argument of
+// launch_stack_reduce): bit 0 adds onto B's current words (B += ...), bit 1
+// adds FP16 partials in FP32 and rounds the total once.
+constexpr int kReduceAccumulate = kReduceModeAccumulate;
+constexpr int kReduceCombineF32 = kReduceModeCombineF32;
+
 // B[r, u] (=|+=) the sum over chunks p = 0..P-1 of the workspace partials.
 // A 256-thread block takes 64 output words (one per lane).  Its 4
 // wavefronts each sum a contiguous quarter of the chunks in chunk order,
-// and the non-empty quarter sums are then added in quarter order onto the
-// existing B word (accumulate) or onto zero: a fixed order, so the result
-// is deterministic, with four times the loads in flight of one thread per
-// word.  The sums run in T::wide_t: FP32, also for FP16 partials, whose
-// total is rounded to FP16 once (the partials themselves hold FP16
-// nearest-even sums).
-template <class T>
+// starting from +0, and the non-empty quarter sums are then added in
+// quarter order onto the existing B word (accumulate) or onto +0: a fixed
+// order, so the result is deterministic, with four times the loads in
+// flight of one thread per word.
+// WIDE = false: every addition is one of the partials' own (FP32, or FP16
+// nearest-even per half for FP16 partials), so an FP16 sketch is accumulated
+// in FP16 from its first contribution to its stored value.  WIDE = true
+// (FP16 only): the FP16 partials are widened exactly to FP32, summed in
+// FP32, and the total is rounded to FP16 once.
+template <class T, bool WIDE>
 __global__ __launch_bounds__(256) void k_stack_reduce(const StackApplyArgs args, int32_t spw,
                                                        int32_t accumulate) {
-    typedef typename T::wide_t wide_t;
+    struct Narrow {
+        typedef uint32_t wide_t;
+        __device__ static wide_t widen(uint32_t w) { return w; }
+        __device__ static wide_t wide_add(wide_t a, wide_t b) { return T::sum(a, b); }
+        __device__ static uint32_t narrow(wide_t a) { return a; }
+    };
+    typedef typename std::conditional<WIDE, T, Narrow>::type C;
+    typedef typename C::wide_t wide_t;
     __shared__ wide_t part[4][64];
     typename T::out_t *B = reinterpret_cast<typename T::out_t *>(args.B);
     const int64_t total = (int64_t)args.d * args.units;
@@ -456,7 +475,7 @@ __global__ __launch_bounds__(256) void k_stack_reduce(const StackApplyArgs args,
         const bool act = k < total;
         const int r = act ? (int)(k / args.units) : 0;
         const int32_t u = act ? (int32_t)(k - (int64_t)r * args.units) : 0;
-        wide_t acc = T::widen(0u);
+        wide_t acc = C::widen(0u);
         if (act) {
             const int32_t s = u / spw;
             const int cl = u - s * spw;
@@ -467,33 +486,37 @@ __global__ __launch_bounds__(256) void k_stack_reduce(const StackApplyArgs args,
 #pragma unroll
                 for (int qq = 0; qq < 8; ++qq) w[qq] = src[(int64_t)(p + qq) * plane];
 #pragma unroll
-                for (int qq = 0; qq < 8; ++qq) acc = T::wide_add(acc, T::widen(w[qq]));
+                for (int qq = 0; qq < 8; ++qq) acc = C::wide_add(acc, C::widen(w[qq]));
             }
-            for (; p < p1; ++p) acc = T::wide_add(acc, T::widen(src[(int64_t)p * plane]));
+            for (; p < p1; ++p) acc = C::wide_add(acc, C::widen(src[(int64_t)p * plane]));
         }
         part[wave][lane] = acc;
         __syncthreads();
         if (wave == 0 && act) {
             const int64_t off = (int64_t)r * args.ldb + u;
-            wide_t sum = T::widen(accumulate ? T::get(B, off) : 0u);
+            wide_t sum = C::widen(accumulate ? T::get(B, off) : 0u);
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                if ((w + 1) * P / 4 > w * P / 4) sum = T::wide_add(sum, part[w][lane]);
-            T::put(B, off, T::narrow(sum));
+                if ((w + 1) * P / 4 > w * P / 4) sum = C::wide_add(sum, part[w][lane]);
+            T::put(B, off, C::narrow(sum));
         }
         __syncthreads();
     }
 }
 
-// Launch of k_stack_reduce over d x units output words.
+// Launch of k_stack_reduce over d x units output words; mode is a
+// combination of kReduceAccumulate and kReduceCombineF32.
 template <class T>
-hipError_t launch_stack_reduce(const StackApplyArgs &a, int32_t spw, int accumulate,
-                               hipStream_t s) {
+hipError_t launch_stack_reduce(const StackApplyArgs &a, int32_t spw, int mode, hipStream_t s) {
     const int64_t total = (int64_t)a.d * a.units;
     int64_t blocks = (total + 63) / 64;
     if (blocks > 65535) blocks = 65535;
     if (blocks < 1) return hipSuccess;
-    k_stack_reduce<T><<<dim3((unsigned)blocks), 256, 0, s>>>(a, spw, accumulate);
+    const int32_t acc = (mode & kReduceAccumulate) ? 1 : 0;
+    if ((mode & kReduceCombineF32) && T::kCols == 2)
+        k_stack_reduce<T, true><<<dim3((unsigned)blocks), 256, 0, s>>>(a, spw, acc);
+    else
+        k_stack_reduce<T, false><<<dim3((unsigned)blocks), 256, 0, s>>>(a, spw, acc);
     return hipGetLastError();
 }
 

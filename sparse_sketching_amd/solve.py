@@ -22,15 +22,19 @@ import torch
 from . import binding as b
 
 
-def sketch_pair(A, rhs, d, zeta, seed, precision="f16acc", row_offset=0):
+def sketch_pair(A, rhs, d, zeta, seed, precision="f16acc", row_offset=0, combine="f16"):
     """(SA, Sb) as float32 device tensors for the same S.  rhs is a length-m
     vector; it is sketched as the first column of an m x 2 matrix (the FP16
-    path works on column pairs)."""
+    path works on column pairs).  combine (FP16 only): "f16" adds the row
+    chunks' FP16 partials with FP16 additions (every addition in FP16, the
+    page's arithmetic), "f32" in FP32 with one final rounding
+    (SK_COMBINE_F32)."""
     m = A.shape[0]
     B2 = torch.zeros((m, 2), dtype=torch.float32, device=A.device)
     B2[:, 0] = rhs
-    SA = b.sketch_fused(A, d, zeta, seed, precision, row_offset=row_offset)
-    Sb = b.sketch_fused(B2, d, zeta, seed, precision, row_offset=row_offset)[:, 0]
+    flags = b.SK_COMBINE_F32 if (precision == "f16acc" and combine == "f32") else 0
+    SA = b.sketch_fused(A, d, zeta, seed, precision, row_offset=row_offset, flags=flags)
+    Sb = b.sketch_fused(B2, d, zeta, seed, precision, row_offset=row_offset, flags=flags)[:, 0]
     return SA.float(), Sb.float().contiguous()
 
 
@@ -59,10 +63,10 @@ def residual(A, x, rhs):
     return float(nr / nb) if float(nb) > 0 else float(nr)
 
 
-def sketch_and_solve(A, rhs, d, zeta, seed, precision="f16acc"):
+def sketch_and_solve(A, rhs, d, zeta, seed, precision="f16acc", combine="f16"):
     """The complete sketch-and-solve: shared-map sketches, FP32 QR solve,
     FP64 residual.  Returns (x, residual)."""
-    SA, Sb = sketch_pair(A, rhs, d, zeta, seed, precision)
+    SA, Sb = sketch_pair(A, rhs, d, zeta, seed, precision, combine=combine)
     x = solve_sketched(SA, Sb)
     return x, residual(A, x, rhs)
 

@@ -18,7 +18,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
     assert set(names) == {"sk_meta_generate", "sk_apply_f32", "sk_apply_f16acc",
-                          "sk_apply_workspace_size", "sk_lds_plan_describe",
+                          "sk_apply_f32_ws", "sk_apply_f16acc_ws", "sk_apply_workspace_size", "sk_lds_plan_describe",
                           "sk_sketch_f32", "sk_sketch_f16acc", "sk_sketch_workspace_size",
                           "sk_fused_plan_describe", "sk_apply_lowp", "sk_apply_blockperm",
                           "sk_apply_blockperm_ex", "sk_blockperm_workspace_size",
@@ -52,7 +52,8 @@ def test_meta_validation(lib, args, expect):
 A, RI, V, B = FAKE, FAKE + (1 << 34), FAKE + (1 << 35), FAKE + (1 << 36)
 
 
-@pytest.mark.parametrize("fn", ["sk_apply_f32", "sk_apply_f16acc"])
+@pytest.mark.parametrize("fn", ["sk_apply_f32", "sk_apply_f16acc", "sk_apply_f32_ws",
+                                "sk_apply_f16acc_ws"])
 @pytest.mark.parametrize("args,expect", [
     ((A, 100, 0, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_SHAPE),      # n < 1
     ((A, 100, 64, 32, RI, V, 4, B, 64, 64, 0), b.SK_ERR_SHAPE),     # lda < n
@@ -63,7 +64,7 @@ A, RI, V, B = FAKE, FAKE + (1 << 34), FAKE + (1 << 35), FAKE + (1 << 36)
     ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 6), b.SK_ERR_ARG),       # FLAT|LDS
     ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 10), b.SK_ERR_ARG),      # FLAT|REG
     ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 12), b.SK_ERR_ARG),      # LDS|REG
-    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 16), b.SK_ERR_ARG),      # unknown flag
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 32), b.SK_ERR_ARG),      # unknown flag
     ((None, 100, 64, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_NULL),
     ((A, 100, 64, 64, None, V, 4, B, 64, 64, 0), b.SK_ERR_NULL),
     ((A, 100, 64, 64, RI, None, 4, B, 64, 64, 0), b.SK_ERR_NULL),
@@ -72,13 +73,25 @@ A, RI, V, B = FAKE, FAKE + (1 << 34), FAKE + (1 << 35), FAKE + (1 << 36)
     ((A, 100, 64, 64, RI, V, 4, RI + 64, 64, 64, 0), b.SK_ERR_ARG),  # B inside metadata
 ])
 def test_apply_validation(lib, fn, args, expect):
-    assert getattr(lib, fn)(*args, None, 0, None) == expect
+    tail = (None, 0, None) if fn.endswith("_ws") else (None,)
+    assert getattr(lib, fn)(*args, *tail) == expect
+
+
+@pytest.mark.parametrize("fn,expect", [
+    ("sk_apply_f32", b.SK_ERR_ARG),         # FP32 output has no FP16 combine
+    ("sk_apply_f32_ws", b.SK_ERR_ARG),
+    ("sk_apply_f16acc", b.SK_ERR_ARG),      # no workspace: no reduce to combine in
+])
+def test_combine_flag_rules(lib, fn, expect):
+    args = (A, 100, 64, 64, RI, V, 4, B, 64, 64, b.SK_COMBINE_F32)
+    tail = (None, 0, None) if fn.endswith("_ws") else (None,)
+    assert getattr(lib, fn)(*args, *tail) == expect
 
 
 WS = FAKE + (1 << 37)
 
 
-@pytest.mark.parametrize("fn", ["sk_apply_f32", "sk_apply_f16acc"])
+@pytest.mark.parametrize("fn", ["sk_apply_f32_ws", "sk_apply_f16acc_ws"])
 @pytest.mark.parametrize("ws,nbytes,expect", [
     (WS + 2, 1 << 20, b.SK_ERR_ALIGN),            # workspace not 4-byte aligned
     (A + 64, 1 << 20, b.SK_ERR_ARG),              # workspace overlaps A
@@ -97,7 +110,8 @@ def test_workspace_validation(lib, fn, ws, nbytes, expect):
     ((0, 100, 64, 64, 3, 0), b.SK_ERR_SHAPE),      # d % zeta
     ((0, 100, 64, 64, 4, 6), b.SK_ERR_ARG),        # FLAT|LDS
     ((0, 100, 64, 64, 4, 12), b.SK_ERR_ARG),       # LDS|REG
-    ((0, 100, 64, 64, 4, 16), b.SK_ERR_ARG),       # unknown flag
+    ((0, 100, 64, 64, 4, 16), b.SK_ERR_ARG),       # FP16 combine on FP32
+    ((0, 100, 64, 64, 4, 32), b.SK_ERR_ARG),       # unknown flag
     ((0, 0, 64, 64, 4, 0), b.SK_OK),               # m = 0: no workspace
     ((1, 100, 64, 64, 4, 2), b.SK_OK),             # FLAT: no workspace
 ])
@@ -117,7 +131,8 @@ def test_workspace_size_validation(lib, args, expect):
     ((A + 4, 100, 64, 64, RI, V, 4, B, 64, 64, 0), b.SK_ERR_ALIGN), # A not 8-byte aligned
 ])
 def test_f16acc_pair_rules(lib, args, expect):
-    assert lib.sk_apply_f16acc(*args, None, 0, None) == expect
+    assert lib.sk_apply_f16acc(*args, None) == expect
+    assert lib.sk_apply_f16acc_ws(*args, None, 0, None) == expect
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -543,3 +558,49 @@ def test_lstsq_validation(lib):
     assert lib.sk_lstsq_workspace_size(d, n, ctypes.byref(out)) == b.SK_OK and out.value == nb
     assert lib.sk_lstsq_workspace_size(d, d + 1, ctypes.byref(out)) == b.SK_ERR_SHAPE
     assert lib.sk_lstsq_workspace_size(d, n, None) == b.SK_ERR_NULL
+
+
+# The four entry points of the sketching boundary, with their parameter
+# lists: (type, name) pairs.  The stream is a hipStream_t passed as void*
+# (the header includes no HIP header).
+BOUNDARY = {
+    "sk_meta_generate": [("uint64_t", "seed"), ("int64_t", "row_offset"), ("int64_t", "m"),
+                         ("int32_t", "d"), ("int32_t", "zeta"), ("int32_t *", "row_idx"),
+                         ("float *", "val"), ("void *", "stream")],
+    "sk_apply_f32": [("const float *", "A"), ("int64_t", "m"), ("int32_t", "n"),
+                     ("int64_t", "lda"), ("const int32_t *", "row_idx"), ("const float *", "val"),
+                     ("int32_t", "zeta"), ("float *", "B"), ("int32_t", "d"), ("int64_t", "ldb"),
+                     ("uint32_t", "flags"), ("void *", "stream")],
+    "sk_apply_f16acc": [("const float *", "A"), ("int64_t", "m"), ("int32_t", "n"),
+                        ("int64_t", "lda"), ("const int32_t *", "row_idx"),
+                        ("const float *", "val"), ("int32_t", "zeta"), ("uint16_t *", "B"),
+                        ("int32_t", "d"), ("int64_t", "ldb"), ("uint32_t", "flags"),
+                        ("void *", "stream")],
+    "sk_apply_blockperm": [("const float *", "A"), ("int64_t", "m"), ("int32_t", "n"),
+                           ("int64_t", "lda"), ("int32_t", "d"), ("int32_t", "M"),
+                           ("int32_t", "kappa"), ("int32_t", "s"), ("uint64_t", "seed"),
+                           ("float *", "Y"), ("int64_t", "ldy"), ("uint32_t", "flags"),
+                           ("void *", "stream")],
+}
+
+
+def _declaration(name):
+    import re
+    with open(b.HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    m = re.search(r"sk_status\s+" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    params = []
+    for p in m.group(1).split(","):
+        p = " ".join(p.split())
+        pm = re.match(r"(.*?)\s*(\w+)$", p)
+        params.append((pm.group(1).replace(" *", " *").strip(), pm.group(2)))
+    return params
+
+
+@pytest.mark.parametrize("name", sorted(BOUNDARY))
+def test_boundary_signatures(lib, name):
+    """The boundary calls take exactly their documented parameter lists
+    (no workspace), and the binding declares the same arity."""
+    assert _declaration(name) == BOUNDARY[name]
+    assert len(b._SIGNATURES[name][1]) == len(BOUNDARY[name])

@@ -193,7 +193,7 @@ def test_register_forced_errors():
     need = b.sk_apply_workspace_size(b.SK_PRECISION_F32, 4096, 128, d, zeta, b.SK_VARIANT_REG)
     ws2 = torch.empty(need + 64, dtype=torch.uint8, device=dev())
     with pytest.raises(b.SketchError) as e:
-        b.sk_apply_f32(A, 4096, 128, 128, ri40, v40, zeta, B, 40, 128, b.SK_VARIANT_REG, ws, 0)
+        b.sk_apply_f32_ws(A, 4096, 128, 128, ri40, v40, zeta, B, 40, 128, b.SK_VARIANT_REG, ws, 0)
     assert e.value.status == b.SK_ERR_UNSUPPORTED
     for Ax, Bx, w, nbytes, flags, expect in [
             (A2, B2, None, 0, b.SK_VARIANT_REG, b.SK_ERR_NULL),
@@ -201,14 +201,14 @@ def test_register_forced_errors():
             (A2, B2, ws2, need - 4, b.SK_VARIANT_REG, b.SK_ERR_ARG),
             (A2, B2, ws2, need, b.SK_VARIANT_REG | b.SK_VARIANT_LDS, b.SK_ERR_ARG)]:
         with pytest.raises(b.SketchError) as e:
-            b.sk_apply_f32(Ax, 4096, Ax.shape[1], Ax.shape[1], ri, v, zeta, Bx, d, Bx.shape[1],
-                           flags, w, nbytes)
+            b.sk_apply_f32_ws(Ax, 4096, Ax.shape[1], Ax.shape[1], ri, v, zeta, Bx, d,
+                              Bx.shape[1], flags, w, nbytes)
         assert e.value.status == expect
     # zeta = 16: a wavefront's 8 rows of a stage hold more than 64 entries
     ri16, v16 = b.meta(1, 4096, d, 16, device=dev())
     assert b.sk_apply_workspace_size(b.SK_PRECISION_F32, 4096, 128, d, 16, b.SK_VARIANT_REG) == 0
     with pytest.raises(b.SketchError) as e:
-        b.sk_apply_f32(A2, 4096, 128, 128, ri16, v16, 16, B2, d, 128, b.SK_VARIANT_REG, ws2, need)
+        b.sk_apply_f32_ws(A2, 4096, 128, 128, ri16, v16, 16, B2, d, 128, b.SK_VARIANT_REG, ws2, need)
     assert e.value.status == b.SK_ERR_UNSUPPORTED
 
 

@@ -63,7 +63,7 @@ def test_apply_in_graph(precision, flags, with_ws):
     dt = torch.float16 if precision == "f16acc" else torch.float32
     B = torch.empty((d, n), dtype=dt, device=dev())
     ws = b.workspace(A, d, zeta, precision, flags) if with_ws else None
-    fn = b.sk_apply_f16acc if precision == "f16acc" else b.sk_apply_f32
+    fn = b.sk_apply_f16acc_ws if precision == "f16acc" else b.sk_apply_f32_ws
     say(f"graph apply {precision} flags={flags} ws={with_ws}")
     replay_matches_eager(lambda: fn(A, m, n, n, ri, v, zeta, B, d, n, flags, ws, 0,
                                     torch.cuda.current_stream().cuda_stream), B)

@@ -153,14 +153,16 @@ def range_case():
     ri, v = oracle.meta_ref(seed, m, d, zeta)
     Ad = to_dev(A)
     rid, vd = b.meta(seed, m, d, zeta, device=dev())
-    return Ad, rid, vd, d, zeta, seed, oracle.sketch_f64(A, ri, v, d, zeta)
+    return Ad, A, ri, v, rid, vd, d, zeta, seed, oracle.sketch_f64(A, ri, v, d, zeta)
 
 
 def _measure(B, k, ref):
+    """(non-finite entries, relative Frobenius error after undoing 2^k,
+    entries that are zero although the exact sketch is not)."""
     x = as_f64(B) * 2.0 ** (-k)
     fin = np.isfinite(x)
     err = oracle.rel_frob(x, ref) if fin.all() else float("nan")
-    return int((~fin).sum()), err
+    return int((~fin).sum()), err, int(((x == 0) & (ref != 0)).sum())
 
 
 @pytest.mark.parametrize("k", [-24, -16, -8, 0, 8, 12])
@@ -168,26 +170,38 @@ def test_range_stress(range_case, k):
     """Common rescaling by 2^k (FP16 sketching page §V-E, Corollary 3):
     FP32 is unaffected; BF16 stays finite over the whole range; the FP16
     variants are finite while the sums fit FP16 and overflow (+-inf) when
-    they do not; at ordinary scale the two-level FP16 sketch is the most
-    accurate FP16 variant.  The range stress is a measurement, not a parity gate: the
-    bars here are properties, and the printed table is the result."""
-    Ad0, ri, v, d, zeta, seed, ref = range_case
+    they do not; at the bottom of the range RN conversion erases the
+    contributions of magnitude at most h/2 (the oracle counts them) and
+    output entries underflow to zero; at ordinary scale the two-level FP16
+    sketch is the most accurate FP16 variant.  The range stress is a
+    measurement, not a parity gate: the bars here are properties, and the
+    printed table is the result."""
+    Ad0, A, ri_h, v_h, ri, v, d, zeta, seed, ref = range_case
     Ad = Ad0 * (2.0**k)
     r32 = _measure(b.sketch_fused(Ad, d, zeta, seed, "f32"), k, ref)
     r16 = _measure(b.sketch_fused(Ad, d, zeta, seed, "f16acc"), k, ref)
+    r16c = _measure(b.sketch_fused(Ad, d, zeta, seed, "f16acc", flags=b.SK_COMBINE_F32), k, ref)
     rfl = _measure(b.apply_lowp(Ad, ri, v, zeta, d, "f16", "rn"), k, ref)
     rsr = _measure(b.apply_lowp(Ad, ri, v, zeta, d, "f16", "sr", sr_seed=1), k, ref)
     rbf = _measure(b.apply_lowp(Ad, ri, v, zeta, d, "bf16", "rn"), k, ref)
     sync()
-    say(f"  k={k:4d} fp32 {r32}  f16 rn two-level {r16}  f16 rn flat {rfl}  f16 sr flat {rsr}  "
-        f"bf16 rn flat {rbf}")
-    assert r32[0] == 0 and r32[1] <= 1e-5
-    assert rbf[0] == 0 and rbf[1] <= 0.2                # finite everywhere (§V-E)
+    Ak = (A * np.float32(2.0**k)).astype(np.float32)
+    erased, sub, total = oracle.f16_erasures(Ak, ri_h, v_h, d, zeta)
+    say(f"  k={k:4d} (non-finite, rel err, zero outputs)  fp32 {r32}  "
+        f"f16 rn two-level {r16}  f16 rn two-level fp32 combine {r16c}  f16 rn flat {rfl}  "
+        f"f16 sr flat {rsr}  bf16 rn flat {rbf}  | oracle: erased contributions "
+        f"{erased}/{total} ({erased / total:.3e}), subnormal {sub}")
+    assert r32[0] == 0 and r32[1] <= 1e-5 and r32[2] == 0
+    assert rbf[0] == 0 and rbf[1] <= 0.2 and rbf[2] == 0    # finite everywhere (§V-E)
     fits = np.abs(ref).max() * 2.0**k < 32768           # every exact sum far inside FP16
     past = int((np.abs(ref) * 2.0**k > 2 * 65520).sum())  # sums far past the FP16 range
-    for nonfin, err in (r16, rfl, rsr):
+    for nonfin, err, _ in (r16, r16c, rfl, rsr):
         if fits:
             assert nonfin == 0
         assert nonfin >= past
     if fits:
-        assert r16[1] < rfl[1] and r16[1] < 2e-2
+        assert r16[1] < rfl[1] and r16[1] < 2e-2 and r16c[1] <= r16[1]
+    # erasure grows toward the bottom of the range (the smallest lognormal
+    # row scales already lose a few hundred contributions at k = 0)
+    if k <= -16:
+        assert erased > 0.01 * total

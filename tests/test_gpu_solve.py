@@ -5,10 +5,15 @@ page App. F.1).
 The oracle forms its own fp64 sketch from its own metadata and solves it;
 the GPU pipeline sketches with the fused kernels and solves with FP32 QR.
 Bars: FP32-sketch residuals within 1e-4 (relative) of the oracle's; FP16
-residuals within 1% of the FP32 ones at d = 2n on the low-coherence system
-(the page reports median paired increases below 0.4%) and within 50% on
-the coherent one, whose 1e3-scaled head rows make FP16 rounding of the
-head entries comparable to the tail's contributions (measured: +32%);
+residuals (every addition in FP16, the page's arithmetic) between the FP32
+residual and the one of the oracle's RN emulation of the page's flat
+(single running sum) order, and close to the oracle's two-level emulation;
+with the FP32 combine of the FP16 chunk partials (SK_COMBINE_F32) within 1%
+of the FP32 residual.  The FP16 residual increase is the FP16 accumulation
+of b's sketch itself: the noise (0.1) is small next to ||Ax0||, so the
+accumulation error of Sb is large next to the residual (the oracle's flat
+emulation gives +18% on the low-coherence system and +131% on the coherent
+one, whose 1e3-scaled head rows dominate the entries they land in);
 metric functions equal to the oracle's on the same arrays."""
 import numpy as np
 import pytest
@@ -38,6 +43,18 @@ def oracle_residual(A, rhs, d, zeta, seed):
     return oracle.residual(A, x, rhs), x
 
 
+def oracle_f16_residual(A, rhs, d, zeta, seed, chunk_rows):
+    """Residual of the solve on the oracle's RN-emulated FP16 sketches of A
+    and [b 0] (FP32 QR), for the flat order (chunk_rows=None) or row chunks
+    combined with FP16 additions."""
+    ri, v = oracle.meta_ref(seed, A.shape[0], d, zeta)
+    B2 = np.zeros((A.shape[0], 2), dtype=np.float32)
+    B2[:, 0] = rhs
+    SA = oracle.sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=chunk_rows).astype(np.float64)
+    Sb = oracle.sketch_f16_rn_emul(B2, ri, v, d, zeta, chunk_rows=chunk_rows)[:, 0]
+    return oracle.residual(A, oracle.sketch_solve(SA, Sb.astype(np.float64)), rhs)
+
+
 @pytest.mark.parametrize("coherent", [False, True])
 def test_sketch_and_solve_matches_oracle(coherent):
     m, n, zeta, seed = 1 << 16, 128, 4, 7
@@ -46,14 +63,24 @@ def test_sketch_and_solve_matches_oracle(coherent):
     Ad, bd = to_dev(A), to_dev(rhs)
     x32, r32 = solve.sketch_and_solve(Ad, bd, d, zeta, seed, "f32")
     x16, r16 = solve.sketch_and_solve(Ad, bd, d, zeta, seed, "f16acc")
+    x16c, r16c = solve.sketch_and_solve(Ad, bd, d, zeta, seed, "f16acc", combine="f32")
     sync()
     r_ref, _ = oracle_residual(A, rhs, d, zeta, seed)
     r_opt = oracle.residual(A, oracle.reference_solution(A, rhs), rhs)
-    say(f"  coherent={coherent}: residual fp32 {r32:.6f} fp16 {r16:.6f} oracle {r_ref:.6f} "
-        f"unsketched {r_opt:.6f}")
+    r_flat = oracle_f16_residual(A, rhs, d, zeta, seed, None)
+    # the fused kernel's chunks at this size are 128 rows (512 workgroups)
+    r_two = oracle_f16_residual(A, rhs, d, zeta, seed, 128)
+    say(f"  coherent={coherent}: residual fp32 {r32:.6f} fp16 {r16:.6f} "
+        f"fp16+fp32-combine {r16c:.6f} oracle fp64 {r_ref:.6f} oracle fp16 flat {r_flat:.6f} "
+        f"oracle fp16 two-level {r_two:.6f} unsketched {r_opt:.6f}")
     assert abs(r32 - r_ref) <= 1e-4 * r_ref
-    assert abs(r16 - r32) <= (0.5 if coherent else 1e-2) * r32
     assert r32 >= r_opt * (1 - 1e-6)
+    assert abs(r16c - r32) <= 1e-2 * r32
+    # FP16 accumulation costs residual as the oracle's emulation predicts:
+    # no worse than the page's flat order, and an increase of the size the
+    # same-size two-level emulation shows
+    assert r_ref * (1 - 1e-2) <= r16 <= r_flat * (1 + 1e-2)
+    assert abs(r16 / r_ref - r_two / r_ref) <= 0.5 * (r_two / r_ref - 1) + 1e-2
 
 
 def test_consistent_system_recovered():
@@ -95,10 +122,11 @@ def test_metrics_equal_oracle_on_same_arrays():
 def test_sparsestack_beats_countsketch_on_coherent_system():
     """Spreading each row over zeta targets helps coherent inputs (§V-C,
     §V-D): at d/n = 8 the zeta = 4 sketch-and-solve residual is no worse
-    than CountSketch's in FP32.  In FP16, at noise 1e-3, both residuals sit
-    on the FP16 rounding floor of the sketched right-hand side (about ten
-    times the FP32 residuals here), where the zeta effect is below the
-    floor's seed-to-seed spread: they must stay within 10% of each other."""
+    than CountSketch's in FP32.  In FP16 (FP16 row-chunk sums combined in
+    FP32), at noise 1e-3, both residuals sit on the FP16 rounding floor of
+    the sketched right-hand side (about ten times the FP32 residuals here),
+    where the zeta effect is below the floor's seed-to-seed spread: they
+    must stay within 10% of each other."""
     m, n = 1 << 16, 64
     d = 8 * n
     A, rhs = system(m, n, 4, coherent=True, noise=1e-3)
@@ -106,7 +134,8 @@ def test_sparsestack_beats_countsketch_on_coherent_system():
     res = {}
     for zeta in (1, 4):
         for prec in ("f32", "f16acc"):
-            res[(zeta, prec)] = min(solve.sketch_and_solve(Ad, bd, d, zeta, s, prec)[1]
+            res[(zeta, prec)] = min(solve.sketch_and_solve(Ad, bd, d, zeta, s, prec,
+                                                           combine="f32")[1]
                                     for s in (1, 2, 3))
     sync()
     say(f"  coherent d/n=8 residuals {res}")

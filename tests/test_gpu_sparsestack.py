@@ -304,21 +304,46 @@ def test_scale_f16acc_flat_error_model(scale_case):
 
 # ---------------------------------------- distortion at d = 2n (coherence)
 
+_DISTORTION = {}
+
+
+def _distortion_case(m, zeta):
+    """U = orth(coherent m x 128) on the device, its metadata and the RN
+    emulation oracle's E_OSE (computed once per shape)."""
+    key = (m, zeta)
+    if key not in _DISTORTION:
+        n = 128
+        d = 2 * n
+        Ud = inputs.orth_torch(inputs.coherent_torch(m, n, seed=0))
+        U = Ud.cpu().numpy()
+        ri, v = oracle.meta_ref(5, m, d, zeta)
+        emu = oracle.sketch_f16_rn_emul(U, ri, v, d, zeta, chunk_rows=4096)
+        _DISTORTION.clear()
+        _DISTORTION[key] = (Ud, oracle.ose_error(emu.astype(np.float64)))
+    return _DISTORTION[key]
+
+
+@pytest.mark.parametrize("path", ["lds", "reg", "fused"])
 @pytest.mark.parametrize("m,zeta", [(1 << 20, 4), (1 << 18, 1), (1 << 18, 8)])
-def test_distortion_matches_rn_emulation(m, zeta):
+def test_distortion_matches_rn_emulation(m, zeta, path):
     """U = orth(A) of the coherent workload (n = 128), d = 2n: the GPU FP16
     sketch's E_OSE = ||(SU)^T SU - I||_2 is within 1e-2 of the RN-emulation
-    oracle's, and its sigma_min/sigma_max stays close to FP32's."""
+    oracle's, and its sigma_min/sigma_max stays close to FP32's, on the LDS
+    and register applies and the fused sketch (the benchmarked path)."""
     n = 128
     d = 2 * n
-    say(f"distortion m={m} zeta={zeta}")
-    Ud = inputs.orth_torch(inputs.coherent_torch(m, n, seed=0))
-    U = Ud.cpu().numpy()
-    B16, _, _ = run(Ud, d, zeta, 5, "f16acc")
-    B32, _, _ = run(Ud, d, zeta, 5, "f32")
-    ri, v = oracle.meta_ref(5, m, d, zeta)
-    emu = oracle.sketch_f16_rn_emul(U, ri, v, d, zeta, chunk_rows=4096)
-    e_gpu, e_emu = oracle.ose_error(B16), oracle.ose_error(emu.astype(np.float64))
+    say(f"distortion m={m} zeta={zeta} {path}")
+    Ud, e_emu = _distortion_case(m, zeta)
+    if path == "fused":
+        B16 = b.sketch_fused(Ud, d, zeta, 5, "f16acc")
+        B32 = b.sketch_fused(Ud, d, zeta, 5, "f32")
+        sync()
+        B16 = B16.cpu().numpy().astype(np.float64)
+        B32 = B32.cpu().numpy().astype(np.float64)
+    else:
+        B16, _, _ = run(Ud, d, zeta, 5, "f16acc", path)
+        B32, _, _ = run(Ud, d, zeta, 5, "f32", path)
+    e_gpu = oracle.ose_error(B16)
     say(f"  E_OSE gpu16 {e_gpu:.5f} emu16 {e_emu:.5f} gpu32 {oracle.ose_error(B32):.5f}")
     assert abs(e_gpu - e_emu) <= 1e-2
     assert abs(oracle.sv_ratio(B16) - oracle.sv_ratio(B32)) <= 1e-2

@@ -9,7 +9,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import meta_ref, rn_f16_add, scale_f32, sketch_f16_rn_emul, sketch_f64
+from oracle import (dense_S, f16_erasures, f16_zero_subnormal_counts, meta_ref, rn_f16_add, scale_f32, sketch_f16_rn_emul,
+                    sketch_f64, sketch_lowp_emul, sketch_matrix)
 from sparse_sketching_amd import inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fp16_rn_values.txt")
@@ -175,3 +176,150 @@ def test_fp16_flat_vs_fp64_error_model():
 
 def test_scale_is_exact_at_zeta4():
     assert scale_f32(4) == np.float32(0.5) and scale_f32(1) == np.float32(1.0)
+
+
+def _scalar_two_level(A, ri, v, d, zeta, chunk_rows, B0=None):
+    """Plain loop with exact rational rounding: each chunk of rows summed in
+    ascending (i, t) order from +0 into its own partial, the partials then
+    added in chunk order, every addition rounded to binary16."""
+    m, n = A.shape
+    B = [[0.0] * n for _ in range(d)] if B0 is None else [list(map(float, r)) for r in B0]
+    for r0 in range(0, m, chunk_rows):
+        P = [[0.0] * n for _ in range(d)]
+        for e in range(r0 * zeta, min(m, r0 + chunk_rows) * zeta):
+            i = e // zeta
+            for j in range(n):
+                q = float(np.float32(A[i, j]) * np.float32(v[e]))
+                c = rn_binary16_exact(Fraction(q))
+                P[ri[e]][j] = rn_binary16_exact(Fraction(P[ri[e]][j]) + Fraction(c))
+        for r in range(d):
+            for j in range(n):
+                B[r][j] = rn_binary16_exact(Fraction(B[r][j]) + Fraction(P[r][j]))
+    return np.array(B)
+
+
+@pytest.mark.parametrize("chunk_rows", [1, 7, 32, 200])
+def test_two_level_matches_scalar_loop(chunk_rows):
+    """The chunked (two-level) FP16 order equals a plain loop with exact
+    rounding, also when it starts from an existing sketch B0."""
+    m, n, d, zeta = 160, 3, 8, 2
+    A = (inputs.gaussian(m, n, seed=5) * np.float32(91.0)).astype(np.float32)
+    ri, v = meta_ref(4, m, d, zeta)
+    got = sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=chunk_rows)
+    assert np.array_equal(got.astype(np.float64), _scalar_two_level(A, ri, v, d, zeta, chunk_rows))
+    B0 = (inputs.gaussian(d, n, seed=6) * np.float32(300.0)).astype(np.float16)
+    got0 = sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=chunk_rows, B0=B0)
+    assert np.array_equal(got0.astype(np.float64),
+                          _scalar_two_level(A, ri, v, d, zeta, chunk_rows, B0=B0))
+
+
+def test_combine_f32_overflow_between_chunks():
+    """Partials 60000, 30000, -50000 on one entry: FP16 additions overflow
+    after the second partial (90000 > 65504) and stay infinite; an FP32
+    combine rounds the finite total 40000 (exact in binary16) once."""
+    d, zeta = 1, 1
+    ri, v = meta_ref(1, 3, d, zeta)
+    want = np.array([60000.0, 30000.0, -50000.0])
+    A = (want / v.astype(np.float64)).astype(np.float32)[:, None]
+    f16 = sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=1, combine="f16")
+    f32 = sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=1, combine="f32")
+    assert np.isinf(f16[0, 0]) and f16[0, 0] > 0
+    assert float(f32[0, 0]) == 40000.0
+    # one chunk: nothing to combine, both equal the flat order
+    flat = sketch_f16_rn_emul(A, ri, v, d, zeta)
+    for c in ("f16", "f32"):
+        assert np.array_equal(sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=3, combine=c), flat)
+
+
+def test_combine_f32_rounds_the_exact_sum_once():
+    """One-row chunks: each partial is RN_f16(k 2^-10), a multiple of 2^-10
+    below 2^4, so 64 of them add exactly in FP32 and the FP32 combine is the
+    exactly rounded binary16 of the partials' sum."""
+    m, n, d, zeta = 64, 4, 4, 1
+    g = np.random.default_rng(3)
+    ri, v = meta_ref(2, m, d, zeta)
+    k = g.integers(-2**14, 2**14, size=(m, n))
+    A = (k * 2.0**-10 / v.astype(np.float64)[:, None]).astype(np.float32)   # q = k 2^-10
+    got = sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=1, combine="f32")
+    for r in range(d):
+        for j in range(n):
+            parts = [Fraction(rn_binary16_exact(Fraction(int(k[i, j]), 2**10)))
+                     for i in range(m) if ri[i] == r]
+            assert float(got[r, j]) == rn_binary16_exact(sum(parts, Fraction(0)))
+
+
+def test_out_of_block_entries_contribute_nothing():
+    """Every oracle function applies the same rule: entry i*zeta + t counts
+    only if its row lies in block t.  Planting rows outside [0, d) or in
+    another block gives the sketch of the metadata with those entries'
+    values set to zero."""
+    m, n, d, zeta = 300, 4, 16, 4
+    A = inputs.gaussian(m, n, seed=2)
+    ri, v = meta_ref(5, m, d, zeta)
+    bad = ri.copy()
+    g = np.random.default_rng(0)
+    sel = g.choice(m * zeta, size=60, replace=False)
+    t = sel % zeta
+    bad[sel[:20]] = ((t[:20] + 1) % zeta) * (d // zeta)        # another block
+    bad[sel[20:40]] = d + 3                                       # past the end
+    bad[sel[40:]] = -1                                            # negative
+    zeroed = v.copy()
+    zeroed[sel] = 0.0
+    assert np.array_equal(sketch_f64(A, bad, v, d, zeta), sketch_f64(A, ri, zeroed, d, zeta))
+    assert np.array_equal(dense_S(bad, v, m, d, zeta), dense_S(ri, zeroed, m, d, zeta))
+    assert np.array_equal(sketch_matrix(bad, v, m, d, zeta).toarray(),
+                          sketch_matrix(ri, zeroed, m, d, zeta).toarray())
+    for ch in (None, 64):
+        assert np.array_equal(sketch_f16_rn_emul(A, bad, v, d, zeta, chunk_rows=ch),
+                              sketch_f16_rn_emul(A, ri, zeroed, d, zeta, chunk_rows=ch))
+    for fmt, conv in (("f16", "rn"), ("f16", "sr"), ("bf16", "rn")):
+        assert np.array_equal(sketch_lowp_emul(A, bad, v, d, zeta, fmt, conv, sr_seed=3),
+                              sketch_lowp_emul(A, ri, zeroed, d, zeta, fmt, conv, sr_seed=3))
+
+
+def test_f16_erasures_closed_form():
+    """Coordinate-like input whose entries are placed around h/2 = 2^-25
+    after the 1/2 scale (FP16 page §V-E: RN erases contributions below h/2,
+    the tie at h/2 included): the counts follow from each entry's value."""
+    m, n, d, zeta = 64, 8, 16, 4
+    row = np.array([2.0**-24,                 # q = h/2: a tie, rounds to 0
+                    2.0**-24 * (1 + 2.0**-20),  # just above h/2: rounds to h
+                    2.0**-30,                 # far below: 0
+                    -(2.0**-25),              # q = -h/4: -0
+                    1.0,                      # normal
+                    0.0,                      # zero: not a contribution
+                    2.0**-13,                 # q = 2^-14, the smallest normal
+                    3 * 2.0**-15],            # q = 1.5 * 2^-15: subnormal
+                   dtype=np.float32)
+    A = np.tile(row, (m, 1)).astype(np.float32)
+    ri, v = meta_ref(3, m, d, zeta)
+    erased, sub, total = f16_erasures(A, ri, v, d, zeta)
+    per_row = m * zeta
+    assert total == 7 * per_row
+    assert erased == 3 * per_row
+    assert sub == 2 * per_row
+    # the entry-by-entry count, with one entry's value of magnitude 3/4:
+    # its products of 2^-24 (3h/4 -> h) and 3 * 2^-15 (1.125 * 2^-14,
+    # normal) move, so one erasure less and one subnormal in, one out
+    v2 = v.copy()
+    v2[1] = np.float32(np.sign(v[1]) * 0.75)
+    assert f16_erasures(A, ri, v2, d, zeta) == (erased - 1, sub, total)
+
+
+def test_zero_subnormal_thresholds_match_the_conversion():
+    """The threshold classification of f16_zero_subnormal_counts equals the
+    nearest-even cast itself on values around h/2 and 2^-14 - h/2 (every
+    FP32 value in a window around each threshold) and on random magnitudes
+    across the subnormal range."""
+    def by_cast(q):
+        c = q.astype(np.float16).astype(np.float64)
+        nz = q != 0
+        return int((nz & (c == 0)).sum()), int(((c > 0) & (c < 2.0**-14)).sum()), int(nz.sum())
+    for t in (2.0**-25, 2.0**-14 - 2.0**-25):
+        bits = np.float32(t).view(np.uint32)
+        q = (np.arange(-4096, 4097, dtype=np.int64) + int(bits)).astype(np.uint32).view(np.float32)
+        assert f16_zero_subnormal_counts(q) == by_cast(q)
+    g = np.random.default_rng(1)
+    q = (2.0 ** g.uniform(-30, -12, 200000)).astype(np.float32)
+    q[::7] = 0
+    assert f16_zero_subnormal_counts(q) == by_cast(q)
