@@ -173,7 +173,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-sample-rows", type=int, default=M_ROWS)
-    ap.add_argument("--cpu-emul-rows", type=int, default=1 << 16)
+    ap.add_argument("--cpu-emul-rows", type=int, default=M_ROWS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-blockperm", action="store_true")
     ap.add_argument("--no-coherence", action="store_true")
