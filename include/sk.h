@@ -336,6 +336,33 @@ sk_status sk_sketch_f16acc(uint64_t seed, int64_t row_offset, const float *A, in
                            void *stream);
 
 /*
+ * sk_sketch_f16acc_noalloc: sk_sketch_f16acc for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): no workspace argument, and the
+ * call allocates nothing.  The fused kernel's partials go to a static
+ * device scratch of 128 MiB that the library holds on every device it runs
+ * on until the process ends; its device address is taken once per device,
+ * on that device's first call.  Same sketch, arguments, flags and order of
+ * additions as sk_sketch_f16acc.
+ *   Only shapes the fused kernel covers run here (zeta <= 16, d % 16 == 0,
+ *   the FP16 alignment rules of sk_sketch_f16acc, a plan whose partials fit
+ *   the 128 MiB: every plan on a 256-CU device up to d = 2048 at 8192 FP16
+ *   columns); any other shape returns SK_ERR_UNSUPPORTED and enqueues
+ *   nothing.
+ *   Every call on a device shares that device's scratch, and each call
+ *   leaves its partials there: calls that overlap in time on one device
+ *   (other streams, other host threads) race and give undefined results;
+ *   order them on one stream.  The scratch needs no clearing: every word a
+ *   call's reduce reads is first written by the same call.
+ * Errors: as sk_sketch_f16acc (no workspace errors), plus
+ * SK_ERR_UNSUPPORTED as above and SK_ERR_HIP when the scratch's device
+ * address cannot be obtained.
+ */
+sk_status sk_sketch_f16acc_noalloc(uint64_t seed, int64_t row_offset, const float *A, int64_t m,
+                                   int32_t n, int64_t lda, int32_t d, int32_t zeta,
+                                   uint16_t *B, int64_t ldb, uint32_t flags, void *stream);
+
+/*
  * sk_sketch_workspace_size: workspace bytes an sk_sketch_f32 (precision
  * SK_PRECISION_F32) or sk_sketch_f16acc (SK_PRECISION_F16ACC) call with
  * these sizes needs on the current device, whatever its lda and A's

@@ -70,6 +70,9 @@ _SIGNATURES = {
     "sk_sketch_f16acc": (_c.c_int, [_c.c_uint64, _c.c_int64, _c.c_void_p, _c.c_int64, _c.c_int32,
                                     _c.c_int64, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_int64,
                                     _c.c_uint32, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "sk_sketch_f16acc_noalloc": (_c.c_int, [_c.c_uint64, _c.c_int64, _c.c_void_p, _c.c_int64,
+                                            _c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32,
+                                            _c.c_void_p, _c.c_int64, _c.c_uint32, _c.c_void_p]),
     "sk_sketch_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32,
                                             _c.c_int32, _c.POINTER(_c.c_size_t)]),
     "sk_fused_plan_describe": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int64,
@@ -318,6 +321,12 @@ def sk_sketch_f16acc(seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags=0, w
     _check("sk_sketch_f16acc", load().sk_sketch_f16acc(
         seed, row_offset, _ptr(A), m, n, lda, d, zeta, _ptr(B), ldb, flags, _ptr(workspace),
         _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def sk_sketch_f16acc_noalloc(seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags=0,
+                             stream=None):
+    _check("sk_sketch_f16acc_noalloc", load().sk_sketch_f16acc_noalloc(
+        seed, row_offset, _ptr(A), m, n, lda, d, zeta, _ptr(B), ldb, flags, _stream(stream)))
 
 
 def sk_sketch_workspace_size(precision, m, n, d, zeta):

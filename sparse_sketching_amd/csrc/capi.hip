@@ -5,10 +5,21 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "sk.h"
 #include "sk_internal.hpp"
 #include "sk_rng.hpp"
+
+// The allocation-free sketch's scratch (sk_sketch_f16acc_noalloc): the
+// fused kernel's partials live in this file-scope device array, of which
+// each device holds its own copy while the library stays loaded.  Host code
+// never passes `scratch` itself to a kernel (on the host the name stands for
+// a host-side shadow, not a device address): it passes the device address
+// hipGetSymbolAddress returns, taken once per device on that device's first
+// call.
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) uint32_t scratch[kStaticScratchBytes / 4];
 
 namespace sk {
 
@@ -289,10 +300,33 @@ size_t sketch_ws_bytes(const sk::DevInfo &di, bool f16, int64_t m, int32_t n, in
     return fused > need ? fused : need;
 }
 
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+uint32_t *scratch_dev[kMaxScratchDevices];     // guarded by scratch_mu
+
+// The device address of `scratch` on the current device.
+sk_status static_scratch(uint32_t **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SK_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return SK_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_dev[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) return SK_ERR_HIP;
+        scratch_dev[dev] = static_cast<uint32_t *>(p);
+    }
+    *out = scratch_dev[dev];
+    return SK_OK;
+}
+
+// use_static: the partials go to the device's static scratch (no
+// workspace argument; only shapes the fused kernel covers within
+// kStaticScratchBytes).
 sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const float *A, int64_t m,
                           int32_t n, int64_t lda, int32_t d, int32_t zeta, void *B,
                           int64_t ldb, uint32_t flags, void *workspace, size_t workspace_bytes,
-                          hipStream_t s) {
+                          hipStream_t s, bool use_static = false) {
     const size_t belem = f16 ? 2 : 4;
     if (m < 0 || row_offset < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0)
         return SK_ERR_SHAPE;
@@ -307,14 +341,16 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
     const int mode = (accumulate ? sk::kReduceModeAccumulate : 0) |
                      ((flags & SK_COMBINE_F32) ? sk::kReduceModeCombineF32 : 0);
     if (m > 0) {
-        if (A == nullptr || workspace == nullptr) return SK_ERR_NULL;
+        if (A == nullptr || (!use_static && workspace == nullptr)) return SK_ERR_NULL;
         if (f16 && (lda % 2 != 0 || (uintptr_t)A % 8 != 0)) return SK_ERR_ALIGN;
-        if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
         const size_t aspan = span_bytes(m, n, lda, 4);
         if (overlaps(A, aspan, B, bspan)) return SK_ERR_ARG;
-        if (overlaps(workspace, workspace_bytes, A, aspan) ||
-            overlaps(workspace, workspace_bytes, B, bspan))
-            return SK_ERR_ARG;
+        if (!use_static) {
+            if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
+            if (overlaps(workspace, workspace_bytes, A, aspan) ||
+                overlaps(workspace, workspace_bytes, B, bspan))
+                return SK_ERR_ARG;
+        }
     }
     sk::DevInfo di;
     if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
@@ -325,9 +361,19 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
                 : sk::launch_zero_words(static_cast<uint32_t *>(B), d, n, ldb, s);
         return hip_status(e);
     }
-    if (workspace_bytes < sketch_ws_bytes(di, f16, m, n, d, zeta)) return SK_ERR_ARG;
     const float scale = scale_of(zeta);
     sk::FusedPlan fp{};
+    if (use_static) {
+        if (!sk::plan_fused(di, f16, m, n, lda, base_align(A), d, zeta, &fp) ||
+            fp.ws_bytes > kStaticScratchBytes)
+            return SK_ERR_UNSUPPORTED;
+        uint32_t *ws = nullptr;
+        const sk_status st = static_scratch(&ws);
+        if (st != SK_OK) return st;
+        return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, nullptr,
+                                           nullptr, d, zeta, scale, B, ldb, ws, mode, s));
+    }
+    if (workspace_bytes < sketch_ws_bytes(di, f16, m, n, d, zeta)) return SK_ERR_ARG;
     if (sk::plan_fused(di, f16, m, n, lda, base_align(A), d, zeta, &fp))
         return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, nullptr,
                                            nullptr, d, zeta, scale, B, ldb,
@@ -655,6 +701,13 @@ sk_status sk_sketch_f16acc(uint64_t seed, int64_t row_offset, const float *A, in
                            void *stream) {
     return sketch_dispatch(true, seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags, workspace,
                            workspace_bytes, (hipStream_t)stream);
+}
+
+sk_status sk_sketch_f16acc_noalloc(uint64_t seed, int64_t row_offset, const float *A, int64_t m,
+                                   int32_t n, int64_t lda, int32_t d, int32_t zeta, uint16_t *B,
+                                   int64_t ldb, uint32_t flags, void *stream) {
+    return sketch_dispatch(true, seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags, nullptr,
+                           0, (hipStream_t)stream, true);
 }
 
 sk_status sk_sketch_workspace_size(int32_t precision, int64_t m, int32_t n, int32_t d,

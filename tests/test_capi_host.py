@@ -20,6 +20,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"sk_meta_generate", "sk_apply_f32", "sk_apply_f16acc",
                           "sk_apply_f32_ws", "sk_apply_f16acc_ws", "sk_apply_workspace_size", "sk_lds_plan_describe",
                           "sk_sketch_f32", "sk_sketch_f16acc", "sk_sketch_workspace_size",
+                          "sk_sketch_f16acc_noalloc",
                           "sk_fused_plan_describe", "sk_apply_lowp", "sk_apply_blockperm",
                           "sk_apply_blockperm_ex", "sk_blockperm_workspace_size",
                           "sk_blockperm_plan_describe", "sk_lstsq_qr_f32",
