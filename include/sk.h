@@ -72,7 +72,7 @@ typedef enum sk_status {
 #define SK_WIRING_AFFINE 1
 
 /* BlockPerm kernels, as sk_blockperm_plan_describe reports them */
-#define SK_BLOCKPERM_KERNEL_COMPONENT 0  /* LDS tiles per component, no workspace */
+#define SK_BLOCKPERM_KERNEL_COMPONENT 0  /* per component and column tile, no workspace */
 #define SK_BLOCKPERM_KERNEL_SLICE     1  /* LDS tiles per (input block, row slice) */
 #define SK_BLOCKPERM_KERNEL_REGISTER  2  /* partial rows in registers */
 
@@ -400,27 +400,41 @@ sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_
  * blocks of N(g), a union of kappa edge-disjoint permutations; inside a
  * wired block pair each input row goes to s hashed output rows with
  * Rademacher signs; each block is scaled so each nonzero is
- * +-1/sqrt(kappa*s).  §5: S is never stored; wiring and hashes are made on
- * the fly, accumulation is private to a workgroup in LDS, each output tile is
- * written once and there are no global atomics.)
+ * +-1/sqrt(kappa*s).  §5.1, §5.2: S is never stored; wiring and hashes are
+ * made on the fly, accumulation is private to a workgroup, each output tile
+ * is written once and there are no global atomics.)
  *
  * Wiring: pi_j(g) = (sigma(g) + j*M/kappa) mod M, j = 0..kappa-1, with sigma
  * the Fisher-Yates permutation of [M] whose swap partner for k = M-1..1 is
  * floor(w0*(k+1)/2^32), w0 the first word of Philox-4x32-10 of counter
- * (k, 0, 0, 2) and key (seed lo, seed hi).
+ * (k, 0, 0, 2) and key (seed lo, seed hi).  The block graph is then M/kappa
+ * disjoint complete bipartite components of kappa output and kappa input
+ * blocks.
  * Hash: with fmix32 the MurmurHash3 32-bit finalizer and
  * c(H, x) = fmix32(H ^ x) + 0x9E3779B9, the block key is
  * K(g,h) = c(c(c(c(0x9E3779B9, seed lo), seed hi), g), h); input row r of
- * block h (0 <= r < B_c) goes to output row g*B_r + floor(v*B_r/2^32) of
- * output block g with sign (v & 1 ? -1 : +1), v = fmix32(K(g,h) ^ r).
+ * block h (0 <= r < B_c) has v = fmix32(K(g,h) ^ r) and
+ * beta = floor(v*B_r/2^32); for s > 1, w = fmix32(v + 0x9E3779B9) and
+ * alpha = 2*floor(w*(B_r/2)/2^32) + 1.  It goes to the s output rows
+ * g*B_r + (beta + i*alpha) mod B_r, i < s (s = 1: beta), with sign
+ * negative when bit i of v is set.
  *
- *   A      device float, m x n, lda >= n.  Y device float, d x n, ldy >= n.
+ * One workgroup per (component, 32-column tile, group of 64 of the
+ * component's kappa*B_r output rows) streams the component's input rows of
+ * its tile, keeps its output rows in registers and writes them once: A is
+ * read once when kappa*B_r <= 64 (ceil(kappa*B_r/64) times otherwise).
+ * No workspace, no atomics, a fixed order of additions (reproducible).
+ *
+ *   A      device float, m x n, lda >= n (any alignment; 16-byte aligned A
+ *          with n and lda multiples of 4 takes 16-byte loads).
+ *   Y      device float, d x n, ldy >= n.
  *   M      blocks (1..1024), m % M == 0, d % M == 0, kappa | M.
- *   s      nonzeros per column inside a block; only s = 1 is built
- *          (SK_ERR_UNSUPPORTED otherwise).
+ *   s      1 <= s <= B_r; s > 1 needs B_r a power of two (the odd stride
+ *          alpha then gives s distinct rows).
  *   flags  SK_ACCUMULATE only.
- * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_UNSUPPORTED (s != 1, or a
- * kappa*B_r tile too large for LDS), SK_ERR_ARG (other flags, aliasing).
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE (sizes, kappa not dividing M, s > B_r),
+ * SK_ERR_UNSUPPORTED (M > 1024; s > 1 with B_r not a power of two),
+ * SK_ERR_ARG (other flags, aliasing), SK_ERR_HIP.
  */
 sk_status sk_apply_blockperm(const float *A, int64_t m, int32_t n, int64_t lda,
                              int32_t d, int32_t M, int32_t kappa, int32_t s,
@@ -457,9 +471,10 @@ sk_status sk_apply_blockperm(const float *A, int64_t m, int32_t n, int64_t lda,
  *           lda % 4 == 0, A is 16-byte aligned and kappa*B_r is 16 R G for
  *           some R in {1, 2, 4, 8, 16} dividing B_r and G <= 8; otherwise in
  *           LDS tiles of 32 columns (SK_BLOCKPERM_KERNEL_SLICE, kappa*B_r up
- *           to what one wavefront tile of LDS holds).  NULL is accepted where
- *           sk_apply_blockperm's component kernel applies (shift wiring,
- *           s = 1, kappa in {1, 2, 4, 8}): that kernel then runs.
+ *           to what one wavefront tile of LDS holds).  NULL is accepted for
+ *           the shift wiring: sk_apply_blockperm's component kernel then
+ *           runs (it also runs with a workspace where neither kernel above
+ *           fills the device better).
  *   flags   SK_ACCUMULATE only.
  * Errors: as sk_apply_blockperm, plus SK_ERR_ARG (unknown wiring, small
  * workspace), SK_ERR_NULL (missing workspace), SK_ERR_ALIGN (workspace not
@@ -486,8 +501,9 @@ sk_status sk_blockperm_workspace_size(int64_t m, int32_t n, int32_t d, int32_t M
  * out int64[SK_BLOCKPERM_PLAN_FIELDS] = {kernel (SK_BLOCKPERM_KERNEL_*), row
  * slices Q, rows per slice, workspace bytes, affine a, affine b, a^-1 mod M,
  * partial rows per wavefront R, row groups G, column slices} (a, b, a^-1 are
- * 0 for the shift wiring; R, G and column slices 0 unless the register
- * kernel runs).
+ * 0 for the shift wiring; R is 0 unless the register kernel runs; G and
+ * the column slices are the register kernel's, or the component kernel's
+ * groups of 64 output rows per component and 32-column tiles, else 0).
  */
 #define SK_BLOCKPERM_PLAN_FIELDS 10
 sk_status sk_blockperm_plan_describe(int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa,

@@ -392,15 +392,17 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
 }
 
 // BlockPerm launch plan: the register kernel where its shape rules hold;
-// else the component kernel (shift wiring, s = 1, kappa in {1, 2, 4, 8},
-// enough components x tiles to fill the device); else the slice kernel with
-// Qs row slices.  The register and slice kernels take a workspace of
+// else the component kernel (shift wiring: a workgroup per component,
+// column tile and 64 output rows, no workspace) where its workgroups fill
+// the device; else the slice kernel with Qs row slices; else the component
+// kernel.  The register and slice kernels take a workspace of
 // Q*kappa*d*n floats for their own Q; where the register kernel is planned
 // the slice kernel stays the fallback for an unaligned A, so the workspace
 // covers both.
 struct BpPlan {
     int kernel;                 // SK_BLOCKPERM_KERNEL_*
     bool comp_ok;               // the component kernel applies (NULL workspace)
+    sk::BpDirectPlan direct;    // its plan
     bool slice_ok;
     int32_t Qs;                 // slice kernel: row slices, rows per slice
     int64_t rps_s;
@@ -485,9 +487,7 @@ bool plan_blockperm(const sk::DevInfo &di, int64_t m, int32_t n, int32_t d, int3
     const int64_t Bc = m / M;
     const int64_t tiles = (n + 31) / 32;
     memset(p, 0, sizeof(*p));
-    p->comp_ok = wiring == SK_WIRING_SHIFT && s == 1 &&
-                 (kappa == 1 || kappa == 2 || kappa == 4 || kappa == 8) &&
-                 (int64_t)kappa * Br <= sk::blockperm_max_rows(di);
+    p->comp_ok = wiring == SK_WIRING_SHIFT && sk::plan_bp_direct(m, n, d, M, kappa, s, &p->direct);
     p->slice_ok = (int64_t)kappa * Br <= sk::blockperm_general_max_rows(di);
     if (p->slice_ok) {
         int64_t Q = (2 * (int64_t)di.num_cu + tiles * M - 1) / (tiles * M);
@@ -502,11 +502,13 @@ bool plan_blockperm(const sk::DevInfo &di, int64_t m, int32_t n, int32_t d, int3
     if (sk::plan_bp_regs(di, m, n, d, M, kappa, s, &p->regs)) {
         p->kernel = SK_BLOCKPERM_KERNEL_REGISTER;
         p->ws_bytes = p->regs.ws_bytes > p->ws_s ? p->regs.ws_bytes : p->ws_s;
-    } else if (p->comp_ok && tiles * (M / kappa) >= di.num_cu) {
+    } else if (p->comp_ok && p->direct.grid >= di.num_cu) {
         p->kernel = SK_BLOCKPERM_KERNEL_COMPONENT;
     } else if (p->slice_ok) {
         p->kernel = SK_BLOCKPERM_KERNEL_SLICE;
         p->ws_bytes = p->ws_s;
+    } else if (p->comp_ok) {
+        p->kernel = SK_BLOCKPERM_KERNEL_COMPONENT;
     } else {
         return false;
     }
@@ -524,6 +526,38 @@ void sigma_table(uint64_t seed, int32_t M, uint16_t *sigma) {
         sigma[k] = sigma[j];
         sigma[j] = t;
     }
+}
+
+// The component kernel (no workspace) for the shift wiring; arguments
+// already validated.
+sk_status run_direct(const float *A, int64_t m, int32_t n, int64_t lda, int32_t d, int32_t M,
+                     int32_t kappa, int32_t s, uint64_t seed, float *Y, int64_t ldy,
+                     uint32_t flags, hipStream_t stream) {
+    sk::BpDirectPlan plan{};
+    if (!sk::plan_bp_direct(m, n, d, M, kappa, s, &plan)) return SK_ERR_UNSUPPORTED;
+    sk::BpDirectArgs args;
+    memset(&args, 0, sizeof(args));
+    args.A = A;
+    args.Y = Y;
+    args.lda = lda;
+    args.ldy = ldy;
+    args.Bc = m / M;
+    args.n = n;
+    args.Br = d / M;
+    args.M = M;
+    args.kappa = kappa;
+    args.s = s;
+    args.C = M / kappa;
+    args.tiles = plan.tiles;
+    args.groups = plan.groups;
+    args.accumulate = (flags & SK_ACCUMULATE) ? 1 : 0;
+    args.scale = scale_of((int64_t)kappa * s);
+    args.seed = seed;
+    sk::BlockPermTable fwd, ginv;
+    memset(&ginv, 0, sizeof(ginv));
+    sigma_table(seed, M, fwd.tab);
+    for (int k = 0; k < M; ++k) ginv.tab[fwd.tab[k]] = (uint16_t)k;
+    return hip_status(sk::launch_bp_direct(plan, args, ginv, stream));
 }
 
 }  // namespace
@@ -785,7 +819,8 @@ sk_status sk_apply_blockperm_ex(const float *A, int64_t m, int32_t n, int64_t ld
     BpPlan p;
     if (!plan_blockperm(di, m, n, d, M, kappa, s, wiring, seed, &p)) return SK_ERR_UNSUPPORTED;
     if (p.kernel == SK_BLOCKPERM_KERNEL_COMPONENT || (workspace == nullptr && p.comp_ok))
-        return sk_apply_blockperm(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags, stream);
+        return run_direct(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags,
+                          (hipStream_t)stream);
     if (workspace == nullptr) return SK_ERR_NULL;
     if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
     if (workspace_bytes < p.ws_bytes) return SK_ERR_ARG;
@@ -862,8 +897,9 @@ sk_status sk_blockperm_plan_describe(int64_t m, int32_t n, int32_t d, int32_t M,
     const int64_t v[SK_BLOCKPERM_PLAN_FIELDS] = {
         p.kernel, regs ? p.regs.Q : (comp ? 0 : p.Qs),
         regs ? p.regs.rows_per_slice : (comp ? 0 : p.rps_s), (int64_t)p.ws_bytes, p.a, p.b,
-        p.ainv, regs ? p.regs.rows_per_wave : 0, regs ? p.regs.groups : 0,
-        regs ? p.regs.slices : 0};
+        p.ainv, regs ? p.regs.rows_per_wave : 0,
+        regs ? p.regs.groups : (comp ? p.direct.groups : 0),
+        regs ? p.regs.slices : (comp ? p.direct.tiles : 0)};
     for (int i = 0; i < SK_BLOCKPERM_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }
@@ -879,39 +915,10 @@ sk_status sk_apply_blockperm(const float *A, int64_t m, int32_t n, int64_t lda, 
     if (flags & ~SK_ACCUMULATE) return SK_ERR_ARG;
     if (A == nullptr || Y == nullptr) return SK_ERR_NULL;
     if (overlaps(A, span_bytes(m, n, lda, 4), Y, span_bytes(d, n, ldy, 4))) return SK_ERR_ARG;
-    if (s != 1) return SK_ERR_UNSUPPORTED;
-    if (kappa != 1 && kappa != 2 && kappa != 4 && kappa != 8) return SK_ERR_UNSUPPORTED;
     const int32_t Br = d / M;
-    sk::DevInfo di;
-    if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
-    if ((int64_t)kappa * Br > sk::blockperm_max_rows(di)) return SK_ERR_UNSUPPORTED;
-
-    sk::BlockPermArgs args;
-    memset(&args, 0, sizeof(args));
-    args.A = A;
-    args.Y = Y;
-    args.lda = lda;
-    args.ldy = ldy;
-    args.Bc = m / M;
-    args.n = n;
-    args.Br = Br;
-    args.C = M / kappa;
-    args.accumulate = (flags & SK_ACCUMULATE) ? 1 : 0;
-    args.scale = scale_of((int64_t)kappa * s);
-    args.seed = seed;
-    // sigma: Fisher-Yates over [M] with Philox draws (domain word 3 = 2).
-    uint16_t sigma[sk::kBlockPermMaxM];
-    for (int k = 0; k < M; ++k) sigma[k] = (uint16_t)k;
-    for (int k = M - 1; k >= 1; --k) {
-        const sk::u32x4 w = sk::philox4x32_10(sk::u32x4{(uint32_t)k, 0u, 0u, 2u}, (uint32_t)seed,
-                                              (uint32_t)(seed >> 32));
-        const uint32_t j = sk::mulhi32(w.x, (uint32_t)(k + 1));
-        const uint16_t t = sigma[k];
-        sigma[k] = sigma[j];
-        sigma[j] = t;
-    }
-    for (int g = 0; g < M; ++g) args.ginv[sigma[g]] = (uint16_t)g;
-    return hip_status(sk::launch_blockperm(args, kappa, (hipStream_t)stream));
+    // s rows per block pair come from an odd stride modulo B_r
+    if (s > 1 && (Br & (Br - 1)) != 0) return SK_ERR_UNSUPPORTED;
+    return run_direct(A, m, n, lda, d, M, kappa, s, seed, Y, ldy, flags, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -130,21 +130,29 @@ hipError_t launch_fused(const FusedPlan &plan, bool f16, const float *A, int64_t
                         int64_t ldb, uint32_t *ws, int mode, hipStream_t stream);
 
 constexpr int kBlockPermMaxM = 1024;
-struct BlockPermArgs {
+
+// BlockPerm without a workspace (blockperm_direct.hip): shift wiring, any
+// kappa | M, s <= B_r (s > 1: B_r a power of two).  A workgroup per (shift
+// component, 32-column tile, group of 64 of the component's kappa*B_r
+// output rows) writes those rows of Y once.
+struct BpDirectArgs {
     const float *A;
     float *Y;
     int64_t lda, ldy;
-    int64_t Bc;             // input rows per block
-    int32_t n, Br;          // columns, output rows per block
-    int32_t C;              // components = M / kappa
+    int64_t Bc;                 // input rows per block
+    int32_t n, Br, M, kappa, s;
+    int32_t C;                  // components = M / kappa
+    int32_t tiles, groups;      // column tiles, row groups per component
     int32_t accumulate;
-    float scale;            // float32(1/sqrt(kappa*s))
-    uint32_t pad_;
+    float scale;                // float32(1/sqrt(kappa*s))
     uint64_t seed;
-    uint16_t ginv[kBlockPermMaxM];  // sigma^{-1}
 };
-// Largest kappa*B_r the LDS tile allows.
-int blockperm_max_rows(const DevInfo &di);
+struct BpDirectPlan {
+    int32_t tiles, groups;
+    int64_t grid;               // components x row groups x column tiles
+};
+bool plan_bp_direct(int64_t m, int32_t n, int32_t d, int32_t M, int32_t kappa, int32_t s,
+                    BpDirectPlan *p);
 
 // General BlockPerm (blockperm_general.hip): any kappa <= 32, s <= 32 unique
 // rows, shift or affine wiring, input blocks in Q row slices; partial tiles
@@ -172,7 +180,9 @@ int blockperm_general_max_rows(const DevInfo &di);
 hipError_t launch_blockperm_general(const BlockPermGenArgs &args, const BlockPermTable &ginv,
                                     const BlockPermTable &fwd, float *Y, int64_t ldy,
                                     int accumulate, hipStream_t stream);
-hipError_t launch_blockperm(const BlockPermArgs &args, int32_t kappa, hipStream_t stream);
+// sigma^-1 of the shift wiring in ginv
+hipError_t launch_bp_direct(const BpDirectPlan &p, const BpDirectArgs &args,
+                            const BlockPermTable &ginv, hipStream_t stream);
 // Y (=|+=) the fixed-order sum of the [M][Q][kappa][B_r][n] partials.
 hipError_t launch_bp_reduce(const BlockPermGenArgs &args, const BlockPermTable &fwd, float *Y,
                             int64_t ldy, int accumulate, hipStream_t stream);

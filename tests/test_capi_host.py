@@ -143,7 +143,7 @@ def test_f16acc_pair_rules(lib, args, expect):
     ((A, 1024, 64, 32, 64, 64, 4, 1, 7, B, 64, 0), b.SK_ERR_SHAPE),    # lda < n
     ((A, 1024, 64, 64, 64, 64, 4, 1, 7, B, 32, 0), b.SK_ERR_SHAPE),    # ldy < n
     ((A, 1024, 64, 64, 64, 64, 4, 2, 7, B, 64, 0), b.SK_ERR_SHAPE),    # s > B_r = 1
-    ((A, 1024, 64, 64, 128, 64, 4, 2, 7, B, 64, 0), b.SK_ERR_UNSUPPORTED),  # s = 2
+    ((A, 1024, 64, 64, 192, 64, 4, 2, 7, B, 64, 0), b.SK_ERR_UNSUPPORTED),  # s = 2, B_r = 3
     ((A, 2048, 64, 64, 2048, 2048, 4, 1, 7, B, 64, 0), b.SK_ERR_UNSUPPORTED),  # M too large
     ((A, 1024, 64, 64, 64, 64, 4, 1, 7, B, 64, 2), b.SK_ERR_ARG),      # variant flag
     ((None, 1024, 64, 64, 64, 64, 4, 1, 7, B, 64, 0), b.SK_ERR_NULL),
@@ -155,11 +155,50 @@ def test_blockperm_validation(lib, args, expect):
     assert lib.sk_apply_blockperm(*args, None) == expect
 
 
-def test_figure2_shape_is_accepted_up_to_s(lib):
-    # FlashSketch Figure 2: M=16, B_r=64, B_c=128, kappa=4, s=2 (d_in=2048, k=1024):
-    # the shapes validate; s=2 is a valid request this library does not build.
-    assert lib.sk_apply_blockperm(A, 2048, 64, 64, 1024, 16, 4, 2, 7, B, 64, 0, None) == \
-        b.SK_ERR_UNSUPPORTED
+def test_figure2_shape_is_planned(lib):
+    # FlashSketch Figure 2: M=16, B_r=64, B_c=128, kappa=4, s=2 (d_in=2048,
+    # k=1024): a valid request of the shift wiring; without a workspace the
+    # component kernel takes it, kappa*B_r = 256 output rows in 4 row groups
+    p = b.sk_blockperm_plan_describe(2048, 64, 1024, 16, 4, 2, b.SK_WIRING_SHIFT, 7,
+                                     num_cu=256, max_lds=160 * 1024)
+    assert p["ws_bytes"] > 0 or p["kernel"] == b.SK_BLOCKPERM_KERNEL_COMPONENT
+
+
+@pytest.mark.parametrize("m,n,d,M,kappa,s", [
+    (1 << 21, 510, 1024, 64, 4, 1),       # the BlockPerm workload (ragged width)
+    (2048, 63, 1024, 16, 4, 2),           # Figure 2 with s = 2
+    (256 * 8, 8, 256, 256, 256, 1),       # kappa = M: one component
+    (600, 7, 18, 6, 2, 1),                # B_r = 3
+    (64 * 129, 37, 64, 64, 64, 1),        # kappa = 64, ragged tiles
+    (4096, 65, 1024, 16, 4, 8),           # kappa * B_r = 256, s = 8
+])
+def test_blockperm_component_grid_covers_every_output_once(m, n, d, M, kappa, s):
+    """The component kernel's workgroups (component, row group, column
+    tile) own disjoint sets of output elements whose union is all of Y:
+    each element is written once, by one workgroup, with no atomics.  The
+    index arithmetic is the kernel's: tile = wg % tiles, group = (wg /
+    tiles) % groups, component = wg / (tiles * groups); a group holds the
+    component's tile rows [64 group, 64 group + 64) of its kappa*B_r.
+    Where sk_apply_blockperm_ex plans the component kernel (odd widths rule
+    out the register kernel; one CU makes any grid fill the device) its
+    groups and tiles are the ones used here."""
+    import numpy as np
+    Br, C = d // M, M // kappa
+    T = kappa * Br
+    G, tiles = -(-T // 64), -(-n // 32)
+    if kappa <= 32:
+        p = b.sk_blockperm_plan_describe(m, n, d, M, kappa, s, b.SK_WIRING_SHIFT, 3, num_cu=1,
+                                         max_lds=160 * 1024)
+        assert p["kernel"] == b.SK_BLOCKPERM_KERNEL_COMPONENT
+        assert (p["groups"], p["slices"]) == (G, tiles)
+    seen = np.zeros((C, T, tiles), dtype=np.int64)
+    for wg in range(C * G * tiles):
+        tile, cg = wg % tiles, wg // tiles
+        grp, rho = cg % G, cg // G
+        r0 = grp * 64
+        seen[rho, r0:min(T, r0 + 64), tile] += 1
+    assert (seen == 1).all()
+    assert tiles * 32 >= n > (tiles - 1) * 32
 
 
 # ------------------------------------------------ LDS plan vs kernel bounds

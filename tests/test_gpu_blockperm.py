@@ -289,3 +289,86 @@ def test_ex_workspace_errors():
         assert e.value.status == expect
     sync()
     assert torch.all(Y == 7.0)
+
+
+# --------------------------- sk_apply_blockperm: no workspace, every shape
+
+def direct(A, d, M, kappa, s, seed, out=None, flags=0, n=None, lda=None):
+    """sk_apply_blockperm through the C ABI (shift wiring, no workspace)."""
+    m = A.shape[0]
+    n = A.shape[1] if n is None else n
+    lda = A.stride(0) if lda is None else lda
+    Y = torch.empty((d, n), dtype=torch.float32, device=A.device) if out is None else out
+    b.sk_apply_blockperm(A, m, n, lda, d, M, kappa, s, seed, Y, Y.stride(0), flags)
+    sync()
+    return Y
+
+
+@pytest.mark.parametrize("m,n,d,M,kappa,s,seed", [
+    (256, 5, 32, 4, 2, 1, 9),           # B_r = 8, 5 columns (scalar loads)
+    (512, 33, 64, 8, 4, 1, 1),          # two column tiles, the second ragged
+    (512, 32, 64, 8, 1, 1, 2),          # kappa = 1: block-diagonal
+    (1024, 40, 128, 16, 8, 1, 3),       # kappa = 8, 16-byte loads, ragged tile
+    (600, 7, 18, 6, 2, 1, 4),           # B_c = 100 (partial stage), B_r = 3
+    (1024, 36, 128, 8, 4, 2, 5),        # s = 2
+    (2048, 64, 512, 16, 16, 1, 6),      # kappa = M = 16: one component, 512 rows in 8 groups
+    (2048, 48, 256, 32, 32, 4, 7),      # kappa = M = 32, s = 4
+    (4096, 64, 1024, 16, 4, 8, 8),      # B_r = 64, s = 8: 256 rows in 4 groups
+    (64 * 129, 32, 64, 64, 64, 1, 10),  # kappa = 64 (beyond the workspace kernels), B_r = 1
+    (128 * 8, 8, 128, 128, 128, 1, 11), # kappa = M = 128
+    (2048, 64, 1024, 16, 4, 2, 12),     # FlashSketch Figure 2 (M=16, B_r=64, B_c=128, s=2)
+])
+def test_direct_vs_oracle(m, n, d, M, kappa, s, seed):
+    """Against the fp64 oracle (itself pinned to the dense S brute force):
+    the no-workspace kernel over the boundary's domain (any kappa | M,
+    s <= B_r)."""
+    say(f"blockperm direct m={m} n={n} d={d} M={M} kappa={kappa} s={s}")
+    A = inputs.gaussian(m, n, seed=seed)
+    Y = direct(to_dev(A), d, M, kappa, s, seed)
+    ref = oracle.blockperm_f64(A, d, M, kappa, s, seed)
+    assert oracle.rel_frob(Y.cpu().numpy(), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("kappa,s", [(4, 1), (16, 1), (4, 4), (1, 16)])
+def test_direct_integer_exact_accumulate_and_repeat(kappa, s):
+    """kappa*s a power of 4: integer inputs give exact sums in any order, so
+    Y equals fp64 bit for bit (a lost or doubled hit changes it);
+    SK_ACCUMULATE adds a second copy.  Within a stage the hits of an output
+    row are added in the order the LDS counter handed out their slots, so
+    two calls on Gaussian inputs agree to FP32 rounding, not bit for bit."""
+    m, n, d, M = 8192, 64, 512, 16
+    A = inputs.integer_matrix(m, n, -8, 8, seed=3)
+    Ad = to_dev(A)
+    ref = oracle.blockperm_f64(A, d, M, kappa, s, 21)
+    Y = direct(Ad, d, M, kappa, s, 21)
+    assert np.array_equal(Y.cpu().numpy().astype(np.float64), ref)
+    direct(Ad, d, M, kappa, s, 21, out=Y, flags=b.SK_ACCUMULATE)
+    assert np.array_equal(Y.cpu().numpy().astype(np.float64), 2 * ref)
+    G = inputs.gaussian_torch(m, n, seed=4)
+    Y1, Y2 = direct(G, d, M, kappa, s, 5), direct(G, d, M, kappa, s, 5)
+    assert float(torch.linalg.norm(Y1 - Y2) / torch.linalg.norm(Y1)) <= 1e-6
+
+
+def test_direct_unaligned_and_padded():
+    """A starting one float past a 16-byte boundary with a padded leading
+    dimension (scalar loads), and a padded output: columns past n untouched."""
+    m, n, d, M, kappa = 4096, 60, 256, 16, 4
+    A = inputs.gaussian(m, 72, seed=6)
+    Ad = to_dev(A)[:, 1:1 + n]
+    out = torch.full((d, 70), 7.0, device=dev())
+    Y = direct(Ad, d, M, kappa, 1, 13, out=out[:, :n], n=n, lda=72)
+    Yh = out.cpu().numpy()
+    assert np.all(Yh[:, n:] == 7.0)
+    ref = oracle.blockperm_f64(np.ascontiguousarray(A[:, 1:1 + n]), d, M, kappa, 1, 13)
+    assert oracle.rel_frob(Yh[:, :n], ref) <= 1e-5
+    del Y
+
+
+def test_direct_unsupported_stride_rule():
+    """s > 1 needs B_r a power of two (the odd stride alpha then gives s
+    distinct rows): B_r = 6 with s = 2 is refused before any launch."""
+    A = torch.zeros((600, 8), device=dev())
+    Y = torch.zeros((36, 8), device=dev())
+    with pytest.raises(b.SketchError) as e:
+        b.sk_apply_blockperm(A, 600, 8, 8, 36, 6, 2, 2, 1, Y, 8, 0)
+    assert e.value.status == b.SK_ERR_UNSUPPORTED
