@@ -467,14 +467,24 @@ def main():
                                 ("fp16_sr_flat", b.SK_FORMAT_F16, b.SK_CONVERT_SR),
                                 ("bf16_rn_flat", b.SK_FORMAT_BF16, b.SK_CONVERT_RN)):
             t[name] = timed(lambda: b.sk_apply_lowp(Ac, mc, nc, nc, ric, vc, zc, Bc16, dc, nc,
-                                                    fmt, conv, 1, 0, 0, sp),
+                                                    fmt, conv, 1, 0, 0, None, 0, sp),
                             max(1, K // 4), 1, stream)
+        nlw = b.sk_apply_workspace_size(b.SK_PRECISION_LOWP, mc, nc, dc, zc, b.SK_VARIANT_REG)
+        wlw = torch.empty(nlw, dtype=torch.uint8, device=dev)
+        for name, fmt, conv in (("fp16_rn_two_level_apply", b.SK_FORMAT_F16, b.SK_CONVERT_RN),
+                                ("fp16_sr_two_level_apply", b.SK_FORMAT_F16, b.SK_CONVERT_SR),
+                                ("bf16_rn_two_level_apply", b.SK_FORMAT_BF16, b.SK_CONVERT_RN)):
+            t[name] = timed(lambda: b.sk_apply_lowp(Ac, mc, nc, nc, ric, vc, zc, Bc16, dc, nc,
+                                                    fmt, conv, 1, 0, b.SK_VARIANT_REG, wlw, nlw,
+                                                    sp), max(1, K // 4), 1, stream)
+        del wlw
         c4 = {"workload": "A 4,194,304 x 64 N(0,1) x exp(2Z) row scales, zeta = 4, d = 128",
               **{k + "_ms": round(v, 4) for k, v in t.items()},
               "fp16_two_level_GBps": round(sparsestack_bytes(mc, nc, dc, zc, 2)
                                            / t["fp16_two_level"] / 1e6, 1),
               "note": "fp32/fp16 two-level are complete sketches (metadata drawn in the call); "
-                      "the flat variants are the apply alone"}
+                      "the flat and *_two_level_apply variants are the apply alone (stored "
+                      "metadata; the two-level applies convert each contribution per hit)"}
         print("[bench] range config: " + ", ".join(f"{k} {v:.4f} ms" for k, v in t.items()),
               file=sys.stderr, flush=True)
         del Ac, ric, vc, Bc16, Bc32, wc16, wc32

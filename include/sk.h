@@ -85,6 +85,7 @@ typedef enum sk_status {
 /* precision argument of sk_apply_workspace_size and sk_sketch_workspace_size */
 #define SK_PRECISION_F32    0
 #define SK_PRECISION_F16ACC 1
+#define SK_PRECISION_LOWP   2   /* sk_apply_workspace_size: sk_apply_lowp */
 
 /*
  * sk_meta_generate: routing and sign metadata of a SparseStack sketch.
@@ -236,9 +237,7 @@ sk_status sk_apply_f16acc_ws(const float *A, int64_t m, int32_t n, int64_t lda,
  * sk_apply_lowp: the reduced-precision sketch with a choice of contribution
  * conversion and accumulation format (FP16 sketching page §III-D: the
  * contribution is converted by one of several rules and fed to the same
- * packed nearest-even atomic accumulation; §V-E: a BF16 variant).
- * The page's flat design: one packed global atomic per (row, block, column
- * pair), so the additions happen in an unspecified order.
+ * packed nearest-even accumulation; §V-E: a BF16 variant).
  *
  *   A, row_idx, val, zeta, d, ldb  as for sk_apply_f16acc (n, lda, ldb
  *            even; A 8-byte and B 4-byte aligned).
@@ -246,7 +245,7 @@ sk_status sk_apply_f16acc_ws(const float *A, int64_t m, int32_t n, int64_t lda,
  *            bfloat16 (SK_FORMAT_BF16, 8-bit exponent and significand).
  *   format, convert
  *            SK_FORMAT_F16 + SK_CONVERT_RN: nearest-even (the FP16 kernel's
- *              rule, here without LDS privatization);
+ *              rule);
  *            SK_FORMAT_F16 + SK_CONVERT_SR: stochastic conversion.  For a
  *              contribution q with FP16 neighbours l <= |q| < v, the
  *              magnitude becomes v when the 32-bit draw r < frac * 2^32,
@@ -256,18 +255,37 @@ sk_status sk_apply_f16acc_ws(const float *A, int64_t m, int32_t n, int64_t lda,
  *              word c mod 4 of Philox-4x32-10 of counter (g lo, g hi,
  *              c div 4, 3 + 4t) and key (sr_seed lo, sr_seed hi);
  *            SK_FORMAT_BF16 + SK_CONVERT_RN: nearest-even conversion to
- *              BF16 and packed BF16 nearest-even additions.
+ *              BF16 and BF16 nearest-even additions.
  *            BF16 with SR is SK_ERR_UNSUPPORTED.
  *   sr_seed, row_offset  the SR draws' seed and A's first global row
  *            (ignored by the RN rules; row_offset >= 0).
- *   flags    SK_ACCUMULATE or 0 (0 zeroes B first, on the stream).
+ *   flags    SK_ACCUMULATE, and one of
+ *              0 or SK_VARIANT_FLAT: the page's flat design, one packed
+ *                global atomic per (row, block, column pair), additions in
+ *                an unspecified order (B is zeroed first unless
+ *                SK_ACCUMULATE); no workspace;
+ *              SK_VARIANT_REG: the two-level design of the fused FP16
+ *                sketch: each workgroup accumulates a chunk of rows in
+ *                registers (packed pairs of the format, nearest-even
+ *                additions, ascending rows) and a reduce adds the chunk
+ *                partials in a fixed order (that of sk_apply_f16acc_ws's
+ *                register variant), in the format, or in FP32 with one
+ *                final rounding when SK_COMBINE_F32 is also given.
+ *                Needs d % 16 == 0, zeta <= 16 and a workspace of
+ *                sk_apply_workspace_size(SK_PRECISION_LOWP, ...,
+ *                SK_VARIANT_REG) bytes (16-byte aligned, disjoint from the
+ *                other buffers).  Reproducible bit for bit.
+ *   workspace, workspace_bytes  SK_VARIANT_REG's scratch (else ignored).
  * Errors: as sk_apply_f16acc, plus SK_ERR_ARG for an unknown format,
- * conversion or flag and SK_ERR_UNSUPPORTED for BF16 with SR.
+ * conversion or flag (SK_COMBINE_F32 without SK_VARIANT_REG), SK_ERR_NULL
+ * (SK_VARIANT_REG without a workspace) and SK_ERR_UNSUPPORTED for BF16 with
+ * SR or a shape SK_VARIANT_REG does not cover.
  */
 sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
                         const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
                         int32_t d, int64_t ldb, int32_t format, int32_t convert,
-                        uint64_t sr_seed, int64_t row_offset, uint32_t flags, void *stream);
+                        uint64_t sr_seed, int64_t row_offset, uint32_t flags,
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sk_apply_workspace_size: bytes of workspace that sk_apply_f32_ws
@@ -275,6 +293,7 @@ sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
  * uses for these sizes and flags on the current device, whatever lda and
  * A's alignment: SK_VARIANT_REG the register plan (for A with lda = n and
  * an aligned base), SK_VARIANT_LDS the LDS plans, 0 the larger of the two.
+ * SK_PRECISION_LOWP: the bytes sk_apply_lowp uses (SK_VARIANT_REG only).
  * 0 when the chosen variant uses none (FLAT, m = 0, or no plan fits).
  * Errors: SK_ERR_NULL (bytes NULL), SK_ERR_SHAPE, SK_ERR_ARG (precision or
  * flags), SK_ERR_HIP (device query failed).

@@ -121,17 +121,13 @@ def contributions(A, row_idx, val, zeta, e, fmt, conv, sr_seed=0, row_offset=0):
     return sr_f16(q, r)
 
 
-def sketch_lowp_emul(A, row_idx, val, d, zeta, fmt="f16", conv="rn", sr_seed=0, row_offset=0):
-    """Reduced-precision sketch with per-contribution conversion and
-    nearest-even accumulation in the same format, every output entry adding
-    its contributions one at a time in ascending (i, t) order starting from
-    +0 (the order of one atomic per contribution applied row by row).
-    Entries outside their own stack block contribute nothing.  Returns
-    float16 (fmt "f16") or float32 holding BF16 values (fmt "bf16")."""
+def _lowp_flat(A, row_idx, val, d, zeta, fmt, conv, sr_seed, row_offset, e0, e1):
+    """Entries [e0, e1) accumulated from +0 in the format, each output entry
+    adding its contributions one at a time in ascending entry order."""
     m, n = A.shape
     db = d // zeta
-    e_all = np.arange(m * zeta, dtype=np.int64)
-    r_all = row_idx.astype(np.int64)
+    e_all = np.arange(e0, e1, dtype=np.int64)
+    r_all = row_idx[e0:e1].astype(np.int64)
     t_all = e_all % zeta
     keep = (r_all >= t_all * db) & (r_all < (t_all + 1) * db)
     e_all, r_all = e_all[keep], r_all[keep]
@@ -149,3 +145,42 @@ def sketch_lowp_emul(A, row_idx, val, d, zeta, fmt="f16", conv="rn", sr_seed=0, 
         c = contributions(A, row_idx, val, zeta, sel, fmt, conv, sr_seed, row_offset)
         B[act] = rn_f16_add(B[act], c) if fmt == "f16" else rn_bf16_add(B[act], c)
     return B
+
+
+def sketch_lowp_emul(A, row_idx, val, d, zeta, fmt="f16", conv="rn", sr_seed=0, row_offset=0,
+                     chunk_rows=None, combine="fmt", B0=None):
+    """Reduced-precision sketch with per-contribution conversion and
+    nearest-even accumulation in the same format.  Entries outside their own
+    stack block contribute nothing.  Returns float16 (fmt "f16") or float32
+    holding BF16 values (fmt "bf16").
+
+    chunk_rows=None: every output entry adds its contributions one at a time
+    in ascending (i, t) order starting from +0 (the order of one atomic per
+    contribution applied row by row).
+    chunk_rows=R: each run of R input rows is accumulated that way into its
+    own partial starting from +0, and the partials are added in chunk order:
+    with nearest-even additions in the format (combine="fmt", every
+    addition in the format), or (combine="f32") summed in FP32 and the total
+    rounded to the format once.  B0 (float16, or float32 holding BF16
+    values): the sum starts from B0 instead of +0."""
+    m = A.shape[0]
+    if combine not in ("fmt", "f32"):
+        raise ValueError("combine is 'fmt' or 'f32'")
+    add = rn_f16_add if fmt == "f16" else rn_bf16_add
+    out_t = np.float16 if fmt == "f16" else np.float32
+    if chunk_rows is None:
+        B = _lowp_flat(A, row_idx, val, d, zeta, fmt, conv, sr_seed, row_offset, 0, m * zeta)
+        return B if B0 is None else add(np.asarray(B0, out_t), B).astype(out_t)
+    parts = [_lowp_flat(A, row_idx, val, d, zeta, fmt, conv, sr_seed, row_offset, r0 * zeta,
+                        min(m, r0 + chunk_rows) * zeta) for r0 in range(0, m, chunk_rows)]
+    start = np.zeros((d, A.shape[1]), out_t) if B0 is None else np.asarray(B0, out_t)
+    if combine == "fmt":
+        B = start
+        for P in parts:
+            B = add(B, P).astype(out_t)
+        return B
+    acc = start.astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for P in parts:
+            acc = acc + P.astype(np.float32)
+        return acc.astype(np.float16) if fmt == "f16" else rn_bf16(acc)

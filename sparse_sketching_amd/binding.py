@@ -26,6 +26,7 @@ SK_VARIANT_REG = 8
 SK_COMBINE_F32 = 16
 SK_PRECISION_F32 = 0
 SK_PRECISION_F16ACC = 1
+SK_PRECISION_LOWP = 2
 SK_FORMAT_F16 = 0
 SK_FORMAT_BF16 = 1
 SK_CONVERT_RN = 0
@@ -81,7 +82,7 @@ _SIGNATURES = {
     "sk_apply_lowp": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
                                  _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
                                  _c.c_int32, _c.c_int32, _c.c_uint64, _c.c_int64, _c.c_uint32,
-                                 _c.c_void_p]),
+                                 _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "sk_apply_blockperm_ex": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64,
                                          _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
                                          _c.c_int32, _c.c_uint64, _c.c_void_p, _c.c_int64,
@@ -303,10 +304,11 @@ def sk_blockperm_plan_describe(m, n, d, M, kappa, s, wiring, seed, num_cu, max_l
 
 
 def sk_apply_lowp(A, m, n, lda, row_idx, val, zeta, B, d, ldb, format, convert, sr_seed=0,
-                  row_offset=0, flags=0, stream=None):
+                  row_offset=0, flags=0, workspace=None, workspace_bytes=0, stream=None):
     _check("sk_apply_lowp", load().sk_apply_lowp(
         _ptr(A), m, n, lda, _ptr(row_idx), _ptr(val), zeta, _ptr(B), d, ldb, format, convert,
-        sr_seed, row_offset, flags, _stream(stream)))
+        sr_seed, row_offset, flags, _ptr(workspace), _nbytes(workspace, workspace_bytes),
+        _stream(stream)))
 
 
 def sk_sketch_f32(seed, row_offset, A, m, n, lda, d, zeta, B, ldb, flags=0, workspace=None,
@@ -428,7 +430,9 @@ def sketch(A, d, zeta, seed, precision="f16acc", flags=0, ws=True, stream=None):
 def apply_lowp(A, row_idx, val, zeta, d, fmt="f16", conv="rn", sr_seed=0, row_offset=0, out=None,
                flags=0, stream=None):
     """Reduced-precision sketch from metadata: fmt "f16" (float16 B) with
-    conv "rn" or "sr", or fmt "bf16" (bfloat16 B) with conv "rn"."""
+    conv "rn" or "sr", or fmt "bf16" (bfloat16 B) with conv "rn".  flags
+    with SK_VARIANT_REG: the two-level design (a workspace is allocated);
+    else the flat atomic design."""
     import torch
     _need_device(A, torch.float32, "A")
     m, n = A.shape
@@ -443,9 +447,14 @@ def apply_lowp(A, row_idx, val, zeta, d, fmt="f16", conv="rn", sr_seed=0, row_of
             raise ValueError("metadata shorter than m*zeta")
     f = SK_FORMAT_F16 if fmt == "f16" else SK_FORMAT_BF16
     c = SK_CONVERT_RN if conv == "rn" else SK_CONVERT_SR
+    ws = None
+    if flags & SK_VARIANT_REG:
+        nb = sk_apply_workspace_size(SK_PRECISION_LOWP, m, n, d, zeta, flags)
+        if nb:
+            ws = torch.empty(nb, dtype=torch.uint8, device=A.device)
     sk_apply_lowp(A, m, n, A.stride(0) if m else n, row_idx if m else None, val if m else None,
-                  zeta, out, d, out.stride(0), f, c, sr_seed, row_offset, flags, stream)
-    _keep(stream, out)
+                  zeta, out, d, out.stride(0), f, c, sr_seed, row_offset, flags, ws, 0, stream)
+    _keep(stream, out, ws)
     return out
 
 

@@ -637,9 +637,22 @@ sk_status sk_apply_workspace_size(int32_t precision, int64_t m, int32_t n, int32
                                   int32_t zeta, uint32_t flags, size_t *bytes) {
     if (bytes == nullptr) return SK_ERR_NULL;
     *bytes = 0;
-    if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC) return SK_ERR_ARG;
+    if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC &&
+        precision != SK_PRECISION_LOWP)
+        return SK_ERR_ARG;
     if (m < 0 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0) return SK_ERR_SHAPE;
-    if (precision == SK_PRECISION_F16ACC && n % 2 != 0) return SK_ERR_SHAPE;
+    if (precision != SK_PRECISION_F32 && n % 2 != 0) return SK_ERR_SHAPE;
+    if (precision == SK_PRECISION_LOWP) {
+        // sk_apply_lowp with SK_VARIANT_REG; no workspace otherwise
+        if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_REG | SK_COMBINE_F32))
+            return SK_ERR_ARG;
+        if (m == 0 || !(flags & SK_VARIANT_REG)) return SK_OK;
+        sk::DevInfo di;
+        if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
+        sk::LowpRegPlan lp{};
+        if (sk::plan_lowp_reg(di, m, n, d, zeta, &lp)) *bytes = lp.ws_bytes;
+        return SK_OK;
+    }
     const uint32_t extra = precision == SK_PRECISION_F16ACC ? SK_COMBINE_F32 : 0u;
     if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_LDS | SK_VARIANT_REG | extra))
         return SK_ERR_ARG;
@@ -699,19 +712,49 @@ sk_status sk_lds_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t 
 sk_status sk_apply_lowp(const float *A, int64_t m, int32_t n, int64_t lda,
                         const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
                         int32_t d, int64_t ldb, int32_t format, int32_t convert,
-                        uint64_t sr_seed, int64_t row_offset, uint32_t flags, void *stream) {
+                        uint64_t sr_seed, int64_t row_offset, uint32_t flags, void *workspace,
+                        size_t workspace_bytes, void *stream) {
     if (format != SK_FORMAT_F16 && format != SK_FORMAT_BF16) return SK_ERR_ARG;
     if (convert != SK_CONVERT_RN && convert != SK_CONVERT_SR) return SK_ERR_ARG;
-    if (flags & ~SK_ACCUMULATE) return SK_ERR_ARG;
+    if (flags & ~(SK_ACCUMULATE | SK_VARIANT_FLAT | SK_VARIANT_REG | SK_COMBINE_F32))
+        return SK_ERR_ARG;
+    if ((flags & SK_VARIANT_FLAT) && (flags & SK_VARIANT_REG)) return SK_ERR_ARG;
     if (row_offset < 0) return SK_ERR_SHAPE;
-    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 2, d, ldb, flags, 0u);
+    sk_status st = check_apply(A, m, n, lda, row_idx, val, zeta, B, 2, d, ldb,
+                               flags & ~(SK_COMBINE_F32), 0u);
     if (st != SK_OK) return st;
     if (n % 2 != 0) return SK_ERR_SHAPE;
     if (ldb % 2 != 0 || (uintptr_t)B % 4 != 0) return SK_ERR_ALIGN;
     if (m > 0 && (lda % 2 != 0 || (uintptr_t)A % 8 != 0)) return SK_ERR_ALIGN;
     if (format == SK_FORMAT_BF16 && convert == SK_CONVERT_SR) return SK_ERR_UNSUPPORTED;
+    const bool reg = (flags & SK_VARIANT_REG) != 0;
+    if (!reg && (flags & SK_COMBINE_F32)) return SK_ERR_ARG;     // no reduce to combine in
     hipStream_t s = (hipStream_t)stream;
-    if (!(flags & SK_ACCUMULATE)) {
+    const bool accumulate = (flags & SK_ACCUMULATE) != 0;
+    if (reg) {
+        if (m == 0) {
+            if (accumulate) return SK_OK;
+            return hip_status(
+                sk::launch_zero_words(reinterpret_cast<uint32_t *>(B), d, n / 2, ldb / 2, s));
+        }
+        if (workspace == nullptr) return SK_ERR_NULL;
+        if ((uintptr_t)workspace % 16 != 0) return SK_ERR_ALIGN;
+        st = check_workspace(workspace, workspace_bytes, A, m, n, lda, row_idx, val, zeta, B,
+                             span_bytes(d, n, ldb, 2));
+        if (st != SK_OK) return st;
+        sk::DevInfo di;
+        if (sk::dev_info(&di) != hipSuccess) return SK_ERR_HIP;
+        sk::LowpRegPlan lp{};
+        if (!sk::plan_lowp_reg(di, m, n, d, zeta, &lp)) return SK_ERR_UNSUPPORTED;
+        if (workspace_bytes < lp.ws_bytes) return SK_ERR_ARG;
+        const int mode = (accumulate ? sk::kReduceModeAccumulate : 0) |
+                         ((flags & SK_COMBINE_F32) ? sk::kReduceModeCombineF32 : 0);
+        return hip_status(sk::launch_lowp_reg(lp, A, m, n, lda, row_idx, val, zeta, B, d, ldb,
+                                              format == SK_FORMAT_BF16,
+                                              convert == SK_CONVERT_SR, sr_seed, row_offset,
+                                              static_cast<uint32_t *>(workspace), mode, s));
+    }
+    if (!accumulate) {
         const hipError_t e =
             sk::launch_zero_words(reinterpret_cast<uint32_t *>(B), d, n / 2, ldb / 2, s);
         if (e != hipSuccess) return SK_ERR_HIP;

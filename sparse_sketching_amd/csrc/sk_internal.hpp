@@ -55,6 +55,33 @@ hipError_t launch_lowp_flat(const float *A, int64_t m, int32_t n, int64_t lda,
                             const int32_t *row_idx, const float *val, int32_t zeta, uint16_t *B,
                             int32_t d, int64_t ldb, bool bf16, bool sr, uint64_t sr_seed,
                             int64_t row_offset, hipStream_t stream);
+// Two-level reduced-precision apply (apply_lowp.hip, k_lowp_reg): chunk
+// partials in registers (FP16 or BF16 pairs), then the fixed-order reduce.
+constexpr int kLowpMaxZeta = 16;
+struct LowpRegArgs {
+    const float *A;
+    const int32_t *row_idx;
+    const float *val;
+    uint32_t *ws;               // [slices][chunks][d][64] partial words
+    int64_t m, lda, rows_per_chunk, row_offset;
+    uint64_t sr_seed;
+    int32_t npairs, d, zeta, chunks, slices, groups;
+};
+struct LowpRegPlan {
+    int R, groups;              // output rows per wavefront, row groups (16 R G = d)
+    int64_t slices;             // 128-column slices
+    int64_t rows_per_chunk, chunks, grid;
+    size_t ws_bytes;
+};
+bool plan_lowp_reg(const DevInfo &di, int64_t m, int32_t n, int32_t d, int32_t zeta,
+                   LowpRegPlan *p);
+// mode: the reduce's kReduceMode* bits (below)
+hipError_t launch_lowp_reg(const LowpRegPlan &p, const float *A, int64_t m, int32_t n,
+                           int64_t lda, const int32_t *ri, const float *v, int32_t zeta,
+                           uint16_t *B, int32_t d, int64_t ldb, bool bf16, bool sr,
+                           uint64_t sr_seed, int64_t row_offset, uint32_t *ws, int mode,
+                           hipStream_t stream);
+
 // The reduce's mode (bits): kReduceModeAccumulate adds onto B's current
 // words (B += ...); kReduceModeCombineF32 (FP16 only) sums the FP16 chunk
 // partials in FP32 and rounds the total once, instead of FP16 nearest-even

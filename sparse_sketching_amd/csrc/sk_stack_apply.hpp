@@ -125,6 +125,35 @@ struct AccF16 {
     }
 };
 
+// BF16 pairs (8-bit exponent and significand): the word arithmetic of the
+// two-level reduced-precision sketch's reduce.  A BF16 addition is the FP32
+// sum of the two (exactly widened) values rounded to BF16 nearest-even once,
+// which is the correctly rounded BF16 sum (FP32 has more than 2 x 8 + 2
+// significand bits).
+struct AccBF16 {
+    static constexpr int kCols = 2;
+    typedef uint32_t out_t;             // two BF16 values, low half = first column
+    __device__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    __device__ static float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+    __device__ static uint32_t pack(float x, float y) {
+        typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+        const bf2_t b = {(__bf16)x, (__bf16)y};          // nearest-even
+        return __builtin_bit_cast(uint32_t, b);
+    }
+    __device__ static uint32_t sum(uint32_t x, uint32_t y) {
+        return pack(lo(x) + lo(y), hi(x) + hi(y));
+    }
+    __device__ static uint32_t get(const out_t *B, int64_t off) { return B[off]; }
+    __device__ static void put(out_t *B, int64_t off, uint32_t w) { B[off] = w; }
+    // the reduce's FP32 combine (one rounding of the total to BF16)
+    typedef float2 wide_t;
+    __device__ static wide_t widen(uint32_t w) { return make_float2(lo(w), hi(w)); }
+    __device__ static wide_t wide_add(wide_t a, wide_t b) {
+        return make_float2(__fadd_rn(a.x, b.x), __fadd_rn(a.y, b.y));
+    }
+    __device__ static uint32_t narrow(wide_t a) { return pack(a.x, a.y); }
+};
+
 // K consecutive floats of A, loaded as one vector; NT adds the nontemporal
 // hint, for passes that read each element of A once.  (Where several
 // workgroups read the same rows, the hint costs their shared L2 hits: on

@@ -105,7 +105,8 @@ def test_workspace_validation(lib, fn, ws, nbytes, expect):
 
 
 @pytest.mark.parametrize("args,expect", [
-    ((2, 100, 64, 64, 4, 0), b.SK_ERR_ARG),        # unknown precision
+    ((3, 100, 64, 64, 4, 0), b.SK_ERR_ARG),        # unknown precision
+    ((2, 100, 64, 64, 4, 16), b.SK_OK),            # the reduced-precision sketch: no REG, none
     ((0, 100, 0, 64, 4, 0), b.SK_ERR_SHAPE),       # n < 1
     ((1, 100, 63, 64, 4, 0), b.SK_ERR_SHAPE),      # odd n for FP16
     ((0, 100, 64, 64, 3, 0), b.SK_ERR_SHAPE),      # d % zeta
@@ -464,7 +465,10 @@ def test_fused_plan_alignment_and_validation(lib):
 @pytest.mark.parametrize("args,expect", [
     ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 2, 0, 0, 0, 0), b.SK_ERR_ARG),      # unknown format
     ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 2, 0, 0, 0), b.SK_ERR_ARG),      # unknown conversion
-    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 0, 0, 0, 2), b.SK_ERR_ARG),      # variant flag
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 0, 0, 0, 4), b.SK_ERR_ARG),      # LDS variant
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 0, 0, 0, 10), b.SK_ERR_ARG),     # FLAT|REG
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 0, 0, 0, 16), b.SK_ERR_ARG),     # combine, no REG
+    ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 1, 0, 0, 8), b.SK_ERR_NULL),     # REG, no workspace
     ((A, 100, 64, 64, RI, V, 4, B, 64, 64, 0, 1, 0, -1, 0), b.SK_ERR_SHAPE),   # row_offset < 0
     ((A, 100, 63, 64, RI, V, 4, B, 64, 64, 0, 0, 0, 0, 0), b.SK_ERR_SHAPE),    # odd n
     ((A, 100, 64, 64, RI, V, 3, B, 64, 64, 0, 0, 0, 0, 0), b.SK_ERR_SHAPE),    # d % zeta
@@ -475,7 +479,7 @@ def test_fused_plan_alignment_and_validation(lib):
     ((A, 100, 64, 64, RI, V, 4, A + 256, 64, 64, 0, 0, 0, 0, 0), b.SK_ERR_ARG),  # B inside A
 ])
 def test_lowp_validation(lib, args, expect):
-    assert lib.sk_apply_lowp(*args, None) == expect
+    assert lib.sk_apply_lowp(*args, None, 0, None) == expect
 
 
 # ------------------------------------------------------- general BlockPerm

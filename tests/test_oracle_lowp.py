@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import meta_ref, sketch_f16_rn_emul, sketch_f64, sketch_lowp_emul
 from oracle.philox import philox_scalar
 from sparse_sketching_amd import inputs
 
@@ -179,3 +180,39 @@ def test_lowp_sr_mean_over_draws_is_unbiased():
     e12, e192 = mean_err(range(12)), mean_err(range(100, 292))
     assert oracle.rel_frob(rn, ref) > 0.9                  # RN loses nearly everything
     assert e192 < 0.3 and e12 / e192 > 2.5, (e12, e192)
+
+
+@pytest.mark.parametrize("fmt,conv", [("f16", "rn"), ("f16", "sr"), ("bf16", "rn")])
+def test_lowp_chunked_orders(fmt, conv):
+    """Chunks of one row: each partial holds at most one contribution per
+    output entry, so the chunked order equals the flat one; the whole matrix
+    as one chunk equals it too; FP16 RN chunks equal the RN oracle's own
+    chunked order (an independent implementation)."""
+    m, n, d, zeta = 300, 6, 16, 4
+    A = (inputs.gaussian(m, n, seed=2) * np.float32(29.0)).astype(np.float32)
+    ri, v = meta_ref(3, m, d, zeta)
+    flat = sketch_lowp_emul(A, ri, v, d, zeta, fmt, conv, sr_seed=5, row_offset=7)
+    one = sketch_lowp_emul(A, ri, v, d, zeta, fmt, conv, sr_seed=5, row_offset=7, chunk_rows=1)
+    whole = sketch_lowp_emul(A, ri, v, d, zeta, fmt, conv, sr_seed=5, row_offset=7,
+                             chunk_rows=m)
+    assert np.array_equal(one, flat) and np.array_equal(whole, flat)
+    if fmt == "f16" and conv == "rn":
+        for ch in (7, 64):
+            assert np.array_equal(sketch_lowp_emul(A, ri, v, d, zeta, chunk_rows=ch),
+                                  sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=ch))
+            assert np.array_equal(
+                sketch_lowp_emul(A, ri, v, d, zeta, chunk_rows=ch, combine="f32"),
+                sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=ch, combine="f32"))
+
+
+def test_lowp_bf16_chunked_exact_sums():
+    """Integer inputs whose every partial sum is exact in BF16: any chunking
+    and either combine equal fp64."""
+    m, n, d, zeta = 2048, 8, 64, 4
+    A = inputs.integer_matrix(m, n, -3, 3, seed=8)
+    ri, v = meta_ref(2, m, d, zeta)
+    ref = sketch_f64(A, ri, v, d, zeta)
+    assert np.abs(ref).max() <= 256
+    for ch, comb in ((64, "fmt"), (100, "f32"), (None, "fmt")):
+        got = sketch_lowp_emul(A, ri, v, d, zeta, "bf16", "rn", chunk_rows=ch, combine=comb)
+        assert np.array_equal(got.astype(np.float64), ref)
