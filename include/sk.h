@@ -553,9 +553,14 @@ sk_status sk_lds_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t 
  * Householder QR of SA, the projection Q^T Sb and a triangular solve: the
  * reduced solve of sketch-and-solve least squares (FP16 sketching page
  * §V-A, §V-D: FP32 QR, projection and solve on the d x n sketch;
- * FlashSketch page App. F.1.4).  A few launches per panel of up to 32
+ * FlashSketch page App. F.1.4).  Two launches per panel of up to 32
  * columns: the panel factored by one workgroup (reflectors as in LAPACK's
  * larfg, combined as I - V T V^T), the trailing columns updated by several.
+ * Every column of [SA | Sb] is first scaled by a power of two that brings
+ * its largest magnitude into [1/2, 1), and x scaled back at the end: the QR
+ * commutes exactly with such scalings, so x is the same bit for bit as
+ * without them wherever no intermediate overflows or underflows, and no
+ * norm or dot product overflows for any finite input.
  *   SA        device float, d x n row-major, row stride ld >= n; 1 <= n <= d
  *             <= 2048.  Not modified.
  *   Sb        device float[d].  Not modified.
@@ -571,8 +576,8 @@ sk_status sk_lds_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t 
 sk_status sk_lstsq_qr_f32(const float *SA, int32_t d, int32_t n, int64_t ld, const float *Sb,
                           float *x, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes of sk_lstsq_qr_f32 for these sizes ((n + 1) * d + 1024
- * floats).
+/* Workspace bytes of sk_lstsq_qr_f32 for these sizes ((n + 1) * (d + 1) +
+ * 1024 floats).
  * Errors: SK_ERR_NULL, SK_ERR_SHAPE. */
 sk_status sk_lstsq_workspace_size(int32_t d, int32_t n, size_t *bytes);
 

@@ -804,7 +804,7 @@ sk_status sk_lstsq_workspace_size(int32_t d, int32_t n, size_t *bytes) {
     if (bytes == nullptr) return SK_ERR_NULL;
     *bytes = 0;
     if (n < 1 || d < n || d > sk::kQrMaxRows) return SK_ERR_SHAPE;
-    *bytes = ((size_t)(n + 1) * (size_t)d + 1024) * sizeof(float);
+    *bytes = sk::lstsq_workspace_floats(d, n) * sizeof(float);
     return SK_OK;
 }
 
@@ -814,7 +814,7 @@ sk_status sk_lstsq_qr_f32(const float *SA, int32_t d, int32_t n, int64_t ld, con
     if (SA == nullptr || Sb == nullptr || x == nullptr || workspace == nullptr)
         return SK_ERR_NULL;
     if ((uintptr_t)workspace % 4 != 0) return SK_ERR_ALIGN;
-    const size_t need = ((size_t)(n + 1) * (size_t)d + 1024) * sizeof(float);
+    const size_t need = sk::lstsq_workspace_floats(d, n) * sizeof(float);
     if (workspace_bytes < need) return SK_ERR_ARG;
     const size_t aspan = span_bytes(d, n, ld, 4);
     if (overlaps(workspace, need, SA, aspan) || overlaps(workspace, need, Sb, (size_t)d * 4) ||

@@ -240,10 +240,11 @@ hipError_t launch_bp_regs(const BpRegsPlan &p, const BlockPermGenArgs &args,
                           int64_t ldy, int accumulate, hipStream_t stream);
 
 // Least squares on a small sketch (lstsq.hip): x = argmin ||SA x - Sb||_2 by
-// an FP32 Householder QR, one workgroup.  SA is d x n row-major (row stride
-// ld), 1 <= n <= d <= kQrMaxRows; W is a workspace of (n + 1) * d + 1024
+// an FP32 blocked Householder QR.  SA is d x n row-major (row stride ld),
+// 1 <= n <= d <= kQrMaxRows; W is a workspace of lstsq_workspace_floats(d, n)
 // floats.
 constexpr int kQrMaxRows = 2048;
+size_t lstsq_workspace_floats(int32_t d, int32_t n);
 hipError_t launch_lstsq_qr(const float *SA, int32_t d, int32_t n, int64_t ld, const float *Sb,
                            float *x, float *W, hipStream_t stream);
 

@@ -576,14 +576,14 @@ def test_blockperm_ex_validation(lib, args, expect):
 def test_lstsq_validation(lib):
     """sk_lstsq_qr_f32 rejects bad arguments before any HIP call (host
     buffers stand in for device pointers; every call here fails validation,
-    so nothing is launched), and the workspace size is (n + 1) d + 1024
-    floats."""
+    so nothing is launched), and the workspace size is (n + 1)(d + 1) + 1024
+    floats (the columns, the panel's T, the column exponents)."""
     d, n = 64, 32
     SA = (ctypes.c_float * (d * n))()
     Sb = (ctypes.c_float * d)()
     x = (ctypes.c_float * n)()
-    ws = (ctypes.c_float * ((n + 1) * d + 1025))()
-    nb = ((n + 1) * d + 1024) * 4
+    ws = (ctypes.c_float * ((n + 1) * (d + 1) + 1025))()
+    nb = ((n + 1) * (d + 1) + 1024) * 4
     f = lib.sk_lstsq_qr_f32
     A, B, X, Wp = (ctypes.addressof(t) for t in (SA, Sb, x, ws))
     assert f(A, d, d + 1, d + 1, B, X, Wp, nb, None) == b.SK_ERR_SHAPE      # n > d

@@ -203,6 +203,42 @@ def test_lstsq_qr_exact_triangular(d, n):
     assert np.array_equal(x.cpu().numpy().astype(np.float64), x0)
 
 
+@pytest.mark.parametrize("d,n", [(512, 256), (100, 37)])
+def test_lstsq_qr_power_of_two_scaling(d, n):
+    """The solver scales every column of [SA | Sb] by a power of two before
+    the QR and x back after it, and Householder QR commutes exactly with such
+    scalings: with SA's columns scaled by 2^k_j and Sb by 2^kb, x_j comes out
+    as x0_j 2^(kb - k_j) bit for bit (x0: the unscaled system's solution);
+    with everything scaled by 2^90 or 2^-90, where the squared entries
+    overflow or underflow in FP32, x0 itself, bit for bit, and x0 is within
+    the oracle's bar."""
+    from sparse_sketching_amd import binding as b
+    say(f"lstsq power-of-two scaling d={d} n={n}")
+    g = np.random.default_rng(d + 5 * n)
+    M = g.standard_normal((d, n)).astype(np.float32)
+    y = g.standard_normal(d).astype(np.float32)
+    assert np.abs(M).min() > 2.0**-30 and np.abs(y).min() > 2.0**-30   # scaled copies stay normal
+    x0 = b.lstsq_qr(to_dev(M), to_dev(y))
+    sync()
+    x0 = x0.cpu().numpy()
+    ref = oracle.lstsq_qr(M, y)
+    assert np.linalg.norm(x0 - ref) <= 5e-5 * np.linalg.norm(ref)
+    k = g.integers(-40, 41, size=n)
+    kb = 17
+    Mk = np.ldexp(M, k[None, :]).astype(np.float32)
+    xk = b.lstsq_qr(to_dev(Mk), to_dev(np.ldexp(y, kb).astype(np.float32)))
+    sync()
+    assert np.array_equal(xk.cpu().numpy(), np.ldexp(x0, kb - k).astype(np.float32))
+    for e in (90, -90):
+        Me = np.ldexp(M, e).astype(np.float32)
+        sq = Me.astype(np.float32) * Me.astype(np.float32)
+        # the test can fail: unscaled, the column norms overflow (underflow)
+        assert np.isinf(sq).any() if e > 0 else (sq == 0).all()
+        xe = b.lstsq_qr(to_dev(Me), to_dev(np.ldexp(y, e).astype(np.float32)))
+        sync()
+        assert np.array_equal(xe.cpu().numpy(), x0), e
+
+
 def test_lstsq_qr_matches_sketch_solve_route():
     """The library's solver on a real sketch (the FP32 fused sketch of a 2^16
     x 128 system, d = 256): same residual as the oracle's FP32 QR of the same
