@@ -435,10 +435,12 @@ template <int PB> struct TrailShape {
 // a <- a - V u, u = T^T (V^T a) = T^T w, by forward substitution in G:
 // u_i = tau_i (w_i - sum_{q<i} G[q][i] u_q) (T^-1 = diag(1/tau) +
 // strictly-upper(G) for the forward recurrence; this form also holds for
-// tau_i = 0).  Wavefront w of block b takes columns p0 + PB + 8 b + 2 w and
-// the next; V (unit lower trapezoid) from W.
+// tau_i = 0).  Wavefront w of block b takes columns p0 + PB + 2 (kTrailWaves b
+// + w) and the next; V (unit lower trapezoid) from W.
+constexpr int kTrailWaves = 8;                  // 512 threads: V staged in one round of loads
+                                                // for up to 512 panel rows
 template <int PB>
-__global__ __launch_bounds__(256) void k_qr_trail(const QrArgs args, int p0) {
+__global__ __launch_bounds__(kTrailWaves * 64) void k_qr_trail(const QrArgs args, int p0) {
     constexpr int LS = TrailShape<PB>::LS, RT = TrailShape<PB>::RT, NQ = (PB + 3) / 4;
     constexpr int SH = 6 - ilog2(PB);               // lane l holds dot product l >> SH
     __shared__ __align__(16) float V[kQrTrailFloats];
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(256) void k_qr_trail(const QrArgs args, int p0) {
     float *const W = args.W;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int dp = d - p0;
-    const int k0 = p0 + PB + (blockIdx.x * 4 + wave) * 2;
+    const int k0 = p0 + PB + (blockIdx.x * kTrailWaves + wave) * 2;
     const bool live = k0 <= n, two = k0 < n;
     float *const a0 = W + (int64_t)k0 * d + p0;
     float *const a1 = a0 + d;                       // column k0 + 1 when two
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(256) void k_qr_trail(const QrArgs args, int p0) {
         tq[q] = args.G[q * (kQrMaxNb + 1)];
     }
     constexpr int CW = PB < 4 ? 4 : PB;             // columns written (zero padding read)
-    for (int r0 = 0; r0 < dp; r0 += 256) {
+    for (int r0 = 0; r0 < dp; r0 += kTrailWaves * 64) {
         const int r = r0 + tid;
         float t[CW];
 #pragma unroll
@@ -624,8 +626,8 @@ hipError_t qr_panel_step(const QrArgs &a, int p0, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ntrail = a.n + 1 - (p0 + PB);         // columns after the panel, rhs included
-    const int blocks = (ntrail + 7) / 8;
-    k_qr_trail<PB><<<dim3(blocks), dim3(256), 0, s>>>(a, p0);
+    const int blocks = (ntrail + 2 * kTrailWaves - 1) / (2 * kTrailWaves);
+    k_qr_trail<PB><<<dim3(blocks), dim3(kTrailWaves * 64), 0, s>>>(a, p0);
     return hipGetLastError();
 }
 
