@@ -52,10 +52,14 @@ HEADLINE_KERNELS = ("k_stack_fused<AccF16,2,128,32,1,false,false>",
                     "k_stack_reduce<AccF16,false>")
 # HBM bytes one complete fused FP16 step moves, from rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE passes over bench.py --profile-pass (KiB per
-# dispatch; FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a 1 GiB device
-# copy reads on the same counters).  Valid for the kernels named here only;
-# None until the counters are taken on these kernels.
-TRAFFIC = None
+# dispatch, averaged over the pass's three calls; FETCH_SIZE x 2.0 and
+# WRITE_SIZE x 1.0, the factors a 1 GiB device copy reads on the same
+# counters: 524,305 KiB fetched and 1,048,576 KiB written per GiB).  Valid for
+# the kernels named here only (the summary under profiles/ gives the commands).
+TRAFFIC = {"kernels": HEADLINE_KERNELS,
+           "fetch_kib": [524681, 32801],     # fused kernel (A once), reduce (partials)
+           "write_kib": [65536, 256],        # fused kernel (partials), reduce (sketch)
+           "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def sparsestack_bytes(m, n, d, zeta, out_elem):
