@@ -34,7 +34,11 @@
  *     sketching page §V-A); with SK_ACCUMULATE it computes B += S A, so a
  *     matrix can be sketched in row chunks (see sk_meta_generate).
  *   - A and B must not overlap (SK_ERR_ARG).
- *   - Calls are reentrant and hold no state between calls.
+ *   - Calls are reentrant.  The library keeps two kinds of state across
+ *     calls: a per-device cache of device properties (compute-unit count
+ *     and LDS size, filled on first use and read-only afterwards), and the
+ *     per-device static scratch of sk_sketch_f16acc_noalloc (calls of it
+ *     that overlap on one device race on that scratch).
  */
 #ifndef SK_SKETCH_H
 #define SK_SKETCH_H
