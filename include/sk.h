@@ -417,6 +417,30 @@ sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_
                                  int32_t max_lds, int64_t *out);
 
 /*
+ * sk_sketch_plan_describe: the launch plan of sk_sketch_f32 /
+ * sk_sketch_f16acc for the given sizes (arguments as for
+ * sk_fused_plan_describe).  Narrow rows take the owner kernel where it
+ * covers them (rows of at most 32 words: FP16 of at most 64 columns, FP32 of
+ * at most 32; rows of 64 words with d <= 128): lanes own output rows, and
+ * each stage's hits are counting-sorted into per-row lists walked in
+ * ascending row order (the same order of additions as the register kernel);
+ * other shapes take the register kernel sk_fused_plan_describe reports.  Pure host
+ * computation, for tests and tools.
+ *   out  int64[SK_SKETCH_PLAN_FIELDS], written: {kernel (0: the fallback,
+ *        1: register kernel, 2: owner kernel), words per lane, lanes per
+ *        output row (owner), threads per workgroup, a row's words padded to
+ *        a power of two (owner), input rows per stage, list capacity per
+ *        output row and stage (owner), words per lane load (owner), rows per
+ *        chunk, chunks, workgroups, workspace bytes, dynamic LDS bytes per
+ *        workgroup (owner), workgroups per CU the plan is sized for}.
+ * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ARG (precision, num_cu, max_lds).
+ */
+#define SK_SKETCH_PLAN_FIELDS 14
+sk_status sk_sketch_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
+                                  int32_t a_align, int32_t d, int32_t zeta, int32_t num_cu,
+                                  int32_t max_lds, int64_t *out);
+
+/*
  * sk_apply_blockperm: Y = S A (or Y += S A) for S ~ BlockPerm-SJLT.
  * (FlashSketch page §4: input rows in M contiguous blocks of B_c = m/M,
  * output rows in M blocks of B_r = d/M; output block g reads the kappa input

@@ -166,7 +166,8 @@ def _accumulate_flat(A, row_idx, val, d, zeta, e0, e1):
     return B
 
 
-def sketch_f16_rn_emul(A, row_idx, val, d, zeta, chunk_rows=None, combine="f16", B0=None):
+def sketch_f16_rn_emul(A, row_idx, val, d, zeta, chunk_rows=None, combine="f16", B0=None,
+                       groups=None):
     """FP16-accumulated sketch with per-contribution RN conversion.
 
     chunk_rows=None: every output entry adds its contributions one at a
@@ -183,6 +184,13 @@ def sketch_f16_rn_emul(A, row_idx, val, d, zeta, chunk_rows=None, combine="f16",
     B0 (float16 d x n): the sum starts from B0 instead of +0 (a sketch
     accumulated onto an existing one); with combine="f32" B0 is the first
     term of the FP32 sum.
+    groups=G (with chunk_rows): the P chunk partials are combined in G
+    contiguous groups, group w holding chunks [w*P//G, (w+1)*P//G); each
+    group is summed from +0 in chunk order, and the non-empty group sums are
+    added in group order onto B0 or +0 (FP16 RN additions throughout, or,
+    with combine="f32", FP32 additions and one rounding of the total).
+    This is one more fixed order of the same FP16 RN additions; groups=None
+    adds the chunk partials one after another.
     """
     m = A.shape[0]
     if combine not in ("f16", "f32"):
@@ -194,6 +202,27 @@ def sketch_f16_rn_emul(A, row_idx, val, d, zeta, chunk_rows=None, combine="f16",
              for r0 in range(0, m, chunk_rows)]
     start = np.zeros((d, A.shape[1]), dtype=np.float16) if B0 is None else \
         np.asarray(B0, dtype=np.float16)
+    if groups is not None:
+        P = len(parts)
+        spans = [(w * P // groups, (w + 1) * P // groups) for w in range(groups)]
+        if combine == "f16":
+            B = start
+            for lo, hi in spans:
+                if hi > lo:
+                    q = np.zeros_like(start)
+                    for part in parts[lo:hi]:
+                        q = rn_f16_add(q, part)
+                    B = rn_f16_add(B, q)
+            return B
+        acc = start.astype(np.float32)
+        with np.errstate(over="ignore", invalid="ignore"):
+            for lo, hi in spans:
+                if hi > lo:
+                    q = np.zeros(start.shape, dtype=np.float32)
+                    for part in parts[lo:hi]:
+                        q = q + part.astype(np.float32)
+                    acc = acc + q
+            return acc.astype(np.float16)
     if combine == "f16":
         B = start
         for P in parts:

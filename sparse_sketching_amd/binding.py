@@ -79,6 +79,9 @@ _SIGNATURES = {
     "sk_fused_plan_describe": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int64,
                                           _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
                                           _c.c_int32, _c.POINTER(_c.c_int64)]),
+    "sk_sketch_plan_describe": (_c.c_int, [_c.c_int32, _c.c_int64, _c.c_int32, _c.c_int64,
+                                          _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
+                                          _c.c_int32, _c.POINTER(_c.c_int64)]),
     "sk_apply_lowp": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int32, _c.c_int64, _c.c_void_p,
                                  _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int64,
                                  _c.c_int32, _c.c_int32, _c.c_uint64, _c.c_int64, _c.c_uint32,
@@ -341,6 +344,19 @@ def sk_sketch_workspace_size(precision, m, n, d, zeta):
 
 FUSED_PLAN_FIELDS = ("fused", "rows_per_wave", "groups", "slices", "rows_per_chunk", "chunks",
                      "grid", "ws_bytes", "words", "stage_rows", "per_cu")
+
+
+SKETCH_PLAN_FIELDS = ("kernel", "words", "lanes_per_row", "threads", "row_words", "stage_rows",
+                      "cap", "load_words", "rows_per_chunk", "chunks", "grid", "ws_bytes",
+                      "lds_bytes", "per_cu")
+
+
+def sk_sketch_plan_describe(precision, m, n, lda, a_align, d, zeta, num_cu, max_lds):
+    """The complete sketch's launch plan as a dict (host computation)."""
+    out = (ctypes.c_int64 * len(SKETCH_PLAN_FIELDS))()
+    _check("sk_sketch_plan_describe", load().sk_sketch_plan_describe(
+        precision, m, n, lda, int(a_align), d, zeta, num_cu, max_lds, out))
+    return dict(zip(SKETCH_PLAN_FIELDS, list(out)))
 
 
 def sk_fused_plan_describe(precision, m, n, lda, a_align, d, zeta, num_cu, max_lds):

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsksketch.so")
 SOURCES = ["capi.hip", "meta.hip", "apply_f32.hip", "apply_f16.hip", "apply_stack.hip",
-           "fused.hip", "apply_lowp.hip",
+           "fused.hip", "fused_owner.hip", "apply_lowp.hip",
            "blockperm_general.hip", "blockperm_regs.hip", "blockperm_direct.hip", "lstsq.hip"]
 ARCH = "gfx950"
 

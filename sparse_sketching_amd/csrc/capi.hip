@@ -297,7 +297,15 @@ size_t sketch_ws_bytes(const sk::DevInfo &di, bool f16, int64_t m, int32_t n, in
     if (m == 0) return 0;
     size_t need = fallback_ws_bytes(di, f16, m, n, d, zeta);
     const size_t fused = fused_ws_bytes(di, f16, m, n, d, zeta);
-    return fused > need ? fused : need;
+    if (fused > need) need = fused;
+    // the owner kernel's plan (its load width follows lda and the alignment)
+    for (int a = 4; a <= 16; a *= 2)
+        for (int64_t lda = n; lda <= n + 1; ++lda) {
+            sk::FusedPlan fp{};
+            if (sk::plan_owner(di, f16, m, n, lda, a, d, zeta, &fp) && fp.ws_bytes > need)
+                need = fp.ws_bytes;
+        }
+    return need;
 }
 
 constexpr int kMaxScratchDevices = 64;
@@ -364,20 +372,20 @@ sk_status sketch_dispatch(bool f16, uint64_t seed, int64_t row_offset, const flo
     const float scale = scale_of(zeta);
     sk::FusedPlan fp{};
     if (use_static) {
-        if (!sk::plan_fused(di, f16, m, n, lda, base_align(A), d, zeta, &fp) ||
+        if (!sk::plan_sketch(di, f16, m, n, lda, base_align(A), d, zeta, &fp) ||
             fp.ws_bytes > kStaticScratchBytes)
             return SK_ERR_UNSUPPORTED;
         uint32_t *ws = nullptr;
         const sk_status st = static_scratch(&ws);
         if (st != SK_OK) return st;
-        return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, nullptr,
-                                           nullptr, d, zeta, scale, B, ldb, ws, mode, s));
+        return hip_status(sk::launch_sketch(fp, f16, A, m, n, lda, seed, row_offset, d, zeta,
+                                            scale, B, ldb, ws, mode, s));
     }
     if (workspace_bytes < sketch_ws_bytes(di, f16, m, n, d, zeta)) return SK_ERR_ARG;
-    if (sk::plan_fused(di, f16, m, n, lda, base_align(A), d, zeta, &fp))
-        return hip_status(sk::launch_fused(fp, f16, A, m, n, lda, seed, row_offset, nullptr,
-                                           nullptr, d, zeta, scale, B, ldb,
-                                           static_cast<uint32_t *>(workspace), mode, s));
+    if (sk::plan_sketch(di, f16, m, n, lda, base_align(A), d, zeta, &fp))
+        return hip_status(sk::launch_sketch(fp, f16, A, m, n, lda, seed, row_offset, d, zeta,
+                                            scale, B, ldb, static_cast<uint32_t *>(workspace),
+                                            mode, s));
     // not covered by the fused kernel: metadata into the workspace, then
     // the LDS (or flat) apply with the rest of it
     char *w = static_cast<char *>(workspace);
@@ -844,6 +852,39 @@ sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_
                                              (int64_t)p.ws_bytes, p.words, p.stage_rows,
                                              p.dual ? 2 : 1};
     for (int i = 0; i < SK_FUSED_PLAN_FIELDS; ++i) out[i] = v[i];
+    return SK_OK;
+}
+
+sk_status sk_sketch_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
+                                  int32_t a_align, int32_t d, int32_t zeta, int32_t num_cu,
+                                  int32_t max_lds, int64_t *out) {
+    if (out == nullptr) return SK_ERR_NULL;
+    for (int i = 0; i < SK_SKETCH_PLAN_FIELDS; ++i) out[i] = 0;
+    if (precision != SK_PRECISION_F32 && precision != SK_PRECISION_F16ACC) return SK_ERR_ARG;
+    if (m < 1 || n < 1 || d < 1 || zeta < 1 || zeta > d || d % zeta != 0 || lda < n)
+        return SK_ERR_SHAPE;
+    if (precision == SK_PRECISION_F16ACC && n % 2 != 0) return SK_ERR_SHAPE;
+    if (num_cu < 1 || max_lds < 1) return SK_ERR_ARG;
+    sk::DevInfo di{num_cu, max_lds};
+    sk::FusedPlan p{};
+    if (!sk::plan_sketch(di, precision == SK_PRECISION_F16ACC, m, n, lda, a_align, d, zeta, &p))
+        return SK_OK;
+    const bool own = p.kind == sk::kFusedOwner;
+    const int64_t v[SK_SKETCH_PLAN_FIELDS] = {own ? 2 : 1,
+                                              p.words,
+                                              own ? p.lanes_per_row : 0,
+                                              own ? p.threads : 1024,
+                                              own ? p.row_words : 0,
+                                              p.stage_rows,
+                                              own ? p.cap : 0,
+                                              own ? p.load_words : 0,
+                                              p.rows_per_chunk,
+                                              p.chunks,
+                                              p.grid,
+                                              (int64_t)p.ws_bytes,
+                                              own ? (int64_t)p.lds_bytes : 0,
+                                              p.dual ? 2 : 1};
+    for (int i = 0; i < SK_SKETCH_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }
 

@@ -495,6 +495,8 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     // FP16 W = 1, R <= 32; FP32 W = 2, R <= 16 (all fit 64 VGPRs)
     const bool dual = W <= 2 && W * R + 4 * K <= 40 && di.max_lds >= 2 * kFusedDualLdsBytes;
     if (W == 1 && !dual && R != 64) return false;   // W = 1, one per CU: R = 64 only
+    *p = FusedPlan{};
+    p->kind = kFusedRegister;
     p->words = W;
     p->dual = dual ? 1 : 0;
     p->stage_rows = (W == 2 && !dual) ? 128 : 64;
@@ -518,10 +520,41 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     return true;
 }
 
+// Narrow rows go to the owner kernel where it covers them: rows of at most
+// 32 words (FP16 up to 64 columns, FP32 up to 32), and rows of 64 words
+// (FP16 128 columns, FP32 64) at no more than 8 words per lane (d <= 128).
+// Measured on MI355X (2^20 rows unless noted, complete sketch): FP16
+// 2 columns, d = 512: 36-42 us against 144 in the register kernel; FP16 64
+// columns, 4,194,304 rows, d = 128: 231-235 us against 341; FP32 64 columns
+// there: 244-249 us against 330; FP16 32 columns, d = 1024: 116 us against
+// 181; but FP32 64 columns at d = 256 (16 words per lane): 161 us against
+// 139, and FP16 128 columns at d = 256: 144-169 us against 99-144.
+bool plan_sketch(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
+                 int32_t d, int32_t zeta, FusedPlan *p) {
+    FusedPlan q{};
+    if (plan_owner(di, f16, m, n, lda, a_align, d, zeta, &q) && (q.row_words <= 32 || q.words <= 8)) {
+        *p = q;
+        return true;
+    }
+    return plan_fused(di, f16, m, n, lda, a_align, d, zeta, p);
+}
+
+hipError_t launch_sketch(const FusedPlan &p, bool f16, const float *A, int64_t m, int32_t n,
+                         int64_t lda, uint64_t seed, int64_t row_offset, int32_t d, int32_t zeta,
+                         float scale, void *B, int64_t ldb, uint32_t *ws, int mode,
+                         hipStream_t s) {
+    if (p.kind == kFusedOwner)
+        return launch_owner(p, f16, A, m, n, lda, seed, row_offset, d, zeta, scale, B, ldb, ws,
+                            mode, s);
+    return launch_fused(p, f16, A, m, n, lda, seed, row_offset, nullptr, nullptr, d, zeta, scale,
+                        B, ldb, ws, mode, s);
+}
+
 hipError_t launch_fused(const FusedPlan &p, bool f16, const float *A, int64_t m, int32_t n,
                         int64_t lda, uint64_t seed, int64_t row_offset, const int32_t *row_idx,
                         const float *val, int32_t d, int32_t zeta, float scale, void *B,
                         int64_t ldb, uint32_t *ws, int mode, hipStream_t s) {
+    if (p.kind != kFusedRegister) return hipErrorInvalidValue;
     FusedArgs a{};
     a.A = A;
     a.ws = ws;

@@ -125,8 +125,14 @@ struct FusedArgs {
     int32_t chunks, slices, groups;
     float scale;                // float32(1/sqrt(zeta))
 };
+// The two fused kernels: output rows in wavefront registers over column
+// slices (fused.hip), or output rows owned by lanes (fused_owner.hip).
+constexpr int kFusedRegister = 0;
+constexpr int kFusedOwner = 1;
 struct FusedPlan {
-    int words;                  // W: partial words per lane and output row (1, 2 or 4)
+    int kind;                   // kFusedRegister or kFusedOwner
+    int words;                  // W: partial words per lane and output row (1, 2 or 4;
+                                // owner kernel: V, 1 to 64)
     int dual;                   // 1: the two-workgroups-per-CU shape
     int stage_rows;             // input rows per LDS stage (128 at W = 2 one per CU,
                                 // 64 otherwise)
@@ -139,6 +145,13 @@ struct FusedPlan {
     int64_t chunks;
     int64_t grid;               // workgroups (1-D, XCD-grouped)
     size_t ws_bytes;            // partial workspace
+    // owner kernel only
+    int threads;                // per workgroup: d x lanes_per_row
+    int row_words;              // U: a row's words padded to a power of two
+    int lanes_per_row;          // L = U / V
+    int cap;                    // hits per output row and stage a list holds
+    int load_words;             // words per lane load (1, 2 or 4)
+    size_t lds_bytes;           // dynamic LDS per workgroup
 };
 // a_align: the alignment of A's base in bytes (16 or more: any lane load;
 // the kernel needs 16 for FP16 and for W = 4, 8 for FP32 at W = 2).  A plan
@@ -151,6 +164,23 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
 // row_idx / val NULL: the metadata is drawn from (seed, row_offset) in the
 // kernel; else it is read from them (the stored-metadata apply; seed and
 // row_offset unused) and scale must be float32(1/sqrt(zeta)).
+// The owner kernel's plan (false: it does not cover the shape) and launch
+// (then the reduce, as launch_fused); drawn metadata only.
+bool plan_owner(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
+                int32_t d, int32_t zeta, FusedPlan *plan);
+hipError_t launch_owner(const FusedPlan &plan, bool f16, const float *A, int64_t m, int32_t n,
+                        int64_t lda, uint64_t seed, int64_t row_offset, int32_t d, int32_t zeta,
+                        float scale, void *B, int64_t ldb, uint32_t *ws, int mode,
+                        hipStream_t stream);
+// The plan of the complete fused sketch (metadata drawn in the kernel): the
+// owner kernel for narrow rows where it covers the shape, else the register
+// kernel; launch_sketch runs either.
+bool plan_sketch(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
+                 int32_t d, int32_t zeta, FusedPlan *plan);
+hipError_t launch_sketch(const FusedPlan &plan, bool f16, const float *A, int64_t m, int32_t n,
+                         int64_t lda, uint64_t seed, int64_t row_offset, int32_t d, int32_t zeta,
+                         float scale, void *B, int64_t ldb, uint32_t *ws, int mode,
+                         hipStream_t stream);
 hipError_t launch_fused(const FusedPlan &plan, bool f16, const float *A, int64_t m, int32_t n,
                         int64_t lda, uint64_t seed, int64_t row_offset, const int32_t *row_idx,
                         const float *val, int32_t d, int32_t zeta, float scale, void *B,

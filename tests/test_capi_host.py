@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol(lib):
                           "sk_apply_f32_ws", "sk_apply_f16acc_ws", "sk_apply_workspace_size", "sk_lds_plan_describe",
                           "sk_sketch_f32", "sk_sketch_f16acc", "sk_sketch_workspace_size",
                           "sk_sketch_f16acc_noalloc",
-                          "sk_fused_plan_describe", "sk_apply_lowp", "sk_apply_blockperm",
+                          "sk_fused_plan_describe", "sk_sketch_plan_describe", "sk_apply_lowp",
+                          "sk_apply_blockperm",
                           "sk_apply_blockperm_ex", "sk_blockperm_workspace_size",
                           "sk_blockperm_plan_describe", "sk_lstsq_qr_f32",
                           "sk_lstsq_workspace_size", "sk_status_string"}
@@ -396,6 +397,120 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
     assert len(seen) == p["slices"] * p["chunks"] * g
     # the fused kernel's metadata stage holds at most 16 blocks
     assert zeta <= 16
+
+
+OWNER_SHAPES = FUSED_SHAPES + [
+    (1 << 20, 2, 512, 4), (1 << 20, 2, 256, 8), (4194304, 64, 128, 4), (1 << 20, 32, 1024, 1),
+    (1 << 20, 64, 256, 16), (1 << 16, 4, 64, 1), (777, 6, 48, 3), (5000, 62, 40, 8),
+    (64, 64, 128, 4), (1, 2, 64, 4), (1 << 20, 16, 4096, 4), (3000, 2, 16, 16),
+]
+
+
+@pytest.mark.parametrize("precision", [b.SK_PRECISION_F32, b.SK_PRECISION_F16ACC])
+@pytest.mark.parametrize("m,n,d,zeta", OWNER_SHAPES)
+@pytest.mark.parametrize("lda_extra,align", [(0, 16), (1, 4), (2, 8)])
+def test_sketch_plan_fits_owner_kernel(lib, precision, m, n, d, zeta, lda_extra, align):
+    """Replays the owner kernel's indexing on its plan: the workgroup's
+    threads are whole wavefronts and cover d output rows x L lanes, each
+    lane's V words of a padded row lie inside it, every stage load reads
+    inside its row with the load's alignment, the LDS carve (two stage
+    buffers, two mask sets, two entry sets, the lists) fits, list reads of 4
+    entries stay inside an output row's list, a stage row index fits the
+    list entry's 15 bits, and every partial store stays inside the
+    workspace.  Shapes the owner kernel does not take report the register
+    kernel or the fallback."""
+    f16 = precision == b.SK_PRECISION_F16ACC
+    if f16 and n % 2:
+        pytest.skip("odd n")
+    lda = n + lda_extra * (2 if f16 else 1)
+    p = b.sk_sketch_plan_describe(precision, m, n, lda, align, d, zeta, **MI355X)
+    kc = 2 if f16 else 1
+    nw = n // kc
+    U = 1 << (nw - 1).bit_length()
+    if p["kernel"] != 2:
+        # rows the owner kernel leaves: 64 words at more than 8 per lane,
+        # wider than its 16 words per lane allow at this d, a d its
+        # workgroup cannot tile, or zeta > 16
+        if U <= 64 and p["kernel"] != 0:
+            kmax = 2 if f16 else 4
+            kw = kmax if (nw % kmax == 0 and U % kmax == 0 and lda % (kmax * kc) == 0
+                          and align >= kmax * kc * 4) else 1
+            V = 1
+            while V < U and d * (U // V) > 1024:
+                V *= 2
+            # (a 128-row stage needs more than four loads per thread)
+            assert (U == 64 and d * U > 1024 * 8) or d * U > 1024 * 16 or zeta > 16 or \
+                d % zeta or (d * U) % 64 or (lda % kc) or align < 4 * kc or \
+                128 * U > 4 * kw * d * (U // V)
+        return
+    assert U <= 32 or d * U <= 1024 * 8
+    V, L, NT, U = p["words"], p["lanes_per_row"], p["threads"], p["row_words"]
+    S, cap, kw = p["stage_rows"], p["cap"], p["load_words"]
+    assert U >= nw and U & (U - 1) == 0 and U <= 64 and V * L == U and V <= 16
+    assert NT == d * L and NT % 64 == 0 and NT <= 1024
+    assert S % 128 == 0 and S <= 512 and cap % 4 == 0 and 4 <= cap <= S
+    # list entries hold a row's word offset in 15 bits (the -0 row's included)
+    assert S * U < 1 << 15
+    # loads: kw words = kw * kc floats, at most four per thread and stage
+    assert kw in (1, 2, 4) and U % kw == 0 and nw % kw == 0
+    fl = kw * kc
+    assert lda % fl == 0 and align >= 4 * fl
+    nload = -(-(S * U // kw) // NT)
+    assert nload <= 4
+    lpr = U // kw
+    for tid in (0, 1, NT // 2, NT - 1):
+        for i in range(nload):
+            q = tid + i * NT
+            row, w0 = q // lpr, (q % lpr) * kw
+            if row < S and w0 < nw:
+                assert w0 * kc + fl <= n                 # inside the row
+                assert (w0 * kc) % fl == 0                # aligned
+    # LDS carve in words: two stage buffers of S + 1 rows (row S: the -0
+    # row), padding to 16 bytes, 4 trash words, two mask sets (per output
+    # row MW mask words and 4 count words: a byte per 64 stage rows, at most
+    # 8), two entry sets, the lists
+    MW = S // 32
+    assert S // 64 <= 8
+    bufs = 2 * (S + 1) * U
+    trash = bufs + (bufs & 2)
+    masks = trash + 4
+    ents = masks + 2 * d * (MW + 4)
+    lists = ents + 2 * zeta * S
+    words = lists + d * (cap + 4)
+    assert 4 * words == p["lds_bytes"] <= MI355X["max_lds"]
+    assert p["per_cu"] in (1, 2) and p["per_cu"] * p["lds_bytes"] <= MI355X["max_lds"]
+    assert trash % 4 == 0 and masks % 4 == 0 and ents % 4 == 0 and lists % 4 == 0
+    assert MW % 4 == 0 and (S + 1) * U % kw == 0      # the second buffer's stores stay aligned
+    # chunks of whole stages cover m; one workgroup per chunk
+    rpc = p["rows_per_chunk"]
+    assert rpc % S == 0 and p["chunks"] * rpc >= m > (p["chunks"] - 1) * rpc
+    assert p["grid"] == p["chunks"] <= 65535
+    # partial stores: lane (o, g) writes words [g*V, g*V + V) of row o
+    for tid in (0, NT - 1):
+        o, g = tid // L, tid % L
+        last = ((p["chunks"] - 1) * d + o) * U + g * V + V
+        assert o < d and last * 4 <= p["ws_bytes"]
+    assert p["ws_bytes"] == p["chunks"] * d * U * 4
+
+
+def test_sketch_plan_kernel_choice(lib):
+    """Narrow rows take the owner kernel (the m x 2 right-hand side of
+    sketch-and-solve, the 64-column range workload), wider ones the
+    register kernel."""
+    P16, P32 = b.SK_PRECISION_F16ACC, b.SK_PRECISION_F32
+    q = b.sk_sketch_plan_describe(P16, 1 << 20, 2, 2, 16, 512, 4, **MI355X)
+    assert (q["kernel"], q["words"], q["lanes_per_row"], q["threads"]) == (2, 1, 1, 512)
+    q = b.sk_sketch_plan_describe(P16, 4194304, 64, 64, 16, 128, 4, **MI355X)
+    assert (q["kernel"], q["words"], q["lanes_per_row"], q["threads"], q["row_words"]) == \
+        (2, 4, 8, 1024, 32)
+    assert b.sk_sketch_plan_describe(P16, 1 << 20, 256, 256, 16, 512, 4, **MI355X)["kernel"] == 1
+    assert b.sk_sketch_plan_describe(P32, 1 << 20, 256, 256, 16, 512, 4, **MI355X)["kernel"] == 1
+    # 64-word rows: the owner kernel at d = 128 (8 words per lane), the
+    # register kernel from d = 256
+    q = b.sk_sketch_plan_describe(P32, 4194304, 64, 64, 16, 128, 4, **MI355X)
+    assert (q["kernel"], q["words"], q["lanes_per_row"]) == (2, 8, 8)
+    for prec, n in ((P32, 64), (P16, 128)):
+        assert b.sk_sketch_plan_describe(prec, 1 << 20, n, n, 16, 256, 8, **MI355X)["kernel"] == 1
 
 
 def test_fused_plan_word_width(lib):

@@ -5,11 +5,12 @@ page App. F.1).
 The oracle forms its own fp64 sketch from its own metadata and solves it;
 the GPU pipeline sketches with the fused kernels and solves with FP32 QR.
 Bars: FP32-sketch residuals within 1e-4 (relative) of the oracle's; FP16
-residuals (every addition in FP16, the page's arithmetic) between the FP32
-residual and the one of the oracle's RN emulation of the page's flat
-(single running sum) order, and close to the oracle's two-level emulation;
-with the FP32 combine of the FP16 chunk partials (SK_COMBINE_F32) within 1%
-of the FP32 residual.  The FP16 residual increase is the FP16 accumulation
+residuals (every addition in FP16, the page's arithmetic), with the FP16 or
+the FP32 combine of the chunk partials (SK_COMBINE_F32), within 1e-4 of the
+residual of the oracle's RN emulation of the library's own order (each
+sketch's plan chunks, the reduce's four groups: the sketches agree bit for
+bit, the QR is FP32 against the oracle's fp64), and no worse than the
+page's flat (single running sum) order.  The FP16 residual increase is the FP16 accumulation
 of b's sketch itself: the noise (0.1) is small next to ||Ax0||, so the
 accumulation error of Sb is large next to the residual (the oracle's flat
 emulation gives +18% on the low-coherence system and +131% on the coherent
@@ -20,6 +21,7 @@ import pytest
 import torch
 
 import oracle
+from sparse_sketching_amd import binding as b
 from sparse_sketching_amd import inputs
 from sparse_sketching_amd import solve
 from tests.gpuutil import dev, say, sync, to_dev
@@ -43,16 +45,28 @@ def oracle_residual(A, rhs, d, zeta, seed):
     return oracle.residual(A, x, rhs), x
 
 
-def oracle_f16_residual(A, rhs, d, zeta, seed, chunk_rows):
+def oracle_f16_residual(A, rhs, d, zeta, seed, chunk_rows, chunk_rows_b=None, groups=None,
+                        combine="f16"):
     """Residual of the solve on the oracle's RN-emulated FP16 sketches of A
-    and [b 0] (FP32 QR), for the flat order (chunk_rows=None) or row chunks
-    combined with FP16 additions."""
+    and [b 0], for the flat order (chunk_rows=None) or row chunks (of
+    chunk_rows rows for A, chunk_rows_b for [b 0]) combined with FP16
+    additions, one after another or in `groups` groups (or, combine="f32",
+    in FP32 rounded once)."""
     ri, v = oracle.meta_ref(seed, A.shape[0], d, zeta)
     B2 = np.zeros((A.shape[0], 2), dtype=np.float32)
     B2[:, 0] = rhs
-    SA = oracle.sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=chunk_rows).astype(np.float64)
-    Sb = oracle.sketch_f16_rn_emul(B2, ri, v, d, zeta, chunk_rows=chunk_rows)[:, 0]
+    cb = chunk_rows if chunk_rows_b is None else chunk_rows_b
+    SA = oracle.sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=chunk_rows, groups=groups,
+                                   combine=combine).astype(np.float64)
+    Sb = oracle.sketch_f16_rn_emul(B2, ri, v, d, zeta, chunk_rows=cb, groups=groups,
+                                   combine=combine)[:, 0]
     return oracle.residual(A, oracle.sketch_solve(SA, Sb.astype(np.float64)), rhs)
+
+
+def sketch_chunk_rows(m, n, d, zeta):
+    """Rows per chunk of the fused FP16 sketch's plan (MI355X)."""
+    return b.sk_sketch_plan_describe(b.SK_PRECISION_F16ACC, m, n, n, 16, d, zeta,
+                                     num_cu=256, max_lds=160 * 1024)["rows_per_chunk"]
 
 
 @pytest.mark.parametrize("coherent", [False, True])
@@ -68,21 +82,24 @@ def test_sketch_and_solve_matches_oracle(coherent):
     r_ref, _ = oracle_residual(A, rhs, d, zeta, seed)
     r_opt = oracle.residual(A, oracle.reference_solution(A, rhs), rhs)
     r_flat = oracle_f16_residual(A, rhs, d, zeta, seed, None)
-    # the fused kernel's chunks at this size are 128 rows (512 workgroups)
-    r_two = oracle_f16_residual(A, rhs, d, zeta, seed, 128)
+    # the emulation of the library's own order: the fused sketches' chunks
+    # (the register kernel's for A, the owner kernel's for the two-column
+    # [b 0]) and the reduce's four groups
+    ca, cb = sketch_chunk_rows(m, n, d, zeta), sketch_chunk_rows(m, 2, d, zeta)
+    r_emu = oracle_f16_residual(A, rhs, d, zeta, seed, ca, cb, groups=4)
+    r_emu_c = oracle_f16_residual(A, rhs, d, zeta, seed, ca, cb, groups=4, combine="f32")
     say(f"  coherent={coherent}: residual fp32 {r32:.6f} fp16 {r16:.6f} "
         f"fp16+fp32-combine {r16c:.6f} oracle fp64 {r_ref:.6f} oracle fp16 flat {r_flat:.6f} "
-        f"oracle fp16 two-level {r_two:.6f} unsketched {r_opt:.6f}")
+        f"oracle fp16 library order {r_emu:.6f} / {r_emu_c:.6f} unsketched {r_opt:.6f}")
     assert abs(r32 - r_ref) <= 1e-4 * r_ref
     assert r32 >= r_opt * (1 - 1e-6)
-    assert abs(r16c - r32) <= 1e-2 * r32
-    # FP16 accumulation costs residual as the oracle's emulation predicts:
-    # no worse than the page's flat order, and no worse than the sequential
-    # two-level order of the same chunk size (the fused kernel's combine is
-    # a shallower tree of four quarter-sums, measured +17% against the
-    # emulation's +53% on the coherent system)
+    # the FP16 sketches are the emulation's bit for bit; what is left is the
+    # FP32 QR against the oracle's fp64 solve
+    assert abs(r16 - r_emu) <= 1e-4 * r_emu
+    assert abs(r16c - r_emu_c) <= 1e-4 * r_emu_c
+    # FP16 accumulation costs residual, but no more than the page's flat
+    # order
     assert r_ref * (1 - 1e-2) <= r16 <= r_flat * (1 + 1e-2)
-    assert r16 <= r_two * (1 + 5e-2)
 
 
 def test_consistent_system_recovered():

@@ -198,6 +198,78 @@ def _scalar_two_level(A, ri, v, d, zeta, chunk_rows, B0=None):
     return np.array(B)
 
 
+def _scalar_grouped(A, ri, v, d, zeta, chunk_rows, groups, B0=None):
+    """Plain loop with exact rational rounding for the grouped combine:
+    chunk partials as above, then G contiguous groups of them (group w:
+    chunks [w*P//G, (w+1)*P//G)), each summed from +0 in chunk order, and
+    the non-empty group sums added in group order onto B0 or +0; every
+    addition rounded to binary16."""
+    m, n = A.shape
+    parts = []
+    for r0 in range(0, m, chunk_rows):
+        P = [[0.0] * n for _ in range(d)]
+        for e in range(r0 * zeta, min(m, r0 + chunk_rows) * zeta):
+            i = e // zeta
+            for j in range(n):
+                q = float(np.float32(A[i, j]) * np.float32(v[e]))
+                c = rn_binary16_exact(Fraction(q))
+                P[ri[e]][j] = rn_binary16_exact(Fraction(P[ri[e]][j]) + Fraction(c))
+        parts.append(P)
+    B = [[0.0] * n for _ in range(d)] if B0 is None else [list(map(float, r)) for r in B0]
+    npart = len(parts)
+    for w in range(groups):
+        lo, hi = w * npart // groups, (w + 1) * npart // groups
+        if hi == lo:
+            continue
+        Q = [[0.0] * n for _ in range(d)]
+        for P in parts[lo:hi]:
+            for r in range(d):
+                for j in range(n):
+                    Q[r][j] = rn_binary16_exact(Fraction(Q[r][j]) + Fraction(P[r][j]))
+        for r in range(d):
+            for j in range(n):
+                B[r][j] = rn_binary16_exact(Fraction(B[r][j]) + Fraction(Q[r][j]))
+    return np.array(B)
+
+
+@pytest.mark.parametrize("chunk_rows,groups", [(1, 4), (7, 4), (32, 3), (10, 64)])
+def test_grouped_combine_matches_scalar_loop(chunk_rows, groups):
+    """The grouped chunk combine equals a plain loop with exact rounding,
+    from +0 and from an existing sketch B0 (more groups than chunks leave
+    groups empty)."""
+    m, n, d, zeta = 160, 3, 8, 2
+    A = (inputs.gaussian(m, n, seed=15) * np.float32(91.0)).astype(np.float32)
+    ri, v = meta_ref(14, m, d, zeta)
+    got = sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=chunk_rows, groups=groups)
+    assert np.array_equal(got.astype(np.float64),
+                          _scalar_grouped(A, ri, v, d, zeta, chunk_rows, groups))
+    B0 = (inputs.gaussian(d, n, seed=16) * np.float32(300.0)).astype(np.float16)
+    got0 = sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=chunk_rows, groups=groups, B0=B0)
+    assert np.array_equal(got0.astype(np.float64),
+                          _scalar_grouped(A, ri, v, d, zeta, chunk_rows, groups, B0=B0))
+
+
+def test_grouped_combine_association():
+    """One output entry, one-row chunks with partials 2048, 0, 1, 1 (d = 1,
+    zeta = 1, values +1).  Added one after another each +1 is a tie at 2048
+    (spacing 2) and rounds back to 2048; in two groups (2048 + 0) and
+    (1 + 1) = 2 the total is 2048 + 2 = 2050, exact.  Groups of one chunk
+    each, or one group, give the sequential order."""
+    A = np.array([[2048.0], [0.0], [1.0], [1.0]], dtype=np.float32)
+    ri = np.zeros(4, dtype=np.int32)
+    v = np.ones(4, dtype=np.float32)
+    seq = sketch_f16_rn_emul(A, ri, v, 1, 1, chunk_rows=1)
+    assert float(seq[0, 0]) == 2048.0
+    assert float(sketch_f16_rn_emul(A, ri, v, 1, 1, chunk_rows=1, groups=2)[0, 0]) == 2050.0
+    for g in (1, 4, 8):
+        assert float(sketch_f16_rn_emul(A, ri, v, 1, 1, chunk_rows=1, groups=g)[0, 0]) == 2048.0
+    # FP32 combine: (2048 + 0) + (1 + 1) and the sequential FP32 sum are both
+    # exact, 2050 rounded once
+    for g in (None, 2, 4):
+        assert float(sketch_f16_rn_emul(A, ri, v, 1, 1, chunk_rows=1, combine="f32",
+                                        groups=g)[0, 0]) == 2050.0
+
+
 @pytest.mark.parametrize("chunk_rows", [1, 7, 32, 200])
 def test_two_level_matches_scalar_loop(chunk_rows):
     """The chunked (two-level) FP16 order equals a plain loop with exact

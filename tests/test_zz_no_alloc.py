@@ -33,10 +33,12 @@ def _pair(A, d, zeta, seed, flags=0, B0=None, row_offset=0):
 
 
 def test_noalloc_equals_workspace_call_twice_shrinking():
-    """Two calls in a row, the second on a smaller input: each equals the
-    workspace call bit for bit (the second call's reduce reads only what
-    it wrote, whatever the first left in the scratch)."""
-    for (m, n, d, zeta, seed) in ((1 << 20, 256, 512, 4, 1), (70001, 128, 256, 8, 2)):
+    """Calls in a row, each on a smaller input (the last a right-hand side
+    of two columns, which the owner kernel sketches): each equals the
+    workspace call bit for bit (a call's reduce reads only what it wrote,
+    whatever the one before left in the scratch)."""
+    for (m, n, d, zeta, seed) in ((1 << 20, 256, 512, 4, 1), (70001, 128, 256, 8, 2),
+                                  (50000, 2, 512, 4, 3)):
         say(f"noalloc {m}x{n} d={d} zeta={zeta}")
         A = inputs.gaussian_torch(m, n, seed=seed)
         got, want = _pair(A, d, zeta, seed)
@@ -61,18 +63,19 @@ def test_noalloc_flags_and_offsets():
 
 def test_noalloc_refuses_what_it_does_not_cover():
     """Partials beyond the 128 MiB scratch (262144 FP16 columns, d = 512:
-    1024 column slices of 256 KiB) and shapes the fused kernel does not
-    cover (d not a multiple of 16) return SK_ERR_UNSUPPORTED; m = 0 zeroes B."""
+    1024 column slices of 256 KiB) and shapes neither fused kernel covers
+    (256 columns, wider than the owner kernel's rows, with d not a multiple
+    of 16) return SK_ERR_UNSUPPORTED; m = 0 zeroes B."""
     A = torch.zeros((64, 1 << 18), dtype=torch.float32, device=dev())
     B = torch.empty((512, 1 << 18), dtype=torch.float16, device=dev())
     with pytest.raises(b.SketchError) as e:
         b.sk_sketch_f16acc_noalloc(1, 0, A, 64, 1 << 18, 1 << 18, 512, 4, B, 1 << 18, 0)
     assert e.value.status == b.SK_ERR_UNSUPPORTED
     del A, B
-    A = inputs.gaussian_torch(1000, 64, seed=1)
-    B = torch.empty((40, 64), dtype=torch.float16, device=dev())
+    A = inputs.gaussian_torch(1000, 256, seed=1)
+    B = torch.empty((40, 256), dtype=torch.float16, device=dev())
     with pytest.raises(b.SketchError) as e:
-        b.sk_sketch_f16acc_noalloc(1, 0, A, 1000, 64, 64, 40, 4, B, 64, 0)
+        b.sk_sketch_f16acc_noalloc(1, 0, A, 1000, 256, 256, 40, 4, B, 256, 0)
     assert e.value.status == b.SK_ERR_UNSUPPORTED
     B = torch.full((64, 64), 3.0, dtype=torch.float16, device=dev())
     b.sk_sketch_f16acc_noalloc(1, 0, None, 0, 64, 64, 64, 4, B, 64, 0)
