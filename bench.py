@@ -289,7 +289,11 @@ def main():
             wsc = b.sketch_workspace(Ac, 128, 4, "f16acc")
             for _ in range(2):
                 b.sk_sketch_f16acc(SEED, 0, Ac, 4194304, 64, 64, 128, 4, Bc, 64, 0, wsc, 0, sp)
-            del Ac, Bc, wsc
+            B32 = torch.empty((128, 64), dtype=torch.float32, device=dev)
+            ws32c = b.sketch_workspace(Ac, 128, 4, "f32")
+            for _ in range(2):
+                b.sk_sketch_f32(SEED, 0, Ac, 4194304, 64, 64, 128, 4, B32, 64, 0, ws32c, 0, sp)
+            del Ac, Bc, wsc, B32, ws32c
             R2 = torch.zeros((m, 2), dtype=torch.float32, device=dev)
             Bc = torch.empty((d, 2), dtype=torch.float16, device=dev)
             wsc = b.sketch_workspace(R2, d, zeta, "f16acc")
@@ -297,7 +301,8 @@ def main():
                 b.sk_sketch_f16acc(SEED, 0, R2, m, 2, 2, d, zeta, Bc, 2, 0, wsc, 0, sp)
             del R2, Bc, wsc
             done.append("2 x fused f16 sketch of 2^20 x 128 at (zeta, d) = (8, 1024) and "
-                        "(4, 512), of 4,194,304 x 64 at (4, 128), and of 2^20 x 2 at (4, 512)")
+                        "(4, 512), of 4,194,304 x 64 at (4, 128) (and 2 x fused f32), and of "
+                        "2^20 x 2 at (4, 512)")
         if "headline" in legs or "blockperm" in legs:
             del A, ri, val, ws16, ws32, wsr16, wsr32, wsf16, wsf32
             torch.cuda.empty_cache()

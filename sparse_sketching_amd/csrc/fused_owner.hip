@@ -46,6 +46,7 @@ struct OwnerArgs {
     int32_t U, L;               // words per row padded to a power of two; lanes per output row
     int32_t d, zeta;
     int32_t S, cap;             // input rows per stage; list capacity per output row
+    int32_t ms, cs;             // words between output rows' masks, lists
     float scale;                // float32(1/sqrt(zeta))
 };
 
@@ -77,6 +78,15 @@ __device__ __forceinline__ void read_words(const uint32_t *p, uint32_t (&x)[V]) 
     }
 }
 
+// Words between consecutive output rows' mask (or list) words: at least w +
+// 4 (the 4 count words after the mask; for a list, room for a 16-byte read
+// at its last slot); where the LDS allows, an odd number of 16-byte units,
+// so that 16 lanes reading consecutive rows' words at one offset hit 16
+// distinct groups of 4 banks.
+constexpr int owner_row_stride(int w, bool spread) {
+    return (spread && ((w >> 2) & 1)) ? w + 8 : w + 4;
+}
+
 // The sign bits of T's +-1 word (FP16 pair: both halves)
 template <class T> constexpr uint32_t kUnitSign = T::kCols == 2 ? 0x80008000u : 0x80000000u;
 
@@ -92,8 +102,8 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     const int s_log = 31 - __builtin_clz((unsigned)S);
     const int u_log = 31 - __builtin_clz((unsigned)U);
     const int MW = S >> 5;              // mask words per output row (a multiple of 4)
-    const int MS = MW + 4;              // a row's mask words, then its count words
-    const int CS = args.cap + 4;        // list stride in words
+    const int MS = args.ms;             // a row's mask words, then its 4 count words
+    const int CS = args.cs;             // list stride in words
     const uint32_t cap = (uint32_t)args.cap;
     const uint32_t db = (uint32_t)(d / zeta);
     // LDS, in words:
@@ -396,10 +406,10 @@ const void *pick_owner(bool f16, int V, int kw) {
 
 }  // namespace
 
-size_t owner_lds_bytes(int32_t S, int32_t U, int32_t d, int32_t zeta, int32_t cap) {
+size_t owner_lds_bytes(int32_t S, int32_t U, int32_t d, int32_t zeta, int32_t cap, bool spread) {
     const size_t bufs = (size_t)2 * (S + 1) * U;
-    return 4 * (bufs + (bufs & 2) + 4 + (size_t)2 * d * (S / 32 + 4) + (size_t)2 * zeta * S +
-                (size_t)d * (cap + 4));
+    return 4 * (bufs + (bufs & 2) + 4 + (size_t)2 * d * owner_row_stride(S / 32, spread) +
+                (size_t)2 * zeta * S + (size_t)d * owner_row_stride(cap, spread));
 }
 
 // Plan of the owner kernel: FP16 rows of at most 64 column pairs, FP32 rows
@@ -453,10 +463,12 @@ bool plan_owner(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
         if (c > s) c = s;
         return (int32_t)c;
     };
-    while (S > 128 && owner_lds_bytes((int32_t)S, U, d, zeta, cap_for(S)) > (size_t)di.max_lds)
+    while (S > 128 &&
+           owner_lds_bytes((int32_t)S, U, d, zeta, cap_for(S), false) > (size_t)di.max_lds)
         S /= 2;
     const int32_t cap = cap_for(S);
-    const size_t lds = owner_lds_bytes((int32_t)S, U, d, zeta, cap);
+    const bool spread = owner_lds_bytes((int32_t)S, U, d, zeta, cap, true) <= (size_t)di.max_lds;
+    const size_t lds = owner_lds_bytes((int32_t)S, U, d, zeta, cap, spread);
     if (lds > (size_t)di.max_lds) return false;
     const int per_cu = (size_t)di.max_lds >= 2 * lds && NT <= 512 ? 2 : 1;
     const int64_t stages = (m + S - 1) / S;
@@ -479,6 +491,8 @@ bool plan_owner(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     p->row_words = U;
     p->lanes_per_row = L;
     p->cap = cap;
+    p->mask_stride = owner_row_stride((int)S / 32, spread);
+    p->list_stride = owner_row_stride(cap, spread);
     p->load_words = kw;
     p->lds_bytes = lds;
     p->ws_bytes = (size_t)p->chunks * (size_t)d * (size_t)U * 4;
@@ -506,6 +520,8 @@ hipError_t launch_owner(const FusedPlan &p, bool f16, const float *A, int64_t m,
     a.zeta = zeta;
     a.S = p.stage_rows;
     a.cap = p.cap;
+    a.ms = p.mask_stride;
+    a.cs = p.list_stride;
     a.scale = scale;
     const void *kern = pick_owner(f16, p.words, p.load_words);
     if (kern == nullptr) return hipErrorInvalidValue;

@@ -150,6 +150,8 @@ struct FusedPlan {
     int row_words;              // U: a row's words padded to a power of two
     int lanes_per_row;          // L = U / V
     int cap;                    // hits per output row and stage a list holds
+    int mask_stride;            // LDS words between output rows' masks (and counts)
+    int list_stride;            // LDS words between output rows' lists
     int load_words;             // words per lane load (1, 2 or 4)
     size_t lds_bytes;           // dynamic LDS per workgroup
 };

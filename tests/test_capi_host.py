@@ -471,12 +471,19 @@ def test_sketch_plan_fits_owner_kernel(lib, precision, m, n, d, zeta, lda_extra,
     # 8), two entry sets, the lists
     MW = S // 32
     assert S // 64 <= 8
+
+    # row strides: w + 4 words, or (where the LDS allows) the next odd number
+    # of 16-byte units
+    MS, CS = p["mask_stride"], p["list_stride"]
+    spread = MS != MW + 4 or CS != cap + 4 or ((MW // 4) % 2 == 0 and (cap // 4) % 2 == 0)
+    for w, st in ((MW, MS), (cap, CS)):
+        assert st == (w + 8 if spread and (w // 4) % 2 else w + 4)
     bufs = 2 * (S + 1) * U
     trash = bufs + (bufs & 2)
     masks = trash + 4
-    ents = masks + 2 * d * (MW + 4)
+    ents = masks + 2 * d * MS
     lists = ents + 2 * zeta * S
-    words = lists + d * (cap + 4)
+    words = lists + d * CS
     assert 4 * words == p["lds_bytes"] <= MI355X["max_lds"]
     assert p["per_cu"] in (1, 2) and p["per_cu"] * p["lds_bytes"] <= MI355X["max_lds"]
     assert trash % 4 == 0 and masks % 4 == 0 and ents % 4 == 0 and lists % 4 == 0

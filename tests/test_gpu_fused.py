@@ -5,7 +5,9 @@ oracle, whose metadata comes from its own Philox (FP16 sketching page
 
 Bars as for the stored-metadata apply: exact inputs bit for bit, FP32
 within relative Frobenius 1e-5 of fp64, FP16 within 4e-3 (or the error
-model's bar for degenerate shapes).  Shapes cover the fused kernel's own
+model's bar for degenerate shapes), and FP16 sketches of Gaussian inputs
+bit for bit equal to the oracle's RN emulation of the library's order (at
+multi-chunk sizes, and on sampled columns at the bench's full size).  Shapes cover the fused kernel's own
 plans (each rows-per-wave size, row groups, several slices, ragged chunks,
 row offsets) and the shapes it hands to the metadata + LDS fallback."""
 import numpy as np
@@ -51,7 +53,7 @@ FUSED_SHAPES = [
     (5000, 128, 1024, 4),       # two row groups (FP16: one word per lane, R = 64, one group)
     (129, 256, 512, 1),         # one stage plus one row
     (1, 128, 64, 4),            # a single row
-    (4096, 64, 128, 4),         # 64 columns: a quarter (FP16) / half (FP32) of the slice's lanes
+    (4096, 64, 128, 4),         # 64 columns at d = 128: the owner kernel (FP16 and FP32)
     (3000, 68, 64, 4),          # 68 columns, lanes past the row clamped
     (6000, 512, 1024, 4),       # FP32 four words: R = 16, four row groups, two slices
     (2049, 260, 256, 16),       # FP32 four words: a 4-column second slice, zeta = 16
@@ -282,3 +284,43 @@ def test_fused_scale_sampled_rows_exact(scale_case):
         hit = np.nonzero(ri == r)[0]
         row = (v[hit].astype(np.float64)[:, None] * Aq_h[hit // zeta]).sum(axis=0)
         assert np.array_equal(B[r], row), r
+
+
+def test_fused_f16_scale_sampled_columns_library_order(scale_case):
+    """At full size, sampled columns: the FP16 sketch (register kernel) is
+    the oracle's RN emulation of the library's order bit for bit: each
+    output entry adds its contributions per row chunk of the plan in
+    ascending row order from +0, and the chunk partials in the reduce's
+    four contiguous groups (FP16 sketching page §III-B, §III-D).  The
+    columns of the FP16 sum are independent, so a few columns of A emulate
+    those columns of the sketch."""
+    Ad, A, d, zeta, seed, _ = scale_case
+    m, n = A.shape
+    p = b.sk_sketch_plan_describe(b.SK_PRECISION_F16ACC, m, n, n, 16, d, zeta, **MI355X)
+    assert p["kernel"] == 1 and p["chunks"] > 4
+    B = run_fused(Ad, d, zeta, seed, "f16acc")
+    cols = [0, 1, 127, 128, 254, 255]
+    ri, v = oracle.meta_ref(seed, m, d, zeta)
+    exp = oracle.sketch_f16_rn_emul(np.ascontiguousarray(A[:, cols]), ri, v, d, zeta,
+                                    chunk_rows=p["rows_per_chunk"], groups=4)
+    assert np.array_equal(B[:, cols], exp.astype(np.float64))
+
+
+# (m, n, d, zeta): register-kernel plans with many row chunks (one and two
+# words per lane, one and two workgroups per CU, 128- and 64-row stages)
+ORDER_SHAPES = [(20000, 256, 512, 4), (30000, 128, 1024, 8), (20000, 384, 512, 4),
+                (9000, 128, 256, 1), (3001, 256, 128, 4), (50000, 96, 512, 2)]
+
+
+@pytest.mark.parametrize("m,n,d,zeta", ORDER_SHAPES)
+def test_fused_f16_library_order(m, n, d, zeta):
+    """The whole FP16 sketch at multi-chunk sizes equals the oracle's RN
+    emulation with the plan's row chunks and the reduce's four groups, bit
+    for bit, on Gaussian inputs whose additions round."""
+    p = b.sk_sketch_plan_describe(b.SK_PRECISION_F16ACC, m, n, n, 16, d, zeta, **MI355X)
+    assert p["kernel"] == 1 and p["chunks"] > 1
+    say(f"library order {m}x{n} d={d} zeta={zeta} chunks={p['chunks']}")
+    A = (inputs.gaussian(m, n, seed=41) * np.float32(3.0)).astype(np.float32)
+    ri, v = oracle.meta_ref(17, m, d, zeta)
+    exp = oracle.sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=p["rows_per_chunk"], groups=4)
+    assert np.array_equal(run_fused(A, d, zeta, 17, "f16acc"), exp.astype(np.float64))
