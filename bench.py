@@ -318,7 +318,14 @@ def main():
             for _ in range(3):
                 b.sk_apply_blockperm(Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, 1, SEED, Y,
                                      BP_N, 0, sp)
-            done.append("3 x BlockPerm register kernel + reduce, 3 x BlockPerm without workspace")
+            ws2 = torch.empty(b.sk_blockperm_workspace_size(BP_M, BP_N, BP_D, BP_BLOCKS,
+                                                            BP_KAPPA, 2, b.SK_WIRING_SHIFT),
+                              dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                b.sk_apply_blockperm_ex(Abp, BP_M, BP_N, BP_N, BP_D, BP_BLOCKS, BP_KAPPA, 2,
+                                        b.SK_WIRING_SHIFT, SEED, Y, BP_N, 0, ws2, ws2.numel(), sp)
+            done.append("3 x BlockPerm register kernel + reduce, 3 x BlockPerm without workspace, "
+                        "3 x BlockPerm register kernel + reduce at s = 2")
         torch.cuda.synchronize()
         print("profile pass done: " + "; ".join(done), flush=True)
         return
