@@ -31,7 +31,7 @@
 //  * The trailing columns, the right-hand side among them, are updated as
 //    a <- (I - V T V^T)^T a = a - V (T^T (V^T a)) (H_1 ... H_PB = I - V T
 //    V^T, T upper triangular, the forward column-wise accumulation) by as
-//    many workgroups as they need (two columns per wavefront), each with its
+//    many workgroups as they need (one column per wavefront), each with its
 //    own LDS copy of V.  The PB dot products of a column are summed across
 //    the wavefront by a transposing butterfly (each exchange halves the
 //    values a lane holds), and u = T^T w is a forward substitution in G, so
@@ -435,8 +435,10 @@ template <int PB> struct TrailShape {
 // a <- a - V u, u = T^T (V^T a) = T^T w, by forward substitution in G:
 // u_i = tau_i (w_i - sum_{q<i} G[q][i] u_q) (T^-1 = diag(1/tau) +
 // strictly-upper(G) for the forward recurrence; this form also holds for
-// tau_i = 0).  Wavefront w of block b takes columns p0 + PB + 2 (kTrailWaves b
-// + w) and the next; V (unit lower trapezoid) from W.
+// tau_i = 0).  Wavefront w of block b takes column p0 + PB + kTrailWaves b +
+// w (one column per wavefront: the update is latency bound, and twice the
+// blocks finish sooner than two columns per wavefront); V (unit lower
+// trapezoid) from W.
 constexpr int kTrailWaves = 8;                  // 512 threads: V staged in one round of loads
                                                 // for up to 512 panel rows
 template <int PB>
@@ -448,18 +450,16 @@ __global__ __launch_bounds__(kTrailWaves * 64) void k_qr_trail(const QrArgs args
     float *const W = args.W;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int dp = d - p0;
-    const int k0 = p0 + PB + (blockIdx.x * kTrailWaves + wave) * 2;
-    const bool live = k0 <= n, two = k0 < n;
+    const int k0 = p0 + PB + blockIdx.x * kTrailWaves + wave;
+    const bool live = k0 <= n;
     float *const a0 = W + (int64_t)k0 * d + p0;
-    float *const a1 = a0 + d;                       // column k0 + 1 when two
-    // the wavefront's columns and G's column (lane & (PB - 1)), in flight
+    // the wavefront's column and G's column (lane & (PB - 1)), in flight
     // while V is staged
-    float x0[RT], x1[RT];
+    float x0[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         const int r = lane + 64 * i;
         x0[i] = live && r < dp ? a0[r] : 0.f;
-        x1[i] = two && r < dp ? a1[r] : 0.f;
     }
     const int ti = lane & (PB - 1);
     float gcol[PB], tq[PB];
@@ -483,9 +483,9 @@ __global__ __launch_bounds__(kTrailWaves * 64) void k_qr_trail(const QrArgs args
     }
     lds_barrier();
     if (!live) return;                              // wave-uniform; no barrier follows
-    float w0[PB], w1[PB];
+    float w0[PB];
 #pragma unroll
-    for (int q = 0; q < PB; ++q) w0[q] = w1[q] = 0.f;
+    for (int q = 0; q < PB; ++q) w0[q] = 0.f;
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         if (64 * i < dp) {
@@ -497,24 +497,18 @@ __global__ __launch_bounds__(kTrailWaves * 64) void k_qr_trail(const QrArgs args
                 const float ve[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (4 * q4 + e < PB) {
-                        w0[4 * q4 + e] = fmaf(ve[e], x0[i], w0[4 * q4 + e]);
-                        w1[4 * q4 + e] = fmaf(ve[e], x1[i], w1[4 * q4 + e]);
-                    }
+                    if (4 * q4 + e < PB) w0[4 * q4 + e] = fmaf(ve[e], x0[i], w0[4 * q4 + e]);
                 }
             }
         }
     }
     // w_i onto lane i (and its copies), then the forward substitution
     float s0 = bperm((ti << SH) * 4, transpose_sum<PB>(w0));
-    float s1 = bperm((ti << SH) * 4, transpose_sum<PB>(w1));
-    float su0[PB], su1[PB];
+    float su0[PB];
 #pragma unroll
     for (int q = 0; q < PB; ++q) {
         su0[q] = tq[q] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s0), q));
-        su1[q] = tq[q] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s1), q));
         s0 = fmaf(-gcol[q], su0[q], s0);            // gcol[q] = 0 on lanes i <= q
-        s1 = fmaf(-gcol[q], su1[q], s1);
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -527,16 +521,10 @@ __global__ __launch_bounds__(kTrailWaves * 64) void k_qr_trail(const QrArgs args
                 const float ve[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (4 * q4 + e < PB) {
-                        x0[i] = fmaf(-ve[e], su0[4 * q4 + e], x0[i]);
-                        x1[i] = fmaf(-ve[e], su1[4 * q4 + e], x1[i]);
-                    }
+                    if (4 * q4 + e < PB) x0[i] = fmaf(-ve[e], su0[4 * q4 + e], x0[i]);
                 }
             }
-            if (r < dp) {
-                a0[r] = x0[i];
-                if (two) a1[r] = x1[i];
-            }
+            if (r < dp) a0[r] = x0[i];
         }
     }
 }
@@ -626,7 +614,7 @@ hipError_t qr_panel_step(const QrArgs &a, int p0, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ntrail = a.n + 1 - (p0 + PB);         // columns after the panel, rhs included
-    const int blocks = (ntrail + 2 * kTrailWaves - 1) / (2 * kTrailWaves);
+    const int blocks = (ntrail + kTrailWaves - 1) / kTrailWaves;
     k_qr_trail<PB><<<dim3(blocks), dim3(kTrailWaves * 64), 0, s>>>(a, p0);
     return hipGetLastError();
 }
