@@ -185,7 +185,8 @@ def main():
     ap.add_argument("--profile-pass", action="store_true",
                     help="few fixed launches of the dominant kernels and a 1 GiB copy, no JSON")
     ap.add_argument("--profile-legs", default="headline",
-                    help="with --profile-pass: comma list of headline, atomics, lds, narrow")
+                    help="with --profile-pass: comma list of headline, atomics, lds, narrow, "
+                         "blockperm, solve")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -303,6 +304,16 @@ def main():
             done.append("2 x fused f16 sketch of 2^20 x 128 at (zeta, d) = (8, 1024) and "
                         "(4, 512), of 4,194,304 x 64 at (4, 128) (and 2 x fused f32), and of "
                         "2^20 x 2 at (4, 512)")
+        if "solve" in legs:
+            gq = torch.Generator(device=dev).manual_seed(0)
+            SA = torch.randn((2 * n, n), device=dev, generator=gq)
+            Sb = torch.randn(2 * n, device=dev, generator=gq)
+            xq = torch.empty(n, dtype=torch.float32, device=dev)
+            wsq = torch.empty(b.sk_lstsq_workspace_size(2 * n, n), dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                b.sk_lstsq_qr_f32(SA, 2 * n, n, n, Sb, xq, wsq, 0, sp)
+            del SA, Sb, xq, wsq
+            done.append(f"3 x FP32 QR solve of a {2 * n} x {n} system (d = 2n)")
         if "headline" in legs or "blockperm" in legs:
             del A, ri, val, ws16, ws32, wsr16, wsr32, wsf16, wsf32
             torch.cuda.empty_cache()
