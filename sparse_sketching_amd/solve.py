@@ -24,17 +24,18 @@ from . import binding as b
 
 def sketch_pair(A, rhs, d, zeta, seed, precision="f16acc", row_offset=0, combine="f16"):
     """(SA, Sb) as float32 device tensors for the same S.  rhs is a length-m
-    vector; it is sketched as the first column of an m x 2 matrix (the FP16
-    path works on column pairs).  combine (FP16 only): "f16" adds the row
-    chunks' FP16 partials with FP16 additions (every addition in FP16, the
-    page's arithmetic), "f32" in FP32 with one final rounding
-    (SK_COMBINE_F32)."""
+    vector: the FP32 path sketches it as an m x 1 matrix; the FP16 path works
+    on column pairs and sketches it as the first column of [b b] (columns
+    are sketched independently; one copy builds the pair).  combine (FP16
+    only): "f16" adds the row chunks' FP16 partials with FP16 additions
+    (every addition in FP16, the page's arithmetic), "f32" in FP32 with one
+    final rounding (SK_COMBINE_F32)."""
     m = A.shape[0]
-    B2 = torch.zeros((m, 2), dtype=torch.float32, device=A.device)
-    B2[:, 0] = rhs
-    flags = b.SK_COMBINE_F32 if (precision == "f16acc" and combine == "f32") else 0
+    f16 = precision == "f16acc"
+    Bv = rhs.reshape(m, 1).expand(m, 2).contiguous() if f16 else rhs.reshape(m, 1)
+    flags = b.SK_COMBINE_F32 if (f16 and combine == "f32") else 0
     SA = b.sketch_fused(A, d, zeta, seed, precision, row_offset=row_offset, flags=flags)
-    Sb = b.sketch_fused(B2, d, zeta, seed, precision, row_offset=row_offset, flags=flags)[:, 0]
+    Sb = b.sketch_fused(Bv, d, zeta, seed, precision, row_offset=row_offset, flags=flags)[:, 0]
     return SA.float(), Sb.float().contiguous()
 
 
