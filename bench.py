@@ -192,7 +192,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the multi-GPU path is a design note, not part of this build", file=sys.stderr)
+              "sharding over several GPUs is described, not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
