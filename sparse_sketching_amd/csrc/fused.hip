@@ -363,8 +363,8 @@ __global__ __launch_bounds__(kWaves * 64, DUAL ? 8 : 4) void k_stack_fused(
 // halves) otherwise; R = 4 and 8 are kept for devices where two workgroups
 // do not share a CU.  W = 2 two per CU: R = 4, 8 (and 16 for FP32), one
 // set in two halves.
-// W = 1: R = 8, 16, 32 two per CU, R = 64 one per CU.  W = 4 (FP32 only):
-// R = 8, 16 with two sets.
+// W = 1: R = 8, 16, 32 two per CU.  W = 4 (FP32 only): R = 8, 16 with two
+// sets.
 template <class T, bool META>
 const void *pick_fused(int W, int S, int R, int P, bool dual) {
     if (W == 2 && S == 128 && !dual) {
@@ -386,8 +386,6 @@ const void *pick_fused(int W, int S, int R, int P, bool dual) {
                 return (const void *)k_stack_fused<T, 1, 64, 16, 1, META, true>;
             if (dual && R == 32 && P == 1)
                 return (const void *)k_stack_fused<T, 1, 64, 32, 1, META, true>;
-            if (!dual && R == 64 && P == 2)
-                return (const void *)k_stack_fused<T, 1, 64, 64, 2, META, false>;
         }
     }
     if constexpr (T::kCols == 1) {
@@ -440,8 +438,8 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
 // slice, half the accumulator registers per output row, so more rows per
 // wave (fewer row groups) or two workgroups per CU, and for FP32 4-byte
 // loads (any width, stride or base).  Else 2 (256 FP16 / 128 FP32 columns).  Rows per wave
-// R = d / (16 G) for the fewest row groups G with W x R <= 64 partial words
-// per lane (R <= 32 at W = 2) and R dividing d/zeta (a wave's rows inside
+// R = d / (16 G) for the fewest row groups G with R <= 32 (16 at W = 4)
+// and R dividing d/zeta (a wave's rows inside
 // one block); R must be one of the built sizes.  Few registers per lane
 // (FP16 W = 2, R <= 8; W = 1, R <= 32; FP32 W = 2, R <= 16) take the
 // two-per-CU shape where the LDS holds two of its workgroups.  Chunks are
@@ -453,7 +451,11 @@ hipError_t launch_fused_t(const FusedPlan &p, const FusedArgs &fa, void *B, int6
 namespace {
 bool plan_rows(int32_t d, int32_t zeta, int W, int *R_out, int *G_out) {
     const int64_t db = d / zeta;
-    const int rmax = W == 1 ? 64 : W == 2 ? 32 : 16, rmin = W == 2 ? 4 : 8;
+    // W = 1 stops at 32 rows per wavefront, two workgroups per CU: at d =
+    // 1024 and 2048 two row groups of R = 32 (A read twice, mostly from L2)
+    // beat one group of R = 64 at one workgroup per CU by 2-11% (FP16 128
+    // and FP32 64 columns, fused and stored-metadata applies)
+    const int rmax = W == 4 ? 16 : 32, rmin = W == 2 ? 4 : 8;
     for (int g = 1; (int64_t)kWaves * g <= d; g *= 2) {
         if (d % (kWaves * g) != 0) break;
         const int64_t r = d / (kWaves * g);
@@ -494,7 +496,7 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     // rows (4 rows x K floats) take at most 40 registers: FP16 W = 2, R <= 8;
     // FP16 W = 1, R <= 32; FP32 W = 2, R <= 16 (all fit 64 VGPRs)
     const bool dual = W <= 2 && W * R + 4 * K <= 40 && di.max_lds >= 2 * kFusedDualLdsBytes;
-    if (W == 1 && !dual && R != 64) return false;   // W = 1, one per CU: R = 64 only
+    if (W == 1 && !dual) return false;              // W = 1 runs two per CU
     *p = FusedPlan{};
     p->kind = kFusedRegister;
     p->words = W;
@@ -502,7 +504,7 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     p->stage_rows = (W == 2 && !dual) ? 128 : 64;
     p->rows_per_wave = R;
     p->groups = G;
-    p->load_sets = dual ? 1 : (R == 8 || R == 16 || R == 64) ? 2 : 1;
+    p->load_sets = dual ? 1 : (R == 8 || R == 16) ? 2 : 1;
     p->slices = (n + 64 * K - 1) / (64 * K);
     const int64_t per_chunk = p->slices * G;
     int64_t want = ((int64_t)di.num_cu * (dual ? 2 : 1) + per_chunk - 1) / per_chunk;

@@ -354,7 +354,7 @@ def test_fused_plan_fits_kernel(lib, precision, m, n, d, zeta):
     # four words per lane only for FP32 wider than 128 columns; one word only
     # for FP16 of at most 128 columns; two per CU (64-row stages) for few
     # partial words per lane; 128-row stages only at two words, one per CU
-    assert (W, S, per_cu) in ((2, 128, 1), (4, 64, 1), (2, 64, 2), (1, 64, 2), (1, 64, 1))
+    assert (W, S, per_cu) in ((2, 128, 1), (4, 64, 1), (2, 64, 2), (1, 64, 2))
     assert W != 4 or (not f16 and n > 128 and n % 4 == 0)
     assert W != 1 or (f16 and n <= 128) or (not f16 and n <= 64)
     K = W * (2 if f16 else 1)
@@ -535,11 +535,12 @@ def test_fused_plan_word_width(lib):
     q = b.sk_fused_plan_describe(P16, 1 << 20, 512, 512, 16, 512, 4, **MI355X)
     assert (q["fused"], q["words"]) == (1, 2)
     # FP16 rows of at most 128 columns: one word per lane (8-byte loads);
-    # R <= 32 two per CU, d = 1024 in one row group (R = 64)
-    for d, R, per_cu in ((256, 16, 2), (512, 32, 2), (1024, 64, 1)):
+    # R <= 32 two per CU, d = 1024 and 2048 in two and four row groups
+    for d, R, G in ((256, 16, 1), (512, 32, 1), (1024, 32, 2), (2048, 32, 4)):
         q = b.sk_fused_plan_describe(P16, 1 << 20, 128, 128, 8, d, 4, **MI355X)
         assert (q["fused"], q["words"], q["rows_per_wave"], q["groups"], q["per_cu"],
-                q["slices"]) == (1, 1, R, 1, per_cu, 1)
+                q["slices"]) == (1, 1, R, G, 2, 1)
+        assert q["grid"] == 512
     # FP32 of at most 64 columns: one word per lane, any width or stride;
     # R = 8 two per CU, 64-row stages, chunks for 512 workgroups
     q = b.sk_fused_plan_describe(P32, 1 << 22, 64, 64, 16, 128, 4, **MI355X)

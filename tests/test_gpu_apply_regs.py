@@ -41,7 +41,7 @@ def run_reg(A, ri, v, zeta, d, precision, flags=b.SK_VARIANT_REG, out=None):
     (3000, 128, 128, 4, (1, 8, 1), (2, 8, 1)),        # R = 8, a short last stage
     (5000, 260, 256, 8, (2, 16, 1), (4, 16, 1)),      # R = 16, zeta = 8, ragged second slice
     (4096, 128, 512, 8, (1, 32, 1), (2, 32, 1)),      # R = 32 (FP16 one word per lane)
-    (3001, 128, 1024, 4, (1, 64, 1), (2, 32, 2)),     # FP16 R = 64: d = 1024 in one group
+    (3001, 128, 1024, 4, (1, 32, 2), (2, 32, 2)),     # FP16 one word, d = 1024 in two groups
     (2500, 136, 1024, 1, (2, 32, 2), (4, 16, 4)),     # row groups (A read 2 / 4 times)
     (3001, 256, 512, 4, (2, 32, 1), (4, 16, 2)),      # FP32 four words, ragged 64-row stage
     (777, 512, 128, 2, (2, 8, 1), (4, 8, 1)),         # FP32 four words, R = 8, two slices

@@ -50,7 +50,7 @@ FUSED_SHAPES = [
     (3001, 256, 128, 4),        # R = 8, ragged last stage
     (1000, 128, 256, 16),       # R = 16, zeta = 16 (four Philox blocks per row)
     (2500, 384, 512, 4),        # R = 32 (FP32: 16, two groups), two slices, ragged slice
-    (5000, 128, 1024, 4),       # two row groups (FP16: one word per lane, R = 64, one group)
+    (5000, 128, 1024, 4),       # two row groups (FP16: one word per lane, R = 32, two per CU)
     (129, 256, 512, 1),         # one stage plus one row
     (1, 128, 64, 4),            # a single row
     (4096, 64, 128, 4),         # 64 columns at d = 128: the owner kernel (FP16 and FP32)
@@ -193,7 +193,7 @@ def test_fused_f32_word_width_by_alignment(offset, lda):
     (5000, 1, 1, 0, 512, 4),        # a vector
     (3001, 31, 33, 1, 256, 16),     # odd width and stride, 4-byte aligned base
     (4096, 63, 64, 3, 128, 1),      # 63 columns, CountSketch
-    (2000, 64, 67, 0, 1024, 4),     # 64 columns, R = 64 (one per CU)
+    (2000, 64, 67, 0, 1024, 4),     # 64 columns, d = 1024 in two row groups
 ])
 def test_fused_f32_one_word_lanes(m, n, lda, offset, d, zeta):
     """FP32 of at most 64 columns runs one word per lane with 4-byte loads:
