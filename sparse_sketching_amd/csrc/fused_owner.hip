@@ -427,6 +427,10 @@ bool plan_owner(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     int U = 1;
     while (U < nw) U *= 2;
     if (U > 64) return false;
+    // a one-word row at d <= 256 is padded to two words: twice the lanes and
+    // wavefronts per CU for the same list walks (2^20 x 2 FP16 at d = 256:
+    // 44 -> 38 us; at d = 512, 1024 threads instead of 512 were no faster)
+    if (U == 1 && d <= 256) U = 2;
     // words per lane: the fewest with d x (U / V) <= 1024 threads, and whole
     // wavefronts
     int V = 1;
