@@ -309,7 +309,8 @@ def test_fused_f16_scale_sampled_columns_library_order(scale_case):
 # (m, n, d, zeta): register-kernel plans with many row chunks (one and two
 # words per lane, one and two workgroups per CU, 128- and 64-row stages)
 ORDER_SHAPES = [(20000, 256, 512, 4), (30000, 128, 1024, 8), (20000, 384, 512, 4),
-                (9000, 128, 256, 1), (3001, 256, 128, 4), (50000, 96, 512, 2)]
+                (9000, 128, 256, 1), (3001, 256, 128, 4), (50000, 96, 512, 2),
+                (12000, 128, 2048, 4)]     # one word per lane, four row groups
 
 
 @pytest.mark.parametrize("m,n,d,zeta", ORDER_SHAPES)
