@@ -526,11 +526,13 @@ bool plan_fused(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
 // 32 words (FP16 up to 64 columns, FP32 up to 32), and rows of 64 words
 // (FP16 128 columns, FP32 64) at no more than 8 words per lane (d <= 128).
 // Measured on MI355X (2^20 rows unless noted, complete sketch): FP16
-// 2 columns, d = 512: 36-42 us against 144 in the register kernel; FP16 64
-// columns, 4,194,304 rows, d = 128: 231-235 us against 341; FP32 64 columns
-// there: 244-249 us against 330; FP16 32 columns, d = 1024: 116 us against
-// 181; but FP32 64 columns at d = 256 (16 words per lane): 161 us against
-// 139, and FP16 128 columns at d = 256: 144-169 us against 99-144.
+// 2 columns, d = 512: 35-42 us against 144 in the register kernel; FP16 64
+// columns, 4,194,304 rows, d = 128: 225-235 us against 341; FP32 64 columns
+// there: 244-250 us against 330; FP16 32 columns, d = 1024: 107 us against
+// 181; but with 16 words per lane the register kernel stays faster: FP32 64
+// columns at d = 256, 111 / 158 us against 102 / 140 (zeta = 4 / 8), FP16
+// 128 columns at d = 256, 108 / 122 / 168 against 102 / 108 / 143 (zeta =
+// 1 / 4 / 8).
 bool plan_sketch(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, int a_align,
                  int32_t d, int32_t zeta, FusedPlan *p) {
     FusedPlan q{};
