@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kMaxWavesG * 64) void k_bp_general(const BlockPermG
     float *tile = acc + (int64_t)wave * trows * 64 + lane;
 
     for (int k = threadIdx.x; k < nw * trows * 64; k += nthr) acc[k] = 0.f;
-    if (threadIdx.x < kappa)
+    if ((int)threadIdx.x < kappa)
         keys[threadIdx.x] = blockperm_key(args.seed, bp_reader(args, ginv, h, threadIdx.x), h);
     __syncthreads();
 

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kW * 64) void k_bp_regs(const BlockPermGenArgs args
         reinterpret_cast<const char *>(args.A) + ((int64_t)h * args.Bc + rb) * args.lda * 4;
     const int64_t ldab = args.lda * 4;
 
-    if (threadIdx.x < kappa)
+    if ((int)threadIdx.x < kappa)
         keys[threadIdx.x] = blockperm_key(args.seed, bp_reader(args, ginv, h, threadIdx.x), h);
 
     float acc[R][4];
