@@ -150,7 +150,10 @@ def _accumulate_flat(A, row_idx, val, d, zeta, e0, e1):
     if e1 <= e0:
         return B
     e = np.arange(e0, e1, dtype=np.int64)
-    keep = in_block(row_idx, d, zeta)[e0:e1]
+    # (entry i*zeta + t: a range starting at a whole row has the same block
+    # index t at each position as the full array)
+    assert e0 % zeta == 0
+    keep = in_block(row_idx[e0:e1], d, zeta)
     e = e[keep]
     if e.size == 0:
         return B
