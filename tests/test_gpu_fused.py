@@ -306,6 +306,32 @@ def test_fused_f16_scale_sampled_columns_library_order(scale_case):
     assert np.array_equal(B[:, cols], exp.astype(np.float64))
 
 
+def test_fused_f16_coherence_scale_sampled_rows_library_order():
+    """The coherence sweep's heaviest point at full size (A 2^20 x 128,
+    zeta = 8, d = 1024: one word per lane in two row groups, two workgroups
+    per CU), sampled output rows in both row groups and several blocks: bit
+    for bit the oracle's RN emulation with the plan's row chunks and the
+    reduce's four groups.  An output row's sum involves only its own
+    contributions, so the emulation keeps the metadata entries of the
+    sampled rows and drops the rest (an entry outside its block adds
+    nothing)."""
+    m, n, d, zeta, seed = 1 << 20, 128, 1024, 8, 3
+    p = b.sk_sketch_plan_describe(b.SK_PRECISION_F16ACC, m, n, n, 16, d, zeta, **MI355X)
+    q = b.sk_fused_plan_describe(b.SK_PRECISION_F16ACC, m, n, n, 16, d, zeta, **MI355X)
+    assert p["kernel"] == 1 and p["chunks"] > 4 and q["groups"] == 2 and q["per_cu"] == 2
+    say("fused coherence-scale case: 2^20 x 128, zeta = 8, d = 1024")
+    Ad = inputs.gaussian_torch(m, n, seed=5)
+    B = run_fused(Ad, d, zeta, seed, "f16acc")
+    A = Ad.cpu().numpy()
+    del Ad
+    rows = np.array([0, 1, 127, 128, 511, 512, 640, 1023])
+    ri, v = oracle.meta_ref(seed, m, d, zeta)
+    ri_s = np.where(np.isin(ri, rows), ri, -1).astype(np.int32)
+    exp = oracle.sketch_f16_rn_emul(A, ri_s, v, d, zeta, chunk_rows=p["rows_per_chunk"],
+                                    groups=4)
+    assert np.array_equal(B[rows], exp[rows].astype(np.float64))
+
+
 # (m, n, d, zeta): register-kernel plans with many row chunks (one and two
 # words per lane, one and two workgroups per CU, 128- and 64-row stages)
 ORDER_SHAPES = [(20000, 256, 512, 4), (30000, 128, 1024, 8), (20000, 384, 512, 4),

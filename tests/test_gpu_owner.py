@@ -157,3 +157,26 @@ def test_owner_accumulate(combine):
     flags = b.SK_ACCUMULATE | (b.SK_COMBINE_F32 if combine == "f32" else 0)
     got = sketch(to_dev(A), d, zeta, seed, "f16acc", out=out, flags=flags)
     assert same(got, f16_expect(A, seed, d, zeta, p, combine=combine, B0=B0))
+
+
+def test_owner_range_shape_full_size_sampled_rows():
+    """The range workload's shape at full size (4,194,304 x 64 FP16, zeta =
+    4, d = 128: the owner kernel at four words per lane), sampled output
+    rows from every block: bit for bit the oracle's RN emulation with the
+    plan's chunks and the reduce's groups.  An output row's sum involves
+    only its own contributions, so the emulation keeps the metadata entries
+    of the sampled rows and drops the rest (an entry outside its block adds
+    nothing)."""
+    m, n, d, zeta, seed = 4194304, 64, 128, 4, 2
+    p = plan("f16acc", m, n, n, 16, d, zeta)
+    assert p["kernel"] == 2 and p["words"] == 4 and p["chunks"] > 4
+    say(f"owner range shape full size: chunks={p['chunks']} rows_per_chunk={p['rows_per_chunk']}")
+    Ad = inputs.gaussian_torch(m, n, seed=6)
+    got = sketch(Ad, d, zeta, seed, "f16acc")
+    A = Ad.cpu().numpy()
+    del Ad
+    rows = np.array([0, 1, 31, 32, 63, 64, 100, 127])
+    ri, v = oracle.meta_ref(seed, m, d, zeta)
+    ri_s = np.where(np.isin(ri, rows), ri, -1).astype(np.int32)
+    exp = oracle.sketch_f16_rn_emul(A, ri_s, v, d, zeta, chunk_rows=p["rows_per_chunk"], groups=4)
+    assert same(got[rows], exp[rows].astype(np.float64))
