@@ -180,3 +180,14 @@ def test_owner_range_shape_full_size_sampled_rows():
     ri_s = np.where(np.isin(ri, rows), ri, -1).astype(np.int32)
     exp = oracle.sketch_f16_rn_emul(A, ri_s, v, d, zeta, chunk_rows=p["rows_per_chunk"], groups=4)
     assert same(got[rows], exp[rows].astype(np.float64))
+
+
+def test_owner_right_hand_side_full_size():
+    """Sketch-and-solve's right-hand side at full size (2^20 x 2 FP16, zeta
+    = 4, d = 512: one word per lane): every output entry bit for bit the
+    oracle's RN emulation of the library order."""
+    m, n, d, zeta, seed = 1 << 20, 2, 512, 4, 4
+    p = plan("f16acc", m, n, n, 16, d, zeta)
+    assert p["kernel"] == 2 and p["words"] == 1 and p["chunks"] > 4
+    A = (inputs.gaussian(m, n, seed=7) * np.float32(3.0)).astype(np.float32)
+    assert same(sketch(to_dev(A), d, zeta, seed, "f16acc"), f16_expect(A, seed, d, zeta, p))
