@@ -433,10 +433,12 @@ sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_
  *        output row and stage (owner), words per lane load (owner), rows per
  *        chunk, chunks, workgroups, workspace bytes, dynamic LDS bytes per
  *        workgroup (owner), workgroups per CU the plan is sized for, LDS
- *        words between output rows' masks and between their lists (owner)}.
+ *        words between output rows' masks and between their lists (owner),
+ *        workgroup barriers per stage (owner: 1 where the LDS holds three
+ *        stage buffers at the same stage rows, else 2)}.
  * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ARG (precision, num_cu, max_lds).
  */
-#define SK_SKETCH_PLAN_FIELDS 16
+#define SK_SKETCH_PLAN_FIELDS 17
 sk_status sk_sketch_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
                                   int32_t a_align, int32_t d, int32_t zeta, int32_t num_cu,
                                   int32_t max_lds, int64_t *out);

@@ -27,8 +27,11 @@
 //    hit: a wavefront serves 64/L output rows per list step.
 //  * A list holds up to `cap` hits; an output row with more hits in a stage
 //    walks the rest straight from its mask (same order, slower).
-//  * Two barriers per stage; the next stage's rows are in flight from HBM
-//    meanwhile (loads with the nontemporal hint: A is read once).
+//  * Two barriers per stage, or one where the LDS holds a third stage
+//    buffer, mask set and entry set at the same stage rows (then stage s is
+//    walked, s + 1 ranked and s + 2 staged and drawn in one phase); the
+//    next stages' rows are in flight from HBM meanwhile (loads with the
+//    nontemporal hint: A is read once).
 #include "sk_internal.hpp"
 #include "sk_rng.hpp"
 #include "sk_stack_apply.hpp"
@@ -90,7 +93,9 @@ constexpr int owner_row_stride(int w, bool spread) {
 // The sign bits of T's +-1 word (FP16 pair: both halves)
 template <class T> constexpr uint32_t kUnitSign = T::kCols == 2 ? 0x80008000u : 0x80000000u;
 
-template <class T, int V, int KF>
+// OB: one barrier per stage (three stage buffers, mask and entry sets, two
+// list sets); else two (two of each, one list set)
+template <class T, int V, int KF, bool OB>
 __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     extern __shared__ __align__(16) uint32_t lds[];
     const int NT = (int)blockDim.x;
@@ -106,23 +111,26 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     const int CS = args.cs;             // list stride in words
     const uint32_t cap = (uint32_t)args.cap;
     const uint32_t db = (uint32_t)(d / zeta);
-    // LDS, in words:
-    //  * two stage buffers [S + 1][U] (row S: the -0 row that unused list
+    // LDS, in words (NB = 3 with one barrier per stage, else 2):
+    //  * NB stage buffers [S + 1][U] (row S: the -0 row that unused list
     //    slots point at), padding to 16 bytes, 4 trash words;
-    //  * two mask sets [d][MS]: per output row, MW words of hit bits (bit j:
+    //  * NB mask sets [d][MS]: per output row, MW words of hit bits (bit j:
     //    stage row j hits the row), then per 64 stage rows a byte count of
     //    its hits (at most 8 bytes, in 4 words with the padding);
-    //  * two entry sets [zeta][S]: output row | sign << 31 of (block, row),
+    //  * NB entry sets [zeta][S]: output row | sign << 31 of (block, row),
     //    ~0 for a row past the chunk;
-    //  * one list set [d][CS]: per output row its hits in ascending row
+    //  * NB - 1 list sets [d][CS]: per output row its hits in ascending row
     //    order, as the row's word offset in a stage buffer | unit sign bits.
+    constexpr int NB = OB ? 3 : 2;
     const int BS = (S + 1) * U;
     uint32_t *const bufs = lds;
-    const uint32_t trash = (uint32_t)(2 * BS + ((2 * BS) & 2));
+    const uint32_t trash = (uint32_t)((NB * BS + 3) & ~3);
     uint32_t *const masks = bufs + trash + 4;
     const int MSET = d * MS;            // words of a mask set
-    uint32_t *const ents = masks + 2 * MSET;
-    uint32_t *const lst = ents + 2 * zeta * S;
+    uint32_t *const ents = masks + NB * MSET;
+    const int ESET = zeta * S;          // words of an entry set
+    uint32_t *const lsts = ents + NB * ESET;
+    const int LSET = d * CS;            // words of a list set
 
     const int32_t chunk = blockIdx.x;
     const int64_t r0 = (int64_t)chunk * args.rows_per_chunk;
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     // counts below it) plus those before it in its own group (mbcnt of the
     // group's 64 mask bits: a wavefront takes one group of one block, lane =
     // row mod 64).  Two groups per pass, their reads issued together.
-    auto rank = [&](const uint32_t *mk, const uint32_t *ent) {
+    auto rank = [&](const uint32_t *mk, const uint32_t *ent, uint32_t *lst) {
         const int per_t = S >> 6;
         const int groups = zeta * per_t;
         for (int g0 = wave; g0 < groups; g0 += 2 * NW) {
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
             for (int k = 0; k < VC; ++k) acc[i + k] = T::fma_unit(x[k], u, acc[i + k]);
         }
     };
-    const uint32_t *const my_list = lst + __umul24((uint32_t)o, (uint32_t)CS);
+    const uint32_t my_list_off = __umul24((uint32_t)o, (uint32_t)CS);
     const uint32_t my_mask = __umul24((uint32_t)o, (uint32_t)MS);
     // zero the lane's share of its row's mask and count words
     auto clear_row = [&](uint32_t *mk) {
@@ -293,14 +301,17 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     // list slot past the row's hits points at the -0 row (x * +1 = -0 adds
     // nothing to any value), so list steps take no branches (below 16 words)
     const uint32_t dummy = (uint32_t)(S << u_log);
-    auto walk = [&](const uint32_t *buf, uint32_t *mk, const uint32_t *ent) -> bool {
+    auto walk = [&](const uint32_t *buf, uint32_t *mk, const uint32_t *ent,
+                    const uint32_t *lst) -> bool {
+        const uint32_t *const my_list = lst + my_list_off;
         const uint2 cw = *reinterpret_cast<const uint2 *>(mk + my_mask + MW);
         const uint32_t count = __builtin_amdgcn_sad_u8(cw.y, 0u, __builtin_amdgcn_sad_u8(cw.x, 0u, 0u));
         const uint32_t cnt = count < cap ? count : cap;
         // the row's count words are read (the L lanes of a row share a
         // wavefront, whose LDS accesses complete in order); clear its words
-        // for the stage two ahead, each lane its share, except where the
-        // rest of the row's hits are walked from the mask below
+        // for the next stage that uses this mask set, each lane its share,
+        // except where the rest of the row's hits are walked from the mask
+        // below
         if (count <= cap) clear_row(mk);
         for (uint32_t p = 0; __ballot(p < cnt) != 0; p += 4) {
             const uint4 e4 = *reinterpret_cast<const uint4 *>(my_list + p);
@@ -338,46 +349,85 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     };
 
     // masks and counts start clear; afterwards each row's words are cleared
-    // once its stage is walked.  Row S of both stage buffers holds -0.
-    for (int i = tid; i < 2 * MSET; i += NT) masks[i] = 0u;
-    for (int i = tid; i < U; i += NT) {
-        bufs[(S << u_log) + i] = kUnitSign<T>;
-        bufs[BS + (S << u_log) + i] = kUnitSign<T>;
-    }
+    // once its stage is walked.  Row S of every stage buffer holds -0.
+    for (int i = tid; i < NB * MSET; i += NT) masks[i] = 0u;
+    for (int i = tid; i < U; i += NT)
+#pragma unroll
+        for (int k = 0; k < NB; ++k) bufs[k * BS + (S << u_log) + i] = kUnitSign<T>;
     __syncthreads();
     load(0, ld[0]);
     load(1, ld[1]);
     stage(ld[0], bufs);
     draw(0, masks, ents);
     load(2, ld[0]);
+    if constexpr (OB) {
+        if (1 < nst) {
+            stage(ld[1], bufs + BS);
+            draw(1, masks + MSET, ents + ESET);
+        }
+        load(3, ld[1]);
+    }
     lds_barrier();
-    rank(masks, ents);
+    rank(masks, ents, lsts);
     lds_barrier();
-    for (int32_t s0 = 0; s0 < nst; s0 += 2) {
-        // two stages per trip, so every buffer and register set index is a
-        // constant; the loads are issued on every path (clamped past the
-        // chunk), so each set's wait counts only the other set's loads
+    if constexpr (OB) {
+        // one barrier per stage: walk s, rank s + 1, stage and draw s + 2 in
+        // one phase.  Stage buffers, mask and entry sets rotate over three
+        // and list sets over two, so the sets a phase reads and writes are
+        // disjoint: the walk reads (and clears its rows' masks in) set s
+        // mod 3, the rank reads set s + 1 and writes list set s + 1 mod 2,
+        // the draw writes set s + 2, last read two phases before.
+        int32_t r3 = 0;                 // s mod 3
+        for (int32_t s0 = 0; s0 < nst; s0 += 2) {
+            // two stages per trip, so the register set index is a constant
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int32_t s = s0 + b;
-            const uint32_t *buf = bufs + b * BS, *ent = ents + b * zeta * S;
-            uint32_t *mk = masks + b * MSET;
-            uint32_t *buf1 = bufs + (b ^ 1) * BS, *mk1 = masks + (b ^ 1) * MSET,
-                     *ent1 = ents + (b ^ 1) * zeta * S;
-            // stage s+1 from the set loaded two stages ago, then that set
-            // takes stage s+3
-            if (s + 1 < nst) {
-                stage(ld[b ^ 1], buf1);
-                draw(s + 1, mk1, ent1);
+            for (int b = 0; b < 2; ++b) {
+                const int32_t s = s0 + b;
+                const int32_t i0 = r3, i1 = r3 == 2 ? 0 : r3 + 1, i2 = r3 == 0 ? 2 : r3 - 1;
+                if (s < nst) {
+                    uint32_t *mk = masks + i0 * MSET;
+                    if (walk(bufs + i0 * BS, mk, ents + i0 * ESET, lsts + b * LSET))
+                        clear_row(mk);
+                }
+                if (s + 1 < nst) rank(masks + i1 * MSET, ents + i1 * ESET, lsts + (b ^ 1) * LSET);
+                // stage s + 2 from the set loaded two stages ago, then that
+                // set takes stage s + 4 (issued on every path, clamped)
+                if (s + 2 < nst) {
+                    stage(ld[b], bufs + i2 * BS);
+                    draw(s + 2, masks + i2 * MSET, ents + i2 * ESET);
+                }
+                load(s + 4, ld[b]);
+                lds_barrier();
+                r3 = i1;
             }
-            load(s + 3, ld[b ^ 1]);
-            // (a row walked past its list still needs its mask words until
-            // the barrier; its lanes clear them after it)
-            const bool over = s < nst && walk(buf, mk, ent);
-            lds_barrier();
-            if (s + 1 < nst) rank(mk1, ent1);
-            if (over) clear_row(mk);
-            lds_barrier();
+        }
+    } else {
+        for (int32_t s0 = 0; s0 < nst; s0 += 2) {
+            // two stages per trip, so every buffer and register set index is
+            // a constant; the loads are issued on every path (clamped past
+            // the chunk), so each set's wait counts only the other set's loads
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int32_t s = s0 + b;
+                const uint32_t *buf = bufs + b * BS, *ent = ents + b * ESET;
+                uint32_t *mk = masks + b * MSET;
+                uint32_t *buf1 = bufs + (b ^ 1) * BS, *mk1 = masks + (b ^ 1) * MSET,
+                         *ent1 = ents + (b ^ 1) * ESET;
+                // stage s+1 from the set loaded two stages ago, then that set
+                // takes stage s+3
+                if (s + 1 < nst) {
+                    stage(ld[b ^ 1], buf1);
+                    draw(s + 1, mk1, ent1);
+                }
+                load(s + 3, ld[b ^ 1]);
+                // (a row walked past its list still needs its mask words
+                // until the barrier; its lanes clear them after it)
+                const bool over = s < nst && walk(buf, mk, ent, lsts);
+                lds_barrier();
+                if (s + 1 < nst) rank(mk1, ent1, lsts);
+                if (over) clear_row(mk);
+                lds_barrier();
+            }
         }
     }
     // the loads past the last stage must land before exit
@@ -395,31 +445,40 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     }
 }
 
-template <class T, int KF>
+template <class T, int KF, bool OB>
 const void *pick_owner_v(int V) {
     switch (V) {
-    case 1: return (const void *)k_stack_owner<T, 1, KF>;
-    case 2: return (const void *)k_stack_owner<T, 2, KF>;
-    case 4: return (const void *)k_stack_owner<T, 4, KF>;
-    case 8: return (const void *)k_stack_owner<T, 8, KF>;
-    case 16: return (const void *)k_stack_owner<T, 16, KF>;
+    case 1: return (const void *)k_stack_owner<T, 1, KF, OB>;
+    case 2: return (const void *)k_stack_owner<T, 2, KF, OB>;
+    case 4: return (const void *)k_stack_owner<T, 4, KF, OB>;
+    case 8: return (const void *)k_stack_owner<T, 8, KF, OB>;
+    case 16: return (const void *)k_stack_owner<T, 16, KF, OB>;
     default: return nullptr;
     }
 }
 
 // the built instances: FP16 loads of one or two words (2 or 4 floats), FP32
-// of one or four
-const void *pick_owner(bool f16, int V, int kw) {
-    if (f16) return kw == 2 ? pick_owner_v<AccF16, 4>(V) : kw == 1 ? pick_owner_v<AccF16, 2>(V) : nullptr;
-    return kw == 4 ? pick_owner_v<AccF32, 4>(V) : kw == 1 ? pick_owner_v<AccF32, 1>(V) : nullptr;
+// of one or four; one or two barriers per stage
+template <bool OB>
+const void *pick_owner_b(bool f16, int V, int kw) {
+    if (f16)
+        return kw == 2 ? pick_owner_v<AccF16, 4, OB>(V) : kw == 1 ? pick_owner_v<AccF16, 2, OB>(V) : nullptr;
+    return kw == 4 ? pick_owner_v<AccF32, 4, OB>(V) : kw == 1 ? pick_owner_v<AccF32, 1, OB>(V) : nullptr;
+}
+const void *pick_owner(bool f16, int V, int kw, int barriers) {
+    return barriers == 1 ? pick_owner_b<true>(f16, V, kw)
+                         : barriers == 2 ? pick_owner_b<false>(f16, V, kw) : nullptr;
 }
 
 }  // namespace
 
-size_t owner_lds_bytes(int32_t S, int32_t U, int32_t d, int32_t zeta, int32_t cap, bool spread) {
-    const size_t bufs = (size_t)2 * (S + 1) * U;
-    return 4 * (bufs + (bufs & 2) + 4 + (size_t)2 * d * owner_row_stride(S / 32, spread) +
-                (size_t)2 * zeta * S + (size_t)d * owner_row_stride(cap, spread));
+// nb: stage buffers, mask and entry sets (3: one barrier per stage, with two
+// list sets; 2: two barriers, one list set)
+size_t owner_lds_bytes(int32_t S, int32_t U, int32_t d, int32_t zeta, int32_t cap, bool spread,
+                       int nb) {
+    const size_t bufs = (size_t)nb * (S + 1) * U;
+    return 4 * (((bufs + 3) & ~(size_t)3) + 4 + (size_t)nb * d * owner_row_stride(S / 32, spread) +
+                (size_t)nb * zeta * S + (size_t)(nb - 1) * d * owner_row_stride(cap, spread));
 }
 
 // Plan of the owner kernel: FP16 rows of at most 64 column pairs, FP32 rows
@@ -478,13 +537,26 @@ bool plan_owner(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
         return (int32_t)c;
     };
     while (S > 128 &&
-           owner_lds_bytes((int32_t)S, U, d, zeta, cap_for(S), false) > (size_t)di.max_lds)
+           owner_lds_bytes((int32_t)S, U, d, zeta, cap_for(S), false, 2) > (size_t)di.max_lds)
         S /= 2;
     const int32_t cap = cap_for(S);
-    const bool spread = owner_lds_bytes((int32_t)S, U, d, zeta, cap, true) <= (size_t)di.max_lds;
-    const size_t lds = owner_lds_bytes((int32_t)S, U, d, zeta, cap, spread);
+    const bool spread = owner_lds_bytes((int32_t)S, U, d, zeta, cap, true, 2) <= (size_t)di.max_lds;
+    size_t lds = owner_lds_bytes((int32_t)S, U, d, zeta, cap, spread, 2);
     if (lds > (size_t)di.max_lds) return false;
-    const int per_cu = (size_t)di.max_lds >= 2 * lds && NT <= 512 ? 2 : 1;
+    auto per_cu_for = [&](size_t b) { return (size_t)di.max_lds >= 2 * b && NT <= 512 ? 2 : 1; };
+    const int per_cu = per_cu_for(lds);
+    // one barrier per stage where a third stage buffer, mask and entry set
+    // and a second list set fit at the same stage rows and workgroups per
+    // CU, for workgroups of 512 threads or more whose output rows average
+    // at least 8 hits a stage (4 x 2^20 x 64 FP16 at d = 128: 226 -> 216
+    // us, 2^20 x 32 FP16 at d = 256, zeta = 8: 72 -> 69 us; with fewer
+    // threads or hits, as at 4 x 2^20 x 2 with d <= 128 or 2^20 x 128 FP16
+    // at d = 128, zeta = 4, it ran up to 5% slower, and where it would need
+    // fewer stage rows, slower still)
+    const size_t lds1 = owner_lds_bytes((int32_t)S, U, d, zeta, cap, spread, 3);
+    const bool one_barrier = NT >= 512 && S * zeta >= 8 * (int64_t)d &&
+                             lds1 <= (size_t)di.max_lds && per_cu_for(lds1) == per_cu;
+    if (one_barrier) lds = lds1;
     const int64_t stages = (m + S - 1) / S;
     int64_t want = (int64_t)di.num_cu * per_cu;
     if (want > stages) want = stages;
@@ -509,6 +581,7 @@ bool plan_owner(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     p->list_stride = owner_row_stride(cap, spread);
     p->load_words = kw;
     p->lds_bytes = lds;
+    p->barriers = one_barrier ? 1 : 2;
     p->ws_bytes = (size_t)p->chunks * (size_t)d * (size_t)U * 4;
     return true;
 }
@@ -537,7 +610,7 @@ hipError_t launch_owner(const FusedPlan &p, bool f16, const float *A, int64_t m,
     a.ms = p.mask_stride;
     a.cs = p.list_stride;
     a.scale = scale;
-    const void *kern = pick_owner(f16, p.words, p.load_words);
+    const void *kern = pick_owner(f16, p.words, p.load_words, p.barriers);
     if (kern == nullptr) return hipErrorInvalidValue;
     hipError_t e = set_lds_limit(kern, p.lds_bytes);
     if (e != hipSuccess) return e;

@@ -465,10 +465,10 @@ def test_sketch_plan_fits_owner_kernel(lib, precision, m, n, d, zeta, lda_extra,
             if row < S and w0 < nw:
                 assert w0 * kc + fl <= n                 # inside the row
                 assert (w0 * kc) % fl == 0                # aligned
-    # LDS carve in words: two stage buffers of S + 1 rows (row S: the -0
-    # row), padding to 16 bytes, 4 trash words, two mask sets (per output
+    # LDS carve in words: nb stage buffers of S + 1 rows (row S: the -0
+    # row), padding to 16 bytes, 4 trash words, nb mask sets (per output
     # row MW mask words and 4 count words: a byte per 64 stage rows, at most
-    # 8), two entry sets, the lists
+    # 8), nb entry sets, nb - 1 list sets; nb = 3 with one barrier per stage
     MW = S // 32
     assert S // 64 <= 8
 
@@ -478,14 +478,25 @@ def test_sketch_plan_fits_owner_kernel(lib, precision, m, n, d, zeta, lda_extra,
     spread = MS != MW + 4 or CS != cap + 4 or ((MW // 4) % 2 == 0 and (cap // 4) % 2 == 0)
     for w, st in ((MW, MS), (cap, CS)):
         assert st == (w + 8 if spread and (w // 4) % 2 else w + 4)
-    bufs = 2 * (S + 1) * U
-    trash = bufs + (bufs & 2)
-    masks = trash + 4
-    ents = masks + 2 * d * MS
-    lists = ents + 2 * zeta * S
-    words = lists + d * CS
+    def carve(nb):
+        bufs = nb * (S + 1) * U
+        trash = -(-bufs // 4) * 4
+        masks = trash + 4
+        ents = masks + nb * d * MS
+        lists = ents + nb * zeta * S
+        return trash, masks, ents, lists, lists + (nb - 1) * d * CS
+
+    assert p["barriers"] in (1, 2)
+    nb = 3 if p["barriers"] == 1 else 2
+    trash, masks, ents, lists, words = carve(nb)
     assert 4 * words == p["lds_bytes"] <= MI355X["max_lds"]
     assert p["per_cu"] in (1, 2) and p["per_cu"] * p["lds_bytes"] <= MI355X["max_lds"]
+    # one barrier wherever the three sets fit at the same stage rows and
+    # workgroups per CU, with 512 threads or more and 8 hits per output row
+    # and stage on average
+    w3 = carve(3)[-1]
+    fits3 = p["per_cu"] * 4 * w3 <= MI355X["max_lds"]
+    assert (nb == 3) == (fits3 and NT >= 512 and S * zeta >= 8 * d)
     assert trash % 4 == 0 and masks % 4 == 0 and ents % 4 == 0 and lists % 4 == 0
     assert MW % 4 == 0 and (S + 1) * U % kw == 0      # the second buffer's stores stay aligned
     # chunks of whole stages cover m; one workgroup per chunk

@@ -101,6 +101,32 @@ def _stage_counts_exceed_cap(m, d, zeta, seed, p):
     return int(np.bincount(key).max()) > p["cap"]
 
 
+@pytest.mark.parametrize("m,n,d,zeta", [(5 * 256 * 512 - 77, 2, 256, 4), (3 * 256 * 256 + 100, 32, 256, 8)])
+def test_owner_one_barrier_pipeline_over_several_stages(m, n, d, zeta):
+    """Shapes the one-barrier pipeline serves, with four or five stages per
+    chunk (the three stage buffers rotate more than once) and a ragged last
+    chunk; at d = 256, n = 2 some output rows overflow their lists."""
+    seed = 13
+    A = (inputs.gaussian(m, n, seed=35) * np.float32(3.0)).astype(np.float32)
+    Ad = to_dev(A)
+    for prec in ("f16acc", "f32"):
+        p = plan(prec, m, n, n, 16, d, zeta)
+        say(f"owner one-barrier {prec} {m}x{n} d={d} zeta={zeta} V={p['words']} S={p['stage_rows']} "
+            f"stages/chunk={p['rows_per_chunk'] // max(p['stage_rows'], 1)} chunks={p['chunks']}")
+        if prec == "f16acc" or n == 2:
+            assert p["kernel"] == 2 and p["barriers"] == 1
+            assert p["rows_per_chunk"] // p["stage_rows"] >= 4
+        if prec == "f16acc":
+            assert same(sketch(Ad, d, zeta, seed, prec), f16_expect(A, seed, d, zeta, p))
+        else:
+            ri, v = oracle.meta_ref(seed, m, d, zeta)
+            exp = oracle.sketch_f64(A, ri, v, d, zeta)
+            got = sketch(Ad, d, zeta, seed, prec)
+            assert np.linalg.norm(got - exp) <= 1e-5 * np.linalg.norm(exp)
+    if n == 2:
+        assert _stage_counts_exceed_cap(m, d, zeta, seed, plan("f16acc", m, n, n, 16, d, zeta))
+
+
 def test_owner_list_overflow_walks_the_mask():
     """Enough stages that some output row has more hits in a stage than its
     list holds (checked on the host from the oracle's metadata): those hits
