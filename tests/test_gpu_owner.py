@@ -101,21 +101,31 @@ def _stage_counts_exceed_cap(m, d, zeta, seed, p):
     return int(np.bincount(key).max()) > p["cap"]
 
 
-@pytest.mark.parametrize("m,n,d,zeta", [(5 * 256 * 512 - 77, 2, 256, 4), (3 * 256 * 256 + 100, 32, 256, 8)])
-def test_owner_one_barrier_pipeline_over_several_stages(m, n, d, zeta):
-    """Shapes the one-barrier pipeline serves, with four or five stages per
-    chunk (the three stage buffers rotate more than once) and a ragged last
-    chunk; at d = 256, n = 2 some output rows overflow their lists."""
+# (m, n, d, zeta, barriers per stage in the FP16 plan, in the FP32 plan)
+ONE_BARRIER_SHAPES = [
+    (5 * 256 * 512 - 77, 2, 256, 4, 1, 1),     # lists overflow; five stages per chunk
+    (3 * 256 * 256 + 100, 32, 256, 8, 1, 2),   # four words per lane, ragged last chunk
+    ((1 << 20) - 3, 8, 128, 4, 1, 1),          # FP16: two workgroups per CU
+    ((1 << 20) - 3, 4, 128, 4, 2, 1),          # FP32: two workgroups per CU
+    (300001, 24, 192, 16, 1, 1),               # zeta = 16, 4 and 8 words per lane
+    (400000, 6, 192, 8, 1, 1),                 # 3 column pairs padded to 4 words, one-word loads
+]
+
+
+@pytest.mark.parametrize("m,n,d,zeta,bar16,bar32", ONE_BARRIER_SHAPES)
+def test_owner_one_barrier_pipeline_over_several_stages(m, n, d, zeta, bar16, bar32):
+    """Shapes the one-barrier pipeline serves, with several stages per chunk
+    (the three stage buffers rotate more than once) and a ragged last chunk,
+    next to the two-barrier pipeline where the plan keeps it."""
     seed = 13
     A = (inputs.gaussian(m, n, seed=35) * np.float32(3.0)).astype(np.float32)
     Ad = to_dev(A)
-    for prec in ("f16acc", "f32"):
+    for prec, bar in (("f16acc", bar16), ("f32", bar32)):
         p = plan(prec, m, n, n, 16, d, zeta)
         say(f"owner one-barrier {prec} {m}x{n} d={d} zeta={zeta} V={p['words']} S={p['stage_rows']} "
-            f"stages/chunk={p['rows_per_chunk'] // max(p['stage_rows'], 1)} chunks={p['chunks']}")
-        if prec == "f16acc" or n == 2:
-            assert p["kernel"] == 2 and p["barriers"] == 1
-            assert p["rows_per_chunk"] // p["stage_rows"] >= 4
+            f"barriers={p['barriers']} per_cu={p['per_cu']} chunks={p['chunks']}")
+        assert p["kernel"] == 2 and p["barriers"] == bar
+        assert p["rows_per_chunk"] // p["stage_rows"] >= 4
         if prec == "f16acc":
             assert same(sketch(Ad, d, zeta, seed, prec), f16_expect(A, seed, d, zeta, p))
         else:
