@@ -435,10 +435,11 @@ sk_status sk_fused_plan_describe(int32_t precision, int64_t m, int32_t n, int64_
  *        workgroup (owner), workgroups per CU the plan is sized for, LDS
  *        words between output rows' masks and between their lists (owner),
  *        workgroup barriers per stage (owner: 1 where the LDS holds three
- *        stage buffers at the same stage rows, else 2)}.
+ *        stage buffers at the same stage rows, else 2), loads per thread and
+ *        stage held in registers (owner: 2 or 4)}.
  * Errors: SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ARG (precision, num_cu, max_lds).
  */
-#define SK_SKETCH_PLAN_FIELDS 17
+#define SK_SKETCH_PLAN_FIELDS 18
 sk_status sk_sketch_plan_describe(int32_t precision, int64_t m, int32_t n, int64_t lda,
                                   int32_t a_align, int32_t d, int32_t zeta, int32_t num_cu,
                                   int32_t max_lds, int64_t *out);

@@ -348,7 +348,8 @@ FUSED_PLAN_FIELDS = ("fused", "rows_per_wave", "groups", "slices", "rows_per_chu
 
 SKETCH_PLAN_FIELDS = ("kernel", "words", "lanes_per_row", "threads", "row_words", "stage_rows",
                       "cap", "load_words", "rows_per_chunk", "chunks", "grid", "ws_bytes",
-                      "lds_bytes", "per_cu", "mask_stride", "list_stride", "barriers")
+                      "lds_bytes", "per_cu", "mask_stride", "list_stride", "barriers",
+                      "load_slots")
 
 
 def sk_sketch_plan_describe(precision, m, n, lda, a_align, d, zeta, num_cu, max_lds):

@@ -886,7 +886,8 @@ sk_status sk_sketch_plan_describe(int32_t precision, int64_t m, int32_t n, int64
                                               p.dual ? 2 : 1,
                                               own ? p.mask_stride : 0,
                                               own ? p.list_stride : 0,
-                                              own ? p.barriers : 0};
+                                              own ? p.barriers : 0,
+                                              own ? p.load_slots : 0};
     for (int i = 0; i < SK_SKETCH_PLAN_FIELDS; ++i) out[i] = v[i];
     return SK_OK;
 }

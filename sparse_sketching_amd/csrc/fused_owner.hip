@@ -94,8 +94,10 @@ constexpr int owner_row_stride(int w, bool spread) {
 template <class T> constexpr uint32_t kUnitSign = T::kCols == 2 ? 0x80008000u : 0x80000000u;
 
 // OB: one barrier per stage (three stage buffers, mask and entry sets, two
-// list sets); else two (two of each, one list set)
-template <class T, int V, int KF, bool OB>
+// list sets); else two (two of each, one list set).  NL: load slots per
+// thread and stage (kOwnerLoads, or 2 at 16 words per lane where a stage
+// needs no more: its two register sets then fit without spilling)
+template <class T, int V, int KF, bool OB, int NL>
 __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     extern __shared__ __align__(16) uint32_t lds[];
     const int NT = (int)blockDim.x;
@@ -156,9 +158,9 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
     // first float at byte lcol of the row; staged at word soff of a stage
     // buffer (the trash words for a repeated load), words past the row's
     // (padding) masked to zero
-    uint32_t lrow[kOwnerLoads], lcol[kOwnerLoads], soff[kOwnerLoads], keep[kOwnerLoads];
+    uint32_t lrow[NL], lcol[NL], soff[NL], keep[NL];
 #pragma unroll
-    for (int i = 0; i < kOwnerLoads; ++i) {
+    for (int i = 0; i < NL; ++i) {
         const int q = tid + i * NT;
         const int qc = q < nq ? q : nq - 1;
         const int w0 = (qc & ((1 << lpr_log) - 1)) * KW;
@@ -167,21 +169,21 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
         soff[i] = q < nq ? (uint32_t)(((qc >> lpr_log) << u_log) + w0) : trash;
         keep[i] = w0 < args.n_words ? ~0u : 0u;
     }
-    FVec<KF> ld[2][kOwnerLoads];
-    auto load = [&](int32_t s, FVec<KF> (&dst)[kOwnerLoads]) {
+    FVec<KF> ld[2][NL];
+    auto load = [&](int32_t s, FVec<KF> (&dst)[NL]) {
         const int32_t first = s * S < nrows ? s * S : 0;
         const char *base = A + (r0 + first) * (int64_t)lda4;
         const uint32_t last = (uint32_t)(nrows - 1 - first);     // last valid row of the stage
 #pragma unroll
-        for (int i = 0; i < kOwnerLoads; ++i) {
+        for (int i = 0; i < NL; ++i) {
             const uint32_t row = lrow[i] < last ? lrow[i] : last;
             dst[i] = load_vec<KF, true>(base + row * lda4 + lcol[i]);
         }
     };
     // the loaded rows' contribution words into stage buffer buf
-    auto stage = [&](const FVec<KF> (&src)[kOwnerLoads], uint32_t *buf) {
+    auto stage = [&](const FVec<KF> (&src)[NL], uint32_t *buf) {
 #pragma unroll
-        for (int i = 0; i < kOwnerLoads; ++i) {
+        for (int i = 0; i < NL; ++i) {
             uint32_t *dst = (soff[i] == trash ? bufs : buf) + soff[i];
             uint32_t w[KW];
 #pragma unroll
@@ -446,28 +448,32 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
 }
 
 template <class T, int KF, bool OB>
-const void *pick_owner_v(int V) {
+const void *pick_owner_v(int V, int nl) {
+    if (nl == 2) return V == 16 ? (const void *)k_stack_owner<T, 16, KF, OB, 2> : nullptr;
+    if (nl != kOwnerLoads) return nullptr;
     switch (V) {
-    case 1: return (const void *)k_stack_owner<T, 1, KF, OB>;
-    case 2: return (const void *)k_stack_owner<T, 2, KF, OB>;
-    case 4: return (const void *)k_stack_owner<T, 4, KF, OB>;
-    case 8: return (const void *)k_stack_owner<T, 8, KF, OB>;
-    case 16: return (const void *)k_stack_owner<T, 16, KF, OB>;
+    case 1: return (const void *)k_stack_owner<T, 1, KF, OB, kOwnerLoads>;
+    case 2: return (const void *)k_stack_owner<T, 2, KF, OB, kOwnerLoads>;
+    case 4: return (const void *)k_stack_owner<T, 4, KF, OB, kOwnerLoads>;
+    case 8: return (const void *)k_stack_owner<T, 8, KF, OB, kOwnerLoads>;
+    case 16: return (const void *)k_stack_owner<T, 16, KF, OB, kOwnerLoads>;
     default: return nullptr;
     }
 }
 
 // the built instances: FP16 loads of one or two words (2 or 4 floats), FP32
-// of one or four; one or two barriers per stage
+// of one or four; one or two barriers per stage; nl load slots
 template <bool OB>
-const void *pick_owner_b(bool f16, int V, int kw) {
+const void *pick_owner_b(bool f16, int V, int kw, int nl) {
     if (f16)
-        return kw == 2 ? pick_owner_v<AccF16, 4, OB>(V) : kw == 1 ? pick_owner_v<AccF16, 2, OB>(V) : nullptr;
-    return kw == 4 ? pick_owner_v<AccF32, 4, OB>(V) : kw == 1 ? pick_owner_v<AccF32, 1, OB>(V) : nullptr;
+        return kw == 2 ? pick_owner_v<AccF16, 4, OB>(V, nl)
+                       : kw == 1 ? pick_owner_v<AccF16, 2, OB>(V, nl) : nullptr;
+    return kw == 4 ? pick_owner_v<AccF32, 4, OB>(V, nl)
+                   : kw == 1 ? pick_owner_v<AccF32, 1, OB>(V, nl) : nullptr;
 }
-const void *pick_owner(bool f16, int V, int kw, int barriers) {
-    return barriers == 1 ? pick_owner_b<true>(f16, V, kw)
-                         : barriers == 2 ? pick_owner_b<false>(f16, V, kw) : nullptr;
+const void *pick_owner(bool f16, int V, int kw, int barriers, int nl) {
+    return barriers == 1 ? pick_owner_b<true>(f16, V, kw, nl)
+                         : barriers == 2 ? pick_owner_b<false>(f16, V, kw, nl) : nullptr;
 }
 
 }  // namespace
@@ -582,6 +588,10 @@ bool plan_owner(const DevInfo &di, bool f16, int64_t m, int32_t n, int64_t lda, 
     p->load_words = kw;
     p->lds_bytes = lds;
     p->barriers = one_barrier ? 1 : 2;
+    // two load slots at 16 words per lane where a stage needs no more (four
+    // spill: 2^20 x 32 FP16 at d = 1024, 108 -> 101 us; halving the stage
+    // rows to fit two slots was slower: 2^20 x 64 FP16 at d = 512, 85 -> 97)
+    p->load_slots = V == kOwnerMaxWords && S * U <= (int64_t)2 * kw * NT ? 2 : kOwnerLoads;
     p->ws_bytes = (size_t)p->chunks * (size_t)d * (size_t)U * 4;
     return true;
 }
@@ -610,7 +620,10 @@ hipError_t launch_owner(const FusedPlan &p, bool f16, const float *A, int64_t m,
     a.ms = p.mask_stride;
     a.cs = p.list_stride;
     a.scale = scale;
-    const void *kern = pick_owner(f16, p.words, p.load_words, p.barriers);
+    // the load slots must cover a stage
+    if ((int64_t)p.stage_rows * p.row_words > (int64_t)p.load_slots * p.load_words * p.threads)
+        return hipErrorInvalidValue;
+    const void *kern = pick_owner(f16, p.words, p.load_words, p.barriers, p.load_slots);
     if (kern == nullptr) return hipErrorInvalidValue;
     hipError_t e = set_lds_limit(kern, p.lds_bytes);
     if (e != hipSuccess) return e;

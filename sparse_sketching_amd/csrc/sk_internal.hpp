@@ -154,6 +154,7 @@ struct FusedPlan {
     int list_stride;            // LDS words between output rows' lists
     int load_words;             // words per lane load (1, 2 or 4)
     int barriers;               // workgroup barriers per stage (1 or 2)
+    int load_slots;             // loads per thread and stage held in registers (2 or 4)
     size_t lds_bytes;           // dynamic LDS per workgroup
 };
 // a_align: the alignment of A's base in bytes (16 or more: any lane load;

@@ -403,6 +403,7 @@ OWNER_SHAPES = FUSED_SHAPES + [
     (1 << 20, 2, 512, 4), (1 << 20, 2, 256, 8), (4194304, 64, 128, 4), (1 << 20, 32, 1024, 1),
     (1 << 20, 64, 256, 16), (1 << 16, 4, 64, 1), (777, 6, 48, 3), (5000, 62, 40, 8),
     (64, 64, 128, 4), (1, 2, 64, 4), (1 << 20, 16, 4096, 4), (3000, 2, 16, 16),
+    (1 << 20, 64, 512, 4), (1 << 20, 32, 512, 4),
 ]
 
 
@@ -456,7 +457,9 @@ def test_sketch_plan_fits_owner_kernel(lib, precision, m, n, d, zeta, lda_extra,
     fl = kw * kc
     assert lda % fl == 0 and align >= 4 * fl
     nload = -(-(S * U // kw) // NT)
-    assert nload <= 4
+    # load slots: two at 16 words per lane where the stage needs no more
+    assert p["load_slots"] == (2 if V == 16 and nload <= 2 else 4)
+    assert nload <= p["load_slots"]
     lpr = U // kw
     for tid in (0, 1, NT // 2, NT - 1):
         for i in range(nload):

@@ -39,6 +39,9 @@ OWNER_SHAPES = [
     (65536, 64, 256, 8),        # eight words per lane
     (1, 4, 64, 4),              # a single row
     (130, 8, 96, 2),            # one stage plus two rows
+    (40000, 64, 512, 4),        # FP16 sixteen words per lane, four load slots
+    (30000, 32, 512, 4),        # FP32 sixteen words per lane, two load slots
+    (300000, 32, 1024, 4),      # FP16 two load slots over several stages per chunk
 ]
 
 
