@@ -6,6 +6,7 @@ import ctypes
 import pytest
 
 from sparse_sketching_amd import binding as b
+from tests.sweep_shapes import SWEEP
 
 FAKE = 1 << 40          # never dereferenced: validation fails before any use
 
@@ -206,6 +207,9 @@ def test_blockperm_component_grid_covers_every_output_once(m, n, d, M, kappa, s)
 # ------------------------------------------------ LDS plan vs kernel bounds
 
 MI355X = dict(num_cu=256, max_lds=160 * 1024)
+# the GPU sweep's shapes (m, n, d, zeta), each once
+SWEEP_SHAPES = sorted({(c["m"], c["n"], c["d"], c["zeta"]) for c in SWEEP})
+
 PLAN_SHAPES = [
     # (m, n, d, zeta): the scale, coherence, range and tiny workloads, ragged
     # and degenerate test shapes, and wide/narrow extremes
@@ -327,7 +331,7 @@ FUSED_SHAPES = PLAN_SHAPES + [
     (1 << 20, 256, 1024, 4), (1 << 20, 256, 256, 16), (1 << 20, 512, 512, 1), (130, 128, 512, 4),
     (1, 128, 64, 4), (129, 256, 2048, 2), (1 << 21, 512, 1024, 4), (10_000, 384, 96, 3),
     (5000, 256, 512, 32), (5000, 256, 64, 16),
-]
+] + SWEEP_SHAPES
 
 
 @pytest.mark.parametrize("precision", [b.SK_PRECISION_F32, b.SK_PRECISION_F16ACC])
@@ -404,7 +408,7 @@ OWNER_SHAPES = FUSED_SHAPES + [
     (1 << 20, 64, 256, 16), (1 << 16, 4, 64, 1), (777, 6, 48, 3), (5000, 62, 40, 8),
     (64, 64, 128, 4), (1, 2, 64, 4), (1 << 20, 16, 4096, 4), (3000, 2, 16, 16),
     (1 << 20, 64, 512, 4), (1 << 20, 32, 512, 4),
-]
+] + SWEEP_SHAPES
 
 
 @pytest.mark.parametrize("precision", [b.SK_PRECISION_F32, b.SK_PRECISION_F16ACC])
@@ -414,8 +418,8 @@ def test_sketch_plan_fits_owner_kernel(lib, precision, m, n, d, zeta, lda_extra,
     """Replays the owner kernel's indexing on its plan: the workgroup's
     threads are whole wavefronts and cover d output rows x L lanes, each
     lane's V words of a padded row lie inside it, every stage load reads
-    inside its row with the load's alignment, the LDS carve (two stage
-    buffers, two mask sets, two entry sets, the lists) fits, list reads of 4
+    inside its row with the load's alignment, the LDS carve (two or three
+    stage buffers, mask sets and entry sets, one or two list sets) fits, list reads of 4
     entries stay inside an output row's list, a stage row index fits the
     list entry's 15 bits, and every partial store stays inside the
     workspace.  Shapes the owner kernel does not take report the register

@@ -1,0 +1,58 @@
+"""GPU sweep over seeded random shapes (tests/sweep_shapes.py): the complete
+sketch through the boundary call, against the oracle, for whichever kernel
+the plan picks.  FP16 from the register and owner kernels must equal the
+oracle's RN emulation in the library's order (per row chunk ascending from
++0, chunk partials combined in four groups) bit for bit; FP32 must be
+within the recursive-summation bound of the FP64 sketch; the metadata + LDS
+fallback's FP16 additions have no fixed order, so it is held to a relative
+bar only where few contributions meet in an entry."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_sketching_amd import binding as b
+from sparse_sketching_amd import inputs
+from tests.gpuutil import dev, say, sync, to_dev
+from tests.sweep_shapes import SWEEP
+
+pytestmark = pytest.mark.gpu
+
+MI355X = dict(num_cu=256, max_lds=160 * 1024)
+PREC = {"f32": b.SK_PRECISION_F32, "f16acc": b.SK_PRECISION_F16ACC}
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_sweep_case_matches_oracle(case):
+    c = SWEEP[case]
+    prec, m, n, d, zeta, pad = c["precision"], c["m"], c["n"], c["d"], c["zeta"], c["pad"]
+    off, seed = c["row_offset"], c["seed"]
+    p = b.sk_sketch_plan_describe(PREC[prec], m, n, n + pad, 16, d, zeta, **MI355X)
+    say(f"sweep {case}: {prec} m={m} n={n} lda={n + pad} d={d} zeta={zeta} offset={off} "
+        f"kernel={p['kernel']} barriers={p['barriers']} chunks={p['chunks']}")
+    A = (inputs.gaussian(m, n + pad, seed=case) * np.float32(3.0)).astype(np.float32)
+    Ad = to_dev(A)[:, :n]
+    dt = torch.float16 if prec == "f16acc" else torch.float32
+    out = torch.full((d, n + 2), 7.0, dtype=dt, device=dev())
+    b.sketch_fused(Ad, d, zeta, seed, prec, row_offset=off, out=out[:, :n])
+    sync()
+    B = out.cpu().numpy().astype(np.float64)
+    assert np.all(B[:, n:] == 7.0)                  # ldb padding untouched
+    B = B[:, :n]
+    A = np.ascontiguousarray(A[:, :n])
+    ri, v = oracle.meta_ref(seed, m, d, zeta, row_offset=off)
+    per_entry = m * zeta / d                        # contributions an entry gets on average
+    if prec == "f16acc" and p["kernel"] in (1, 2):
+        exp = oracle.sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=p["rows_per_chunk"],
+                                        groups=4)
+        assert np.array_equal(B, exp.astype(np.float64))
+        return
+    ref = oracle.sketch_f64(A, ri, v, d, zeta)
+    assert np.all(np.isfinite(B))
+    if prec == "f32":
+        # FP32 sums of k terms: error below k u sum|c| deterministically;
+        # 4 sqrt(k) u relative is the bar here (random signs)
+        tol = max(1e-5, 4.0 * np.sqrt(max(per_entry, 1.0)) * 2.0 ** -24)
+        assert oracle.rel_frob(B, ref) <= tol
+    elif per_entry <= 2048:
+        assert oracle.rel_frob(B, ref) <= 1e-2
