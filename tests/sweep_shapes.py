@@ -32,3 +32,33 @@ def _draw(count=80, seed=20261203):
 
 
 SWEEP = _draw()
+
+
+def _draw_blockperm(count=40, seed=20261204):
+    """(m, n, lda, d, M, kappa, s, wiring, seed) for BlockPerm-SJLT: shift
+    wiring (kappa dividing M) and affine wiring, B_r = d / M from 1 to 32,
+    s up to B_r (B_r a power of two when s > 1), ragged widths."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        shift = len(out) % 2 == 0
+        M = int(g.choice((1, 2, 3, 4, 5, 6, 8, 12, 16, 32, 64, 128)))
+        kappas = [k for k in range(1, min(M, 32) + 1) if (M % k == 0 or not shift)]
+        kappa = int(g.choice(kappas))
+        Br = int(g.choice((1, 2, 3, 4, 8, 16, 32)))
+        d = M * Br
+        if d > 4096:
+            continue
+        s = 1
+        if Br > 1 and Br & (Br - 1) == 0 and g.random() < 0.4:
+            s = int(g.choice([v for v in (2, 4, 8, Br) if v <= min(Br, 32)]))
+        n = int(g.choice((1, 2, 3, 7, 16, 31, 32, 33, 64, 100, 128, 255, 256, 300, 512)))
+        pad = int(g.choice((0, 0, 0, 1, 3)))
+        top = max(1.0, min(65536.0, 2e7 / (n * kappa * s * M)))
+        Bc = int(np.exp(g.uniform(0.0, np.log(top)))) if top > 1 else 1
+        out.append(dict(m=M * max(Bc, 1), n=n, lda=n + pad, d=d, M=M, kappa=kappa, s=s,
+                        wiring="shift" if shift else "affine", seed=int(g.integers(0, 1 << 62))))
+    return out
+
+
+BP_SWEEP = _draw_blockperm()

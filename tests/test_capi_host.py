@@ -6,7 +6,7 @@ import ctypes
 import pytest
 
 from sparse_sketching_amd import binding as b
-from tests.sweep_shapes import SWEEP
+from tests.sweep_shapes import BP_SWEEP, SWEEP
 
 FAKE = 1 << 40          # never dereferenced: validation fails before any use
 
@@ -673,6 +673,46 @@ def test_blockperm_plan_bounds(m, n, d, M, kappa, s, wiring, kernel, R, G):
     # a wavefront's rows inside one reader's block, whole stages per slice
     assert (p["rows_per_wave"], p["groups"]) == (R, G)
     assert 16 * R * G == kappa * Br and Br % R == 0 and rps % 64 == 0
+    assert p["slices"] * 256 >= n > (p["slices"] - 1) * 256
+
+
+@pytest.mark.parametrize("case", range(len(BP_SWEEP)))
+def test_blockperm_sweep_plans_fit_kernels(case):
+    """The GPU sweep's BlockPerm shapes: whichever kernel the plan picks,
+    the component kernel's workgroups own every output element once, and
+    the general kernels' partial indices stay inside the workspace, with
+    the register kernel's wavefronts tiling kappa*B_r inside one block."""
+    import numpy as np
+    c = BP_SWEEP[case]
+    m, n, d, M, kappa, s = c["m"], c["n"], c["d"], c["M"], c["kappa"], c["s"]
+    w = b.SK_WIRING_SHIFT if c["wiring"] == "shift" else b.SK_WIRING_AFFINE
+    p = b.sk_blockperm_plan_describe(m, n, d, M, kappa, s, w, 7, num_cu=256, max_lds=160 * 1024)
+    Bc, Br = m // M, d // M
+    T = kappa * Br
+    if w == b.SK_WIRING_SHIFT:
+        # sk_apply_blockperm's component grid (and _ex's where it plans it)
+        G, tiles, C = -(-T // 64), -(-n // 32), M // kappa
+        seen = np.zeros((C, T, tiles), dtype=np.int64)
+        for wg in range(C * G * tiles):
+            tile, cg = wg % tiles, wg // tiles
+            r0 = (cg % G) * 64
+            seen[cg // G, r0:min(T, r0 + 64), tile] += 1
+        assert (seen == 1).all()
+    if p["kernel"] == b.SK_BLOCKPERM_KERNEL_COMPONENT:
+        assert w == b.SK_WIRING_SHIFT and p["ws_bytes"] == 0
+        return
+    Q, rps = p["Q"], p["rows_per_slice"]
+    assert Q >= 1 and rps * Q >= Bc
+    last = ((((M - 1) * Q + Q - 1) * kappa + kappa - 1) * Br + Br - 1) * n + n - 1
+    assert (last + 1) * 4 <= p["ws_bytes"]
+    if p["kernel"] == b.SK_BLOCKPERM_KERNEL_SLICE:
+        # (trailing slices past the block may be empty: their workgroups
+        # find no rows and store zero partials)
+        assert Q * M <= 65535
+        return
+    assert Bc > rps * (Q - 1)
+    R, G = p["rows_per_wave"], p["groups"]
+    assert 16 * R * G == T and Br % R == 0 and rps % 64 == 0
     assert p["slices"] * 256 >= n > (p["slices"] - 1) * 256
 
 

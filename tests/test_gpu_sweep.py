@@ -5,7 +5,9 @@ oracle's RN emulation in the library's order (per row chunk ascending from
 +0, chunk partials combined in four groups) bit for bit; FP32 must be
 within the recursive-summation bound of the FP64 sketch; the metadata + LDS
 fallback's FP16 additions have no fixed order, so it is held to a relative
-bar only where few contributions meet in an entry."""
+bar only where few contributions meet in an entry.  BlockPerm-SJLT shapes
+run through both boundary calls (with a workspace where the plan takes
+one, and the component kernel without) against the FP64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,7 @@ import oracle
 from sparse_sketching_amd import binding as b
 from sparse_sketching_amd import inputs
 from tests.gpuutil import dev, say, sync, to_dev
-from tests.sweep_shapes import SWEEP
+from tests.sweep_shapes import BP_SWEEP, SWEEP
 
 pytestmark = pytest.mark.gpu
 
@@ -56,3 +58,30 @@ def test_sweep_case_matches_oracle(case):
         assert oracle.rel_frob(B, ref) <= tol
     elif per_entry <= 2048:
         assert oracle.rel_frob(B, ref) <= 1e-2
+
+
+@pytest.mark.parametrize("case", range(len(BP_SWEEP)))
+def test_blockperm_sweep_case_matches_oracle(case):
+    c = BP_SWEEP[case]
+    m, n, lda, d, M, kappa, s = c["m"], c["n"], c["lda"], c["d"], c["M"], c["kappa"], c["s"]
+    wiring, seed = c["wiring"], c["seed"]
+    say(f"blockperm sweep {case}: m={m} n={n} lda={lda} d={d} M={M} kappa={kappa} s={s} "
+        f"wiring={wiring}")
+    A = inputs.gaussian(m, lda, seed=1000 + case)
+    Ad = to_dev(A)[:, :n]
+    A = np.ascontiguousarray(A[:, :n])
+    ref = oracle.blockperm_f64(A, d, M, kappa, s, seed, kind=wiring)
+    # each output row sums about kappa * s * B_c / B_r terms (B_c = m / M)
+    terms = max(kappa * s * (m // M) / (d // M), 1.0)
+    tol = max(1e-5, 4.0 * np.sqrt(terms) * 2.0 ** -24)
+    out = torch.full((d, n + 1), 7.0, dtype=torch.float32, device=dev())
+    b.blockperm(Ad, d, M, kappa, seed, s=s, out=out[:, :n], wiring=wiring)
+    sync()
+    Y = out.cpu().numpy().astype(np.float64)
+    assert np.all(Y[:, n:] == 7.0)
+    assert oracle.rel_frob(Y[:, :n], ref) <= tol
+    if wiring == "shift":
+        Yd = torch.full((d, n), 7.0, dtype=torch.float32, device=dev())
+        b.sk_apply_blockperm(Ad, m, n, lda, d, M, kappa, s, seed, Yd, n)
+        sync()
+        assert oracle.rel_frob(Yd.cpu().numpy().astype(np.float64), ref) <= tol
