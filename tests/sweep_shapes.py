@@ -62,3 +62,20 @@ def _draw_blockperm(count=40, seed=20261204):
 
 
 BP_SWEEP = _draw_blockperm()
+
+
+def _draw_qr(count=24, seed=20261205):
+    """(d, n, pad) for the FP32 QR solve: n from 1 to 1024 and d from n to
+    2048 (panel widths 32, 16 and 8 with every power-of-two tail), some
+    with a padded row stride."""
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        n = int(np.exp(g.uniform(0.0, np.log(1024.0)))) if i % 2 else int(g.integers(256, 1025))
+        extra = int(np.exp(g.uniform(0.0, np.log(2049.0 - n)))) - 1
+        d = n + extra if i % 3 else int(g.integers(max(n, 1506), 2049))   # 8-column panels
+        out.append(dict(d=d, n=n, pad=int(g.choice((0, 0, 0, 5, 16)))))
+    return out
+
+
+QR_SWEEP = _draw_qr()

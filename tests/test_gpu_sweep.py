@@ -7,7 +7,8 @@ within the recursive-summation bound of the FP64 sketch; the metadata + LDS
 fallback's FP16 additions have no fixed order, so it is held to a relative
 bar only where few contributions meet in an entry.  BlockPerm-SJLT shapes
 run through both boundary calls (with a workspace where the plan takes
-one, and the component kernel without) against the FP64 oracle."""
+one, and the component kernel without) against the FP64 oracle, and the
+FP32 QR solve runs over random (d, n) against the oracle's FP64 QR."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +17,7 @@ import oracle
 from sparse_sketching_amd import binding as b
 from sparse_sketching_amd import inputs
 from tests.gpuutil import dev, say, sync, to_dev
-from tests.sweep_shapes import BP_SWEEP, SWEEP
+from tests.sweep_shapes import BP_SWEEP, QR_SWEEP, SWEEP
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +86,26 @@ def test_blockperm_sweep_case_matches_oracle(case):
         b.sk_apply_blockperm(Ad, m, n, lda, d, M, kappa, s, seed, Yd, n)
         sync()
         assert oracle.rel_frob(Yd.cpu().numpy().astype(np.float64), ref) <= tol
+
+
+@pytest.mark.parametrize("case", range(len(QR_SWEEP)))
+def test_qr_sweep_case_matches_oracle(case):
+    """Consistent systems y = M x0 (N(0,1) M): a backward-stable FP32 solve
+    is within a small multiple of cond(M) u of x0's FP64 solution, and its
+    residual within FP32 rounding of the FP64 minimum."""
+    c = QR_SWEEP[case]
+    d, n, pad = c["d"], c["n"], c["pad"]
+    say(f"qr sweep {case}: d={d} n={n} ld={n + pad}")
+    g = np.random.default_rng(5000 + case)
+    M = g.standard_normal((d, n + pad)).astype(np.float32)
+    x0 = g.standard_normal(n)
+    y = (M[:, :n].astype(np.float64) @ x0).astype(np.float32)
+    x = b.lstsq_qr(to_dev(M)[:, :n], to_dev(y))
+    sync()
+    x = x.cpu().numpy().astype(np.float64)
+    Mn = np.ascontiguousarray(M[:, :n])
+    ref = oracle.lstsq_qr(Mn, y)
+    cond = np.linalg.cond(Mn.astype(np.float64))
+    assert np.linalg.norm(x - ref) <= (2e-5 + 1e-6 * cond) * np.linalg.norm(ref)
+    r_ref = oracle.residual(Mn, ref, y)
+    assert oracle.residual(Mn, x, y) <= r_ref * (1 + 1e-5) + 1e-5 * (1 + cond / 100)
