@@ -109,3 +109,54 @@ def test_qr_sweep_case_matches_oracle(case):
     assert np.linalg.norm(x - ref) <= (2e-5 + 1e-6 * cond) * np.linalg.norm(ref)
     r_ref = oracle.residual(Mn, ref, y)
     assert oracle.residual(Mn, x, y) <= r_ref * (1 + 1e-5) + 1e-5 * (1 + cond / 100)
+
+
+APPLY_VARIANTS = (0, b.SK_VARIANT_FLAT, b.SK_VARIANT_LDS, b.SK_VARIANT_REG)
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_apply_sweep_case_matches_oracle(case):
+    """The stored-metadata applies on the sweep's shapes, one seeded pick
+    of variant (default, flat, LDS, register) and workspace per case: FP16
+    through the register kernel bit for bit in the library's order, the
+    order-free variants (flat and LDS atomics) to a relative bar where few
+    contributions meet, FP32 to the summation bound; the register variant
+    forced without a workspace or on a shape it does not cover is
+    refused."""
+    c = SWEEP[case]
+    prec, m, n, d, zeta, pad = c["precision"], c["m"], c["n"], c["d"], c["zeta"], c["pad"]
+    pick = np.random.default_rng(8000 + case)
+    flags = APPLY_VARIANTS[int(pick.integers(4))]
+    use_ws = bool(pick.random() < 0.6)
+    say(f"apply sweep {case}: {prec} m={m} n={n} lda={n + pad} d={d} zeta={zeta} "
+        f"flags={flags} workspace={use_ws}")
+    A = (inputs.gaussian(m, n + pad, seed=2000 + case) * np.float32(3.0)).astype(np.float32)
+    Ad = to_dev(A)[:, :n]
+    A = np.ascontiguousarray(A[:, :n])
+    ri, v = oracle.meta_ref(c["seed"], m, d, zeta)
+    fused = b.sk_fused_plan_describe(PREC[prec], m, n, n + pad, 16, d, zeta, **MI355X)
+    reg = bool(fused["fused"]) and zeta <= 8        # the shapes the register variant covers
+    if flags == b.SK_VARIANT_REG and not (use_ws and reg):
+        # forced without its workspace, or on a shape it does not cover
+        with pytest.raises(b.SketchError):
+            b.apply(Ad, to_dev(ri), to_dev(v), zeta, d, prec, flags=flags,
+                    ws=True if use_ws else None)
+        sync()
+        return
+    out = b.apply(Ad, to_dev(ri), to_dev(v), zeta, d, prec, flags=flags,
+                  ws=True if use_ws else None)
+    sync()
+    B = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(B))
+    per_entry = m * zeta / d
+    if prec == "f16acc" and use_ws and reg and flags in (0, b.SK_VARIANT_REG):
+        exp = oracle.sketch_f16_rn_emul(A, ri, v, d, zeta, chunk_rows=fused["rows_per_chunk"],
+                                        groups=4)
+        assert np.array_equal(B, exp.astype(np.float64))
+        return
+    ref = oracle.sketch_f64(A, ri, v, d, zeta)
+    if prec == "f32":
+        tol = max(1e-5, 4.0 * np.sqrt(max(per_entry, 1.0)) * 2.0 ** -24)
+        assert oracle.rel_frob(B, ref) <= tol
+    elif per_entry <= 2048:
+        assert oracle.rel_frob(B, ref) <= 1e-2
