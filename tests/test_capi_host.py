@@ -31,6 +31,20 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_plan_field_lists_match_the_header():
+    """Each describe call's field count in include/sk.h equals the length
+    of the binding's field-name tuple (the binding sizes its output array
+    from the tuple, so a field added on one side only would be lost or
+    overrun)."""
+    import re
+    text = open(b.HEADER).read()
+    counts = {k: int(v) for k, v in re.findall(r"#define (SK_\w*PLAN_FIELDS) (\d+)", text)}
+    assert counts == {"SK_FUSED_PLAN_FIELDS": len(b.FUSED_PLAN_FIELDS),
+                      "SK_SKETCH_PLAN_FIELDS": len(b.SKETCH_PLAN_FIELDS),
+                      "SK_BLOCKPERM_PLAN_FIELDS": len(b.BLOCKPERM_PLAN_FIELDS),
+                      "SK_PLAN_FIELDS": len(b.PLAN_FIELDS)}
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert lib.sk_status_string(s)
