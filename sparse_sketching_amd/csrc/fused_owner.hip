@@ -17,7 +17,7 @@
 //  * A workgroup owns all d output rows of one chunk of input rows: lane
 //    (o, g) keeps words [g*V, (g+1)*V) of output row o in registers (L = U/V
 //    lanes per row, U = the row's words padded to a power of two).
-//  * Rows stream through LDS in stages of S rows (double-buffered).  For
+//  * Rows stream through LDS in stages of S rows (two or three buffers).  For
 //    each stage the kernel draws the Philox words of its rows, sets bit j of
 //    a per-output-row hit mask for every hit (integer LDS atomic OR, order
 //    free), then ranks each hit among the hits of its output row (the
