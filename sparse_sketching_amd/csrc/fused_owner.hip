@@ -378,7 +378,8 @@ __global__ __launch_bounds__(1024, 1) void k_stack_owner(const OwnerArgs args) {
         // and list sets over two, so the sets a phase reads and writes are
         // disjoint: the walk reads (and clears its rows' masks in) set s
         // mod 3, the rank reads set s + 1 and writes list set s + 1 mod 2,
-        // the draw writes set s + 2, last read two phases before.
+        // the draw writes set s + 2, which the previous phase walked and
+        // cleared (before this phase's barrier-separated start).
         int32_t r3 = 0;                 // s mod 3
         for (int32_t s0 = 0; s0 < nst; s0 += 2) {
             // two stages per trip, so the register set index is a constant
